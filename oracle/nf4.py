@@ -1,0 +1,131 @@
+"""Blockwise 4-bit quantisation, packing and dequantisation (TEST INFRASTRUCTURE ONLY).
+
+Follows "QLoRA Explained: A 4-Bit Base, NF4, and What It Really Costs":
+
+* "Store a weight in 4 bits ..." -- a 4-bit pattern is the index of a row in a
+  16-row table; storing means writing the index of the closest row, reading
+  back means looking the row up.
+* "The table, and the number that stretches it" -- the worked example: the
+  scale of a group is its largest magnitude; dividing by it maps the group into
+  [-1, 1]; round to the closest row; multiply the row by the scale to read back.
+* "Why the groups are small" -- groups of 64 consecutive weights, each with its
+  own scale.
+* "What is QLoRA ..." (studyaidesign), "How it actually works" -- N weights at
+  b bits take N*b/8 bytes: two 4-bit codes per byte.
+
+READINGS (the pages leave these open):
+  * blocks are 64 consecutive elements of the row-major flattening; the last
+    block may be partial;
+  * "divide every weight by the scale" is carried out as one correctly rounded
+    fp32 reciprocal per block, rho = fl32(1/a), then n = fl32(x * rho); a block
+    whose absmax is 0 normalises to all zeros;
+  * the closest row is taken in exact arithmetic; an exact tie between two rows
+    goes to the LOWER index;
+  * element 2i is stored in the low nibble of byte i, element 2i+1 in the high
+    nibble; when the element count is odd the unused high nibble is 0;
+  * dequantisation is w = fl32(table[q] * A) with A the block's scale (fp32),
+    a single fp32 product, no fused operation.
+"""
+
+import numpy as np
+
+from .codebook import midpoints, nf4_codebook
+
+BLOCK = 64
+
+
+def _flat_f32(w):
+    w = np.asarray(w)
+    if w.dtype != np.float32:
+        raise TypeError("weights must be given as float32 values (bf16 inputs widened exactly)")
+    flat = np.ascontiguousarray(w).reshape(-1)
+    if not np.all(np.isfinite(flat)):
+        raise ValueError("non-finite weight: the method does not define a code for it")
+    return flat
+
+
+def n_blocks(n):
+    return (n + BLOCK - 1) // BLOCK
+
+
+def block_absmax(w):
+    """a_b = max |x| over elements [64b, 64b+64) of the flattening, fp32[nb]."""
+    flat = _flat_f32(w)
+    n = flat.size
+    nb = n_blocks(n)
+    pad = np.zeros(nb * BLOCK, dtype=np.float32)
+    pad[:n] = np.abs(flat)
+    return pad.reshape(nb, BLOCK).max(axis=1).astype(np.float32)
+
+
+def normalise(w, absmax):
+    """n = fl32(x * fl32(1/a_b)) per element; zero where a_b == 0."""
+    flat = _flat_f32(w)
+    n = flat.size
+    a = np.asarray(absmax, dtype=np.float32)
+    blk = np.arange(n) // BLOCK
+    ab = a[blk]
+    with np.errstate(divide="ignore"):
+        rho = np.where(ab > 0, np.float32(1.0) / np.where(ab > 0, ab, np.float32(1.0)), np.float32(0.0))
+    rho = rho.astype(np.float32)
+    return (flat * rho).astype(np.float32)
+
+
+def nearest_code(nrm, table):
+    """Index of the closest table row to each fp32 value, ties to the lower index.
+
+    Row i owns the interval (m_{i-1}, m_i] between the exact midpoints, so the
+    index is the number of midpoints strictly below the value.
+    """
+    mids = midpoints(table)
+    v = np.asarray(nrm, dtype=np.float32).astype(np.float64)
+    return np.searchsorted(mids, v, side="left").astype(np.uint8)
+
+
+def pack_codes(q):
+    """Two 4-bit codes per byte: element 2i low nibble, 2i+1 high nibble."""
+    q = np.asarray(q, dtype=np.uint8).reshape(-1)
+    if np.any(q > 15):
+        raise ValueError("codes are 4-bit")
+    n = q.size
+    nbytes = (n + 1) // 2
+    padded = np.zeros(2 * nbytes, dtype=np.uint8)
+    padded[:n] = q
+    return (padded[0::2] | (padded[1::2] << 4)).astype(np.uint8)
+
+
+def unpack_codes(packed, n):
+    """Inverse of pack_codes: uint8[n] codes."""
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    out = np.empty(2 * packed.size, dtype=np.uint8)
+    out[0::2] = packed & 0x0F
+    out[1::2] = packed >> 4
+    return out[:n]
+
+
+def quantize(w, table=None):
+    """Blockwise quantisation of a weight array.
+
+    Returns (packed uint8[ceil(n/2)], absmax fp32[ceil(n/64)], codes uint8[n]).
+    """
+    if table is None:
+        table = nf4_codebook()
+    flat = _flat_f32(w)
+    absmax = block_absmax(flat)
+    nrm = normalise(flat, absmax)
+    q = nearest_code(nrm, table)
+    return pack_codes(q), absmax, q
+
+
+def dequant(packed, n, scale, table=None):
+    """w = fl32(table[q] * A_b) for each element; fp32[n].
+
+    ``scale`` is the per-block fp32 A_b: the absmax itself, or its
+    double-quantised reconstruction.
+    """
+    if table is None:
+        table = nf4_codebook()
+    table = np.asarray(table, dtype=np.float32)
+    q = unpack_codes(packed, n)
+    A = np.asarray(scale, dtype=np.float32)[np.arange(n) // BLOCK]
+    return (table[q] * A).astype(np.float32)
