@@ -1,0 +1,287 @@
+// Codec kernels for gfx950: blockwise NF4 quantisation, double quantisation of
+// the block scales, dequantisation.
+//
+// "QLoRA Explained: A 4-Bit Base, NF4, and What It Really Costs":
+//   - "The table, and the number that stretches it": scale = largest magnitude
+//     of the group, divide, round to the closest row, store its index; read back
+//     by looking the row up and multiplying by the scale.
+//   - "Why the groups are small": groups of 64, each with its own scale.
+//   - "Shrink the scale factors too, and total up the real bill": the scales in
+//     8 bits, 256 per group with one 32-bit constant.
+//
+// All three are HBM-streaming kernels: 128-bit coalesced loads and stores,
+// grid-stride loops over a grid sized to a few waves per CU.  No floating-point
+// contraction: every rounding step is the one the format defines.
+
+#pragma clang fp contract(off)
+
+#include "qn_device.h"
+#include "qn_internal.h"
+
+namespace qn {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+  // quad_perm [1,0,3,2]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+  // quad_perm [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+}
+
+// Row index of one normalised value: bucket lookup plus one compare.
+__device__ __forceinline__ uint32_t nearest_row(float nrm, const float2 *lut) {
+  int b = (int)__builtin_fmaf(nrm, 16.0f, 16.0f);
+  b = min(max(b, 0), 31);
+  const float2 e = lut[b];
+  const float thr = e.x, base = e.y;
+  return as_u32(base) + (nrm >= thr ? 1u : 0u);
+}
+
+// ---------------------------------------------------------------- quantise
+// One lane handles 16 consecutive elements; four neighbouring lanes (a DPP
+// quad) form one block of 64, reduce its absmax with two quad permutes, and
+// each lane stores its 8 bytes of packed codes.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restrict__ W, int64_t n,
+                                                            uint8_t *__restrict__ codes,
+                                                            float *__restrict__ absmax,
+                                                            CodecTables tab) {
+  __shared__ float2 lut[32];
+  if (threadIdx.x < 32) {
+    lut[threadIdx.x] = make_float2(tab.thr[threadIdx.x], __builtin_bit_cast(float, tab.base[threadIdx.x]));
+  }
+  __syncthreads();
+
+  const int64_t nchunks = (n + 15) / 16;
+  const int64_t nbytes = (n + 1) / 2;
+  for (int64_t t0 = (int64_t)blockIdx.x * kThreads; t0 < nchunks; t0 += (int64_t)gridDim.x * kThreads) {
+    const int64_t t = t0 + threadIdx.x;
+    const int64_t e0 = t * 16;
+    float v[16];
+    const bool full = e0 + 16 <= n;
+    if (full) {
+      if constexpr (BF16) {
+        const uint16_t *p = static_cast<const uint16_t *>(W) + e0;
+        const u32x4 a = ld_stream(p);
+        const u32x4 b = ld_stream(p + 8);
+        uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[2 * i] = bf16_lo(w[i]);
+          v[2 * i + 1] = bf16_hi(w[i]);
+        }
+      } else {
+        const float *p = static_cast<const float *>(W) + e0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 a = ld_stream(p + 4 * i);
+          // Copy components to scalars before reinterpreting them: a bit_cast
+          // applied directly to a vector component reads the wrong element.
+          const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[4 * i + j] = as_f32(u[j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t e = e0 + i;
+        float x = 0.0f;
+        if (e < n) {
+          if constexpr (BF16) x = bf16_to_f32(static_cast<const uint16_t *>(W)[e]);
+          else x = static_cast<const float *>(W)[e];
+        }
+        v[i] = x;
+      }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = fmaxf(am, dpp_quad_xor1(am));
+    am = fmaxf(am, dpp_quad_xor2(am));
+    if ((threadIdx.x & 3) == 0 && e0 < n) absmax[t >> 2] = am;
+    // Correctly rounded reciprocal, once per block (infinite when 1/a overflows).
+    const float rho = am > 0.0f ? 1.0f / am : 0.0f;
+
+    uint32_t lo = 0, hi = 0;
+    if (!__builtin_isinf(rho)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lo |= nearest_row(v[i] * rho, lut) << (4 * i);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hi |= nearest_row(v[8 + i] * rho, lut) << (4 * i);
+    } else {
+      // 1/a overflows fp32 (a < 2^-128): divide each weight by a instead.
+      for (int i = 0; i < 8; ++i) lo |= nearest_row(v[i] / am, lut) << (4 * i);
+      for (int i = 0; i < 8; ++i) hi |= nearest_row(v[8 + i] / am, lut) << (4 * i);
+    }
+
+    if (full) {
+      *reinterpret_cast<uint2 *>(codes + 8 * t) = make_uint2(lo, hi);
+    } else if (e0 < n) {
+      // Partial chunk: elements past n were zeros whose row index is the zero
+      // row; clear those nibbles so the padding nibble of an odd count is 0.
+      const int valid = (int)(n - e0);  // 1..15
+      uint64_t word = ((uint64_t)hi << 32) | lo;
+      if (valid < 16) word &= (valid == 0) ? 0ull : ((1ull << (4 * valid)) - 1ull);
+      const int64_t b0 = 8 * t;
+      for (int i = 0; i < 8 && b0 + i < nbytes; ++i) codes[b0 + i] = (uint8_t)(word >> (8 * i));
+    }
+  }
+}
+
+// ------------------------------------------------------------ double quant
+// One workgroup of 256 lanes per group of 256 block scales.
+__global__ __launch_bounds__(kThreads) void double_quant_kernel(const float *__restrict__ absmax, int64_t nb,
+                                                                uint8_t *__restrict__ absmax_q,
+                                                                float *__restrict__ scale2) {
+  __shared__ float wmax[kThreads / 64];
+  const int64_t g = blockIdx.x;
+  const int64_t b = g * QN_GROUP + threadIdx.x;
+  const float a = b < nb ? absmax[b] : 0.0f;
+  float m = a;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float c = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float step = c / 255.0f;
+  if (threadIdx.x == 0) scale2[g] = step;
+  if (b < nb) {
+    uint32_t k = 0;
+    if (step > 0.0f) {
+      const float t = a / step;
+      // t - 1/2 is exact in fp32 for t >= 1/2; below that the ceiling is 0 anyway.
+      const float kf = ceilf(t - 0.5f);
+      k = (uint32_t)fminf(fmaxf(kf, 0.0f), 255.0f);
+    }
+    absmax_q[b] = (uint8_t)k;
+  }
+}
+
+// ---------------------------------------------------------------- dequant
+// One lane expands 32 consecutive elements (16 bytes of codes, half a block)
+// through a 256-entry byte -> (row lo, row hi) table in LDS.
+__device__ __forceinline__ float block_scale(const ScaleSrc &sc, int64_t b) {
+  if (sc.absmax_q) return (float)sc.absmax_q[b] * sc.scale2[b / QN_GROUP];
+  return sc.absmax[b];
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ codes, ScaleSrc sc,
+                                                           int64_t n, void *__restrict__ out,
+                                                           CodecTables tab) {
+  __shared__ float2 pair[256];
+  {
+    const uint32_t v = threadIdx.x;
+    pair[v] = make_float2(tab.code[v & 15], tab.code[v >> 4]);
+  }
+  __syncthreads();
+  const int64_t nchunks = (n + 31) / 32;
+  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < nchunks;
+       t += (int64_t)gridDim.x * kThreads) {
+    const int64_t e0 = t * 32;
+    const float A = block_scale(sc, e0 / QN_BLOCK);
+    if (e0 + 32 <= n) {
+      const u32x4 cw = ld_stream(codes + 16 * t);
+      const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+      if constexpr (OUT_BF16) {
+        uint32_t o[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float2 c = pair[(w[i] >> (8 * j)) & 0xFF];
+            o[4 * i + j] = pack_bf16x2(c.x * A, c.y * A);
+          }
+        }
+        uint16_t *dst = static_cast<uint16_t *>(out) + e0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 ov = {o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+          st_stream(dst + 8 * i, ov);
+        }
+      } else {
+        float *dst = static_cast<float *>(out) + e0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float2 c0 = pair[w[i] & 0xFF];
+          const float2 c1 = pair[(w[i] >> 8) & 0xFF];
+          const float2 c2 = pair[(w[i] >> 16) & 0xFF];
+          const float2 c3 = pair[w[i] >> 24];
+          const f32x4 o0 = {c0.x * A, c0.y * A, c1.x * A, c1.y * A};
+          const f32x4 o1 = {c2.x * A, c2.y * A, c3.x * A, c3.y * A};
+          st_stream_f4(dst + 8 * i, o0);
+          st_stream_f4(dst + 8 * i + 4, o1);
+        }
+      }
+    } else {
+      for (int64_t e = e0; e < n; ++e) {
+        const uint8_t byte = codes[e >> 1];
+        const uint32_t q = (e & 1) ? (byte >> 4) : (byte & 15);
+        const float w = pair[q].x * A;
+        if constexpr (OUT_BF16) {
+          static_cast<uint16_t *>(out)[e] = f32_to_bf16(w);
+        } else {
+          static_cast<float *>(out)[e] = w;
+        }
+      }
+    }
+  }
+}
+
+int grid_for(int64_t work_items, int per_cu_waves = 8) {
+  // At most a few workgroups per CU for a grid-stride loop; at least one item each.
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  static int cus = 0;
+  if (cus == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) == hipSuccess) cus = p.multiProcessorCount;
+    if (cus <= 0) cus = 256;
+  }
+  int64_t wgs = (work_items + kThreads - 1) / kThreads;
+  int64_t cap = (int64_t)cus * per_cu_waves;
+  if (wgs > cap) wgs = cap;
+  if (wgs < 1) wgs = 1;
+  return (int)wgs;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, uint8_t *codes, float *absmax,
+                           hipStream_t s) {
+  const CodecTables &tab = codec_tables();
+  const int64_t nchunks = (n + 15) / 16;
+  const int grid = grid_for(nchunks);
+  if (w_is_bf16)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(kThreads), 0, s, W, n, codes, absmax, tab);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(kThreads), 0, s, W, n, codes, absmax, tab);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *absmax_q, float *scale2,
+                               hipStream_t s) {
+  const int64_t ng = (nb + QN_GROUP - 1) / QN_GROUP;
+  hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)ng), dim3(kThreads), 0, s, absmax, nb, absmax_q,
+                     scale2);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const qn_nf4_weight &W, void *out, int out_bf16, hipStream_t s) {
+  const CodecTables &tab = codec_tables();
+  const int64_t n = W.N * W.K;
+  ScaleSrc sc{W.absmax, W.absmax_q, W.scale2};
+  const int grid = grid_for((n + 31) / 32);
+  if (out_bf16)
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3(grid), dim3(kThreads), 0, s, W.codes, sc, n, out, tab);
+  else
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3(grid), dim3(kThreads), 0, s, W.codes, sc, n, out, tab);
+  return hipGetLastError();
+}
+
+}  // namespace qn

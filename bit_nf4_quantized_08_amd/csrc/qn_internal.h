@@ -1,0 +1,82 @@
+// Internal declarations shared by the host API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qlora_nf4.h"
+
+namespace qn {
+
+// Tables handed to the codec kernels by value (they live in the kernel argument
+// segment; kernels copy what they index dynamically into LDS).
+//   code[16]      the NF4 rows (fp32).
+//   thr[32], base[32]  bucket table for the nearest-row search: a normalised
+//   value n in [-1, 1] falls into bucket b = clamp(int(16 n + 16), 0, 31); the
+//   row index is base[b] + (n >= thr[b]).  Built on the host so that each bucket
+//   holds at most one decision threshold and every threshold lies far (>1e-4)
+//   from a bucket edge, which makes the bucket's own rounding irrelevant.
+struct CodecTables {
+  float code[16];
+  float thr[32];
+  uint32_t base[32];
+};
+
+// Host: the NF4 table and the bucket table (codebook.cpp).  Idempotent, thread-safe.
+const CodecTables &codec_tables();
+// False if the bucket table failed its self-check (never expected).
+bool codec_tables_ok();
+
+// Host: fp64 NF4 rows before rounding (exposed for the library's own checks).
+void nf4_rows_f64(double out[16]);
+
+// Kernel launchers (return hipError_t of the launch).
+hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, uint8_t *codes,
+                           float *absmax, hipStream_t s);
+hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *absmax_q,
+                               float *scale2, hipStream_t s);
+hipError_t launch_dequant(const qn_nf4_weight &W, void *out, int out_bf16, hipStream_t s);
+
+// Scale of block b: fl32(k_b * step_g) with double quantisation, else absmax[b].
+struct ScaleSrc {
+  const float *absmax;
+  const uint8_t *absmax_q;
+  const float *scale2;
+};
+
+// Forward pieces.
+struct FwdArgs {
+  const uint16_t *X;     // bf16 [M,K]
+  int64_t M, N, K, r;
+  const uint8_t *codes;
+  ScaleSrc sc;
+  const uint16_t *A;     // bf16 [r,K]
+  const uint16_t *B;     // bf16 [N,r]
+  float s;               // alpha / r
+  uint16_t *Y;           // bf16 [M,N]
+  float *H_out;          // fp32 [M,r] or null
+  void *ws;
+  size_t ws_bytes;
+};
+size_t fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
+hipError_t run_fwd(const FwdArgs &a, hipStream_t s);
+
+struct BwdArgs {
+  const uint16_t *dY;    // bf16 [M,N]
+  const uint16_t *X;     // bf16 [M,K]
+  int64_t M, N, K, r;
+  const uint8_t *codes;
+  ScaleSrc sc;
+  const uint16_t *A;     // bf16 [r,K]
+  const uint16_t *B;     // bf16 [N,r]
+  float s;
+  uint16_t *dX;          // bf16 [M,K] or null
+  uint16_t *dA;          // bf16 [r,K]
+  uint16_t *dB;          // bf16 [N,r]
+  void *ws;
+  size_t ws_bytes;
+};
+size_t bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
+hipError_t run_bwd(const BwdArgs &a, hipStream_t s);
+
+}  // namespace qn

@@ -50,14 +50,17 @@ def forward(X, W_hat, A, B, alpha):
     return Y, H
 
 
-def backward(G, X, W_hat, A, B, alpha):
-    """Returns (dX [M,K], dA [r,K], dB [N,r]) in fp64; the base gets nothing."""
-    G, X, W_hat, A, B = _f64(G), _f64(X), _f64(W_hat), _f64(A), _f64(B)
+def backward(G, X, W_hat, A, B, alpha, want_dX=True):
+    """Returns (dX [M,K], dA [r,K], dB [N,r]) in fp64; the base gets nothing.
+
+    With want_dX=False (W_hat may then be None) dX is not formed and None is
+    returned in its place; dA and dB are unchanged."""
+    G, X, A, B = _f64(G), _f64(X), _f64(A), _f64(B)
     r = A.shape[0]
     s = float(alpha) / float(r)
     H = X @ A.T
     dH = s * (G @ B)
     dB = s * (G.T @ H)
     dA = dH.T @ X
-    dX = G @ W_hat + dH @ A
+    dX = G @ _f64(W_hat) + dH @ A if want_dX else None
     return dX, dA, dB

@@ -17,8 +17,10 @@ READINGS (the pages leave these open):
   * blocks are 64 consecutive elements of the row-major flattening; the last
     block may be partial;
   * "divide every weight by the scale" is carried out as one correctly rounded
-    fp32 reciprocal per block, rho = fl32(1/a), then n = fl32(x * rho); a block
-    whose absmax is 0 normalises to all zeros;
+    fp32 reciprocal per block, rho = fl32(1/a), then n = fl32(x * rho); where
+    that reciprocal does not exist in fp32 (a < 2^-128, 1/a overflows) each
+    weight is divided directly, n = fl32(x / a); a block whose absmax is 0
+    normalises to all zeros;
   * the closest row is taken in exact arithmetic; an exact tie between two rows
     goes to the LOWER index;
   * element 2i is stored in the low nibble of byte i, element 2i+1 in the high
@@ -59,16 +61,22 @@ def block_absmax(w):
 
 
 def normalise(w, absmax):
-    """n = fl32(x * fl32(1/a_b)) per element; zero where a_b == 0."""
+    """n = fl32(x * fl32(1/a_b)) per element (fl32(x / a_b) where 1/a_b overflows);
+    zero where a_b == 0."""
     flat = _flat_f32(w)
     n = flat.size
     a = np.asarray(absmax, dtype=np.float32)
     blk = np.arange(n) // BLOCK
     ab = a[blk]
-    with np.errstate(divide="ignore"):
-        rho = np.where(ab > 0, np.float32(1.0) / np.where(ab > 0, ab, np.float32(1.0)), np.float32(0.0))
-    rho = rho.astype(np.float32)
-    return (flat * rho).astype(np.float32)
+    safe = np.where(ab > 0, ab, np.float32(1.0)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        rho = (np.float32(1.0) / safe).astype(np.float32)
+        out = (flat * rho).astype(np.float32)
+    direct = np.isinf(rho)
+    if np.any(direct):
+        out[direct] = (flat[direct] / safe[direct]).astype(np.float32)
+    out[ab == 0] = np.float32(0.0)
+    return out
 
 
 def nearest_code(nrm, table):

@@ -104,8 +104,12 @@ def _brute_codes(block, table):
     if a == 0:
         return [int(np.argmin(np.abs(table.astype(np.float64))))] * len(block)
     rho = _f32_round(Fraction(1) / a)
+    direct = np.isinf(rho)      # 1/a overflows fp32: divide each weight instead
     for x in block:
-        n = _f32_round(Fraction(float(x)) * Fraction(float(rho)))
+        if direct:
+            n = _f32_round(Fraction(float(x)) / a)
+        else:
+            n = _f32_round(Fraction(float(x)) * Fraction(float(rho)))
         d = [abs(Fraction(float(n)) - Fraction(float(c))) for c in table]
         best = min(range(16), key=lambda i: (d[i], i))
         out.append(best)
@@ -122,6 +126,10 @@ def test_brute_force_nearest_row(seed, which):
     w[rng.integers(0, n, 3)] *= np.float32(7.0)
     if seed == 0:
         w[64:128] = 0.0                   # a zero block
+    if seed == 1:
+        w[64:128] *= np.float32(1e-37)    # subnormal block: 1/a overflows fp32
+    if seed == 2:
+        w[0:64] *= np.float32(1e-33)      # small normal block
     _, absmax, q = nf4.quantize(w, table=table)
     for b in range(absmax.size):
         blk = w[64 * b:64 * (b + 1)]
