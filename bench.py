@@ -1,0 +1,280 @@
+"""Throughput of the NF4 / QLoRA-linear hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of the single
+4096x4096 projection workload (W ~ N(0, 0.02) as bf16, LoRA r = 16,
+alpha = 32):
+
+  quantise W (bf16 -> NF4 codes + fp32 absmax)      nf4_quantize
+  double-quantise the absmax                         nf4_double_quant
+  dequantise a weight to bf16                        nf4_dequant
+  decode forward, X: 1 x 4096                        qlora_linear_fwd (M = 1)
+  prefill forward, X: 2048 x 4096                    qlora_linear_fwd (M = 2048)
+  backward at M = 2048 (dX, dA, dB)                  qlora_linear_bwd
+
+Inputs are synthetic, generated on the device before the timed region.  Four
+weight slots rotate: step i quantises slot i % 4 while the forward/backward
+read slot (i + 2) % 4, quantised two steps earlier, so weight reads come from
+HBM rather than from a cache that still holds what the quantiser just wrote.
+
+`value` is the step's algorithmic contraction work (prefill forward +
+backward + decode GEMV, FLOPs counted as 2 per multiply-add, dequant work not
+counted) divided by the step time.  Per-stage figures are in `stages`.  The
+`roofline` object is for the kernel with the largest share of the step,
+timed with HIP events recorded by the library around that kernel on its own
+launch stream.  `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+N, K, R, ALPHA = 4096, 4096, 16, 32.0
+M_DEC, M_PRE = 1, 2048
+SLOTS = 4
+
+
+def sizes():
+    n = N * K
+    nb = n // 64
+    ng = (nb + 255) // 256
+    w_bytes = n // 2 + nb + 4 * ng
+    return dict(
+        n=n, nb=nb, ng=ng,
+        quantize_bytes=2 * n + n // 2 + 4 * nb,
+        dq_bytes=4 * nb + nb + 4 * ng,
+        dequant_bytes=w_bytes + 2 * n,
+        gemv_weight_bytes=w_bytes,
+        gemv_all_bytes=w_bytes + 2 * K * M_DEC + 2 * N * M_DEC + 2 * R * K + 2 * N * R,
+        gemv_flops=2 * M_DEC * N * K + 2 * M_DEC * K * R + 2 * M_DEC * R * N,
+        fwd_flops=2 * M_PRE * N * K + 2 * M_PRE * K * R + 2 * M_PRE * R * N,
+        fwd_gemm_kernel_flops=2 * M_PRE * N * K + 2 * M_PRE * R * N,
+        bwd_flops=2 * M_PRE * N * K + 4 * M_PRE * N * R + 4 * M_PRE * R * K,
+        dx_gemm_kernel_flops=2 * M_PRE * N * K + 2 * M_PRE * R * K,
+    )
+
+
+def cpu_baseline():
+    """Time the CPU oracle on a bounded sample of the same workload: the codec on
+    four 4096x4096 bf16 weights, and the step's fp64 contractions in full."""
+    import numpy as np
+    import oracle
+    from bit_nf4_quantized_08_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    tiles = 4
+    s = sizes()
+    t_q = t_codec = 0.0
+    for t in range(tiles):
+        W = synth.bf16_values(synth.to_bf16(synth.gaussian((N, K), 0.02, synth.SEED_BULK0 + t)))
+        t0 = time.perf_counter()
+        packed, absmax, _ = oracle.quantize(W)
+        t1 = time.perf_counter()
+        k, step = oracle.double_quant(absmax)
+        Wh = oracle.dequant_bf16_weight(packed, N, K, oracle.dq_absmax(k, step))
+        t2 = time.perf_counter()
+        t_q += t1 - t0
+        t_codec += t2 - t0
+    X = synth.bf16_values(synth.to_bf16(synth.gaussian((M_PRE, K), 1.0, synth.SEED_X)))
+    A = synth.bf16_values(synth.to_bf16(synth.gaussian((R, K), 0.01, synth.SEED_A)))
+    B = synth.bf16_values(synth.to_bf16(synth.gaussian((N, R), 0.01, synth.SEED_B)))
+    dY = synth.bf16_values(synth.to_bf16(synth.gaussian((M_PRE, N), 1.0, synth.SEED_DY)))
+    t2 = time.perf_counter()
+    oracle.forward(X[:M_DEC], Wh, A, B, ALPHA)
+    oracle.forward(X, Wh, A, B, ALPHA)
+    oracle.backward(dY, X, Wh, A, B, ALPHA)
+    t3 = time.perf_counter()
+    flops = s["gemv_flops"] + s["fwd_flops"] + s["bwd_flops"]
+    return {
+        "value": flops / (t3 - t2) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"codec (quantise, double quant, dequant) on {tiles} 4096x4096 bf16 weights: "
+                   f"{t_codec:.2f} s, quantise {tiles * s['quantize_bytes'] / t_q / 1e9:.3f} GB/s on 1 core; "
+                   f"the step's fp64 contractions in full (decode M=1, prefill M=2048 forward and "
+                   f"backward): {t3 - t2:.2f} s on {blas_threads} BLAS threads"),
+        "quantize_GBps": tiles * s["quantize_bytes"] / t_q / 1e9,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the path is single-GPU; the sharding design is described in the docs).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_nf4_quantized_08_amd import lib
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib.load()
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+
+    def randn(shape, std):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    Ws = [randn((N, K), 0.02) for _ in range(SLOTS)]
+    Xd = randn((M_DEC, K), 1.0)
+    Xp = randn((M_PRE, K), 1.0)
+    A = randn((R, K), 0.01)
+    B = randn((N, R), 0.01)
+    dY = randn((M_PRE, N), 1.0)
+    n = N * K
+    slots = []
+    for i in range(SLOTS):
+        codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        absmax = torch.empty(n // 64, dtype=torch.float32, device=dev)
+        aq = torch.empty(n // 64, dtype=torch.uint8, device=dev)
+        s2 = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device=dev)
+        slots.append(lib.NF4Weight(codes, absmax, aq, s2, N, K))
+    deq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    Yd = torch.empty((M_DEC, N), dtype=torch.bfloat16, device=dev)
+    Yp = torch.empty((M_PRE, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M_PRE, K), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
+    dB = torch.empty((N, R), dtype=torch.bfloat16, device=dev)
+    ws_dec = lib.workspace(lib.QN_OP_FWD, M_DEC, N, K, R, dev)
+    ws_pre = lib.workspace(lib.QN_OP_FWD, M_PRE, N, K, R, dev)
+    ws_bwd = lib.workspace(lib.QN_OP_BWD, M_PRE, N, K, R, dev)
+
+    def quantize(i):
+        w = slots[i % SLOTS]
+        lib.nf4_quantize(Ws[i % SLOTS], codes=w.codes, absmax=w.absmax)
+        lib.nf4_double_quant(w.absmax, absmax_q=w.absmax_q, scale2=w.scale2)
+
+    def step(i, ev=None):
+        def mark(k):
+            if ev is not None:
+                ev[k].record()
+        mark(0)
+        quantize(i)
+        mark(1)
+        w = slots[(i + 2) % SLOTS]
+        lib.nf4_dequant(w, "bf16", out=deq)
+        mark(2)
+        lib.qlora_linear_fwd(Xd, w, A, B, ALPHA, Y=Yd, ws=ws_dec)
+        mark(3)
+        lib.qlora_linear_fwd(Xp, w, A, B, ALPHA, Y=Yp, ws=ws_pre)
+        mark(4)
+        lib.qlora_linear_bwd(dY, Xp, w, A, B, ALPHA, out=(dX, dA, dB), ws=ws_bwd)
+        mark(5)
+
+    for i in range(SLOTS):
+        quantize(i)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    lib.trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    trace = lib.trace_read()
+    lib.trace_enable(False)
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {k: 0.0 for k in ("quantize+dq", "dequant", "fwd_decode", "fwd_prefill", "bwd")}
+    names = list(stage_ms)
+    for e in evs:
+        for j in range(5):
+            stage_ms[names[j]] += e[j].elapsed_time(e[j + 1]) / args.steps
+    kern = {}
+    for kind, ms in trace:
+        kern.setdefault(kind, []).append(ms)
+    kern_avg = {k: sum(v) / len(v) for k, v in kern.items()}
+    kern_per_step = {k: sum(v) / args.steps for k, v in kern.items()}
+
+    s = sizes()
+    flops_step = s["fwd_flops"] + s["bwd_flops"] + s["gemv_flops"]
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    work = {  # algorithmic work per launch, and its roofline
+        "quantize": (s["quantize_bytes"], "hbm"),
+        "double_quant": (s["dq_bytes"], "hbm"),
+        "dequant": (s["dequant_bytes"], "hbm"),
+        "gemv": (s["gemv_all_bytes"], "hbm"),
+        "gemm_fwd": (s["fwd_gemm_kernel_flops"], "mfma"),
+        "gemm_dx": (s["dx_gemm_kernel_flops"], "mfma"),
+    }
+
+    def roof(kind):
+        amount, bound = work[kind]
+        avg = kern_avg[kind]
+        if bound == "hbm":
+            ach = amount / (avg * 1e-3) / 1e9
+            return {"kernel": kind, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                    "avg_ms": round(avg, 5), "work_per_launch": amount}
+        ach = amount / (avg * 1e-3) / 1e12
+        return {"kernel": kind, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_ms": round(avg, 5), "work_per_launch": amount}
+
+    dominant = max((k for k in kern_per_step if k in work), key=lambda k: kern_per_step[k])
+    stages = {
+        "prefill_fwd_TFLOPs": round(s["fwd_flops"] / (stage_ms["fwd_prefill"] * 1e-3) / 1e12, 1),
+        "prefill_fwd_gemm_kernel_TFLOPs": round(s["fwd_gemm_kernel_flops"] / (kern_avg["gemm_fwd"] * 1e-3) / 1e12, 1),
+        "bwd_TFLOPs": round(s["bwd_flops"] / (stage_ms["bwd"] * 1e-3) / 1e12, 1),
+        "decode_weight_GBps": round(s["gemv_weight_bytes"] / (stage_ms["fwd_decode"] * 1e-3) / 1e9, 1),
+        "decode_gemv_kernel_weight_GBps": round(s["gemv_weight_bytes"] / (kern_avg["gemv"] * 1e-3) / 1e9, 1),
+        "quantize_GBps": round(s["quantize_bytes"] / (kern_avg["quantize"] * 1e-3) / 1e9, 1),
+        "dequant_GBps": round(s["dequant_bytes"] / (kern_avg["dequant"] * 1e-3) / 1e9, 1),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "kernel_avg_ms": {k: round(v, 5) for k, v in kern_avg.items()},
+        "kernel_rooflines": {k: roof(k) for k in work if k in kern_avg},
+    }
+    out = {
+        "metric": "NF4 dequant-GEMM TFLOP/s (prefill), weight GB/s (decode GEMV), quantize GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "single 4096x4096 projection: NF4 bs64 + double quant bs256, LoRA r=16 alpha=32, "
+                               "decode M=1 and prefill M=2048 forward, backward at M=2048, bf16 weight source",
+                   "N": N, "K": K, "r": R, "alpha": ALPHA, "M_decode": M_DEC, "M_prefill": M_PRE},
+        "metrics": {
+            "prefill_dequant_gemm_TFLOPs": stages["prefill_fwd_TFLOPs"],
+            "decode_gemv_weight_GBps": stages["decode_weight_GBps"],
+            "quantize_GBps": stages["quantize_GBps"],
+        },
+        "roofline": roof(dominant),
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

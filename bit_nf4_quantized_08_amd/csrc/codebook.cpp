@@ -125,6 +125,13 @@ bool codec_tables_ok() {
   return g_ok;
 }
 
+Code16 code16() {
+  Code16 c;
+  const CodecTables &t = codec_tables();
+  for (int i = 0; i < 16; ++i) c.v[i] = t.code[i];
+  return c;
+}
+
 void nf4_rows_f64(double out[16]) {
   codec_tables();
   std::memcpy(out, g_rows64, sizeof(g_rows64));

@@ -257,6 +257,7 @@ hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, uint8_t *cod
   const CodecTables &tab = codec_tables();
   const int64_t nchunks = (n + 15) / 16;
   const int grid = grid_for(nchunks);
+  TraceScope tr(QN_TRACE_QUANTIZE, s);
   if (w_is_bf16)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(kThreads), 0, s, W, n, codes, absmax, tab);
   else
@@ -267,6 +268,7 @@ hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, uint8_t *cod
 hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *absmax_q, float *scale2,
                                hipStream_t s) {
   const int64_t ng = (nb + QN_GROUP - 1) / QN_GROUP;
+  TraceScope tr(QN_TRACE_DOUBLE_QUANT, s);
   hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)ng), dim3(kThreads), 0, s, absmax, nb, absmax_q,
                      scale2);
   return hipGetLastError();
@@ -277,6 +279,7 @@ hipError_t launch_dequant(const qn_nf4_weight &W, void *out, int out_bf16, hipSt
   const int64_t n = W.N * W.K;
   ScaleSrc sc{W.absmax, W.absmax_q, W.scale2};
   const int grid = grid_for((n + 31) / 32);
+  TraceScope tr(QN_TRACE_DEQUANT, s);
   if (out_bf16)
     hipLaunchKernelGGL(dequant_kernel<true>, dim3(grid), dim3(kThreads), 0, s, W.codes, sc, n, out, tab);
   else

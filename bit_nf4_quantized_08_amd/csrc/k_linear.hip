@@ -32,10 +32,6 @@ constexpr int kThreads = 256;
 constexpr int BK = 64;        // contraction step: one NF4 block along K
 constexpr int LDS_LD = BK + 8;  // bf16 per LDS row: 16 B of padding keeps ds_read_b128 conflict-free
 
-struct Code16 {
-  float v[16];
-};
-
 __device__ __forceinline__ float scale_of(const ScaleSrc &sc, int64_t b) {
   if (sc.absmax_q) return (float)sc.absmax_q[b] * sc.scale2[b / QN_GROUP];
   return sc.absmax[b];
@@ -652,13 +648,6 @@ __global__ __launch_bounds__(kThreads) void gemv_epilogue_kernel(const float *__
 }
 
 // ================================================================ host side
-Code16 code16() {
-  Code16 c;
-  const CodecTables &t = codec_tables();
-  for (int i = 0; i < 16; ++i) c.v[i] = t.code[i];
-  return c;
-}
-
 int num_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -723,10 +712,11 @@ hipError_t run_skinny(const uint16_t *L, int64_t ldl, int64_t M, int64_t Kc, con
 }
 
 template <int BM, int BN, int WAVES_M, int RK, int EK, bool OUT_F32>
-hipError_t launch_gemm(GemmArgs ga, int splits, hipStream_t st) {
+hipError_t launch_gemm(GemmArgs ga, int splits, hipStream_t st, int trace_kind) {
   ga.tiles_m = (int)cdiv(ga.Mrows, BM);
   ga.tiles_n = (int)cdiv(ga.Nout, BN);
   dim3 grid((unsigned)(ga.tiles_m * ga.tiles_n), (unsigned)splits);
+  TraceScope tr(trace_kind, st);
   hipLaunchKernelGGL((gemm_kernel<BM, BN, WAVES_M, RK, EK, OUT_F32>), grid, dim3(kThreads), 0, st, ga, code16());
   return hipGetLastError();
 }
@@ -769,6 +759,7 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
                 row_blocks * splits, hkps};
     dim3 grid((unsigned)(row_blocks * splits + hsplits));
     const Code16 cb = code16();
+    TraceScope tr(QN_TRACE_GEMV, st);
     if (a.M == 1) hipLaunchKernelGGL(gemv_kernel<1>, grid, dim3(kThreads), 0, st, ga, cb);
     else if (a.M <= 2) hipLaunchKernelGGL(gemv_kernel<2>, grid, dim3(kThreads), 0, st, ga, cb);
     else if (a.M <= 4) hipLaunchKernelGGL(gemv_kernel<4>, grid, dim3(kThreads), 0, st, ga, cb);
@@ -788,13 +779,12 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)cdiv(a.M * 64, kThreads)), dim3(kThreads), 0, st,
                      h_part, sp, a.M, a.M, a.r, a.s, a.H_out, false, sH, rp, (uint16_t *)nullptr, (int64_t)0);
   QN_TRY(hipGetLastError());
-  GemmArgs g{};
-  g.L = a.X; g.ldl = a.K; g.Mrows = a.M; g.Nout = a.N; g.Kc = a.K; g.Kvalid = a.K;
-  g.codes = a.codes; g.sc = a.sc;
-  g.L2 = sH; g.ldl2 = rp; g.R2 = a.B; g.ldr2 = a.r; g.r2 = a.r;
-  g.out_bf16 = a.Y; g.ldo = a.N;
-  g.steps_per_split = a.K / BK;
-  return launch_gemm<128, 128, 2, R_NF4_NK, E_NK, false>(g, 1, st);
+  QGemmArgs g{};
+  g.L = a.X; g.ldl = a.K; g.M = a.M; g.Nout = a.N; g.Kc = a.K;
+  g.codes = a.codes; g.absmax = a.sc.absmax; g.absmax_q = a.sc.absmax_q; g.scale2 = a.sc.scale2;
+  g.L2 = sH; g.ldl2 = rp; g.R2 = a.B; g.ldr2 = a.r; g.r = a.r;
+  g.out = a.Y; g.ldo = a.N;
+  return launch_qgemm_fwd(g, st);
 }
 
 // ---------------------------------------------------------------- backward
@@ -858,7 +848,7 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
     const int64_t steps = Mp / BK;
     g.steps_per_split = cdiv(steps, sdb);
     const int splits = (int)cdiv(steps, g.steps_per_split);
-    QN_TRY((launch_gemm<32, 128, 1, R_BF16_KN, E_NONE, true>(g, splits, st)));
+    QN_TRY((launch_gemm<32, 128, 1, R_BF16_KN, E_NONE, true>(g, splits, st, QN_TRACE_GEMM_DB)));
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)cdiv(a.r * a.N, kThreads)), dim3(kThreads), 0, st,
                        gpart, splits, a.r, a.N, rp * a.N, true, a.dB);
     QN_TRY(hipGetLastError());
@@ -872,20 +862,19 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
     const int64_t steps = Mp / BK;
     g.steps_per_split = cdiv(steps, sda);
     const int splits = (int)cdiv(steps, g.steps_per_split);
-    QN_TRY((launch_gemm<32, 128, 1, R_BF16_KN, E_NONE, true>(g, splits, st)));
+    QN_TRY((launch_gemm<32, 128, 1, R_BF16_KN, E_NONE, true>(g, splits, st, QN_TRACE_GEMM_DA)));
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)cdiv(a.r * a.K, kThreads)), dim3(kThreads), 0, st,
                        gpart, splits, a.r, a.K, rp * a.K, false, a.dA);
     QN_TRY(hipGetLastError());
   }
   // dX [M, K] = dY [M, N] * W_hat [N, K] + dH [M, r] * A [r, K]
   if (a.dX) {
-    GemmArgs g{};
-    g.L = a.dY; g.ldl = a.N; g.Mrows = a.M; g.Nout = a.K; g.Kc = a.N; g.Kvalid = a.N;
-    g.codes = a.codes; g.sc = a.sc;
-    g.L2 = dHb; g.ldl2 = rp; g.R2 = a.A; g.ldr2 = a.K; g.r2 = a.r;
-    g.out_bf16 = a.dX; g.ldo = a.K;
-    g.steps_per_split = a.N / BK;
-    QN_TRY((launch_gemm<128, 128, 2, R_NF4_KN, E_KN, false>(g, 1, st)));
+    QGemmArgs g{};
+    g.L = a.dY; g.ldl = a.N; g.M = a.M; g.Nout = a.K; g.Kc = a.N;
+    g.codes = a.codes; g.absmax = a.sc.absmax; g.absmax_q = a.sc.absmax_q; g.scale2 = a.sc.scale2;
+    g.L2 = dHb; g.ldl2 = rp; g.R2 = a.A; g.ldr2 = a.K; g.r = a.r;
+    g.out = a.dX; g.ldo = a.K;
+    QN_TRY(launch_qgemm_dx(g, st));
   }
   return hipSuccess;
 }

@@ -30,6 +30,22 @@ bool codec_tables_ok();
 // Host: fp64 NF4 rows before rounding (exposed for the library's own checks).
 void nf4_rows_f64(double out[16]);
 
+// Kernel-level timing (trace.cpp).  While tracing is enabled, an object of this
+// type records a start event on construction and a stop event on destruction,
+// on the given stream, and logs the pair under `kind` (QN_TRACE_* codes).
+class TraceScope {
+ public:
+  TraceScope(int kind, hipStream_t s);
+  ~TraceScope();
+  TraceScope(const TraceScope &) = delete;
+  TraceScope &operator=(const TraceScope &) = delete;
+
+ private:
+  int kind_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
 // Kernel launchers (return hipError_t of the launch).
 hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, uint8_t *codes,
                            float *absmax, hipStream_t s);
@@ -43,6 +59,39 @@ struct ScaleSrc {
   const uint8_t *absmax_q;
   const float *scale2;
 };
+
+// The 16 NF4 rows passed by value to kernels that build LDS tables from them.
+struct Code16 {
+  float v[16];
+};
+Code16 code16();
+
+// Dequant-GEMM (k_qgemm.hip).  out[M, Nout] (bf16) =
+//   sum_k L[m, k] * W_hat(k, n)  +  sum_{j<r} L2[m, j] * R2(j, n)
+// where W_hat(k, n) = bf16(fl32(table[q] * scale)) of weight element
+//   (n, k) of codes [Nout, Kc]   (forward, "NK"), or
+//   (k, n) of codes [Kc, Nout]   (dX, "KN"),
+// and R2(j, n) = R2[n*ldr2 + j] (forward) or R2[j*ldr2 + n] (dX).
+// Requires Kc % 64 == 0 and Nout % 64 == 0.
+struct QGemmArgs {
+  const uint16_t *L;
+  int64_t ldl;
+  int64_t M, Nout, Kc;
+  const uint8_t *codes;
+  const float *absmax;
+  const uint8_t *absmax_q;
+  const float *scale2;
+  const uint16_t *L2;
+  int64_t ldl2;
+  const uint16_t *R2;
+  int64_t ldr2;
+  int64_t r;
+  uint16_t *out;
+  int64_t ldo;
+  int tiles_m, tiles_n, group_m;
+};
+hipError_t launch_qgemm_fwd(const QGemmArgs &a, hipStream_t s);
+hipError_t launch_qgemm_dx(const QGemmArgs &a, hipStream_t s);
 
 // Forward pieces.
 struct FwdArgs {

@@ -66,6 +66,8 @@ def load():
         "qlora_linear_bwd": (i32, [vp, vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp,
                                    vp, ctypes.c_size_t, vp]),
         "qn_status_string": (ctypes.c_char_p, [i32]),
+        "qn_trace_enable": (i32, [i32]),
+        "qn_trace_read": (i32, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float), i32]),
         "qn_version": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -78,7 +80,8 @@ def load():
 
 def exported_symbols():
     return ["qn_codebook", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_workspace_size",
-            "qlora_linear_fwd", "qlora_linear_bwd", "qn_status_string", "qn_version"]
+            "qlora_linear_fwd", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_trace_enable",
+            "qn_trace_read"]
 
 
 def status_string(status):
@@ -252,6 +255,24 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_
         _ptr(dY), _ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(dX), _ptr(dA),
         _ptr(dB), _ptr(ws), ws.numel(), _stream()))
     return dX, dA, dB
+
+
+TRACE_KINDS = {1: "quantize", 2: "double_quant", 3: "dequant", 4: "gemv", 5: "gemm_fwd", 6: "gemm_dx",
+               7: "gemm_db", 8: "gemm_da"}
+
+
+def trace_enable(on=True):
+    _check("qn_trace_enable", load().qn_trace_enable(1 if on else 0))
+
+
+def trace_read(cap=1 << 16):
+    """Wait for the logged kernels; returns a list of (kind name, milliseconds)."""
+    kinds = (ctypes.c_int * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = load().qn_trace_read(kinds, ms, cap)
+    if n < 0:
+        raise QNError("qn_trace_read", -n)
+    return [(TRACE_KINDS.get(kinds[i], str(kinds[i])), float(ms[i])) for i in range(n)]
 
 
 def raw():

@@ -159,6 +159,25 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M,
                      int64_t r, float alpha, void *dX, void *dA, void *dB,
                      void *workspace, size_t ws_bytes, void *stream);
 
+/* Kernel-level timing log, for measurement (off by default; costs nothing when
+ * off).  While enabled, each call brackets its dominant kernel with two HIP
+ * events recorded on the call's own stream and logs them under one of the
+ * QN_TRACE_* kinds below.  qn_trace_enable(1) clears the log and starts
+ * logging, qn_trace_enable(0) stops.  qn_trace_read() waits for the logged
+ * events, writes up to `cap` (kind, milliseconds) entries to host arrays,
+ * clears the log and returns the number written (negative qn_status on error).
+ * Not for use under HIP graph capture. */
+#define QN_TRACE_QUANTIZE 1      /* nf4_quantize kernel                          */
+#define QN_TRACE_DOUBLE_QUANT 2  /* nf4_double_quant kernel                      */
+#define QN_TRACE_DEQUANT 3       /* nf4_dequant kernel                           */
+#define QN_TRACE_GEMV 4          /* decode-path streaming kernel (fwd, M <= 8)   */
+#define QN_TRACE_GEMM_FWD 5      /* forward dequant-GEMM tile kernel (M > 8)     */
+#define QN_TRACE_GEMM_DX 6       /* backward dX dequant-GEMM tile kernel         */
+#define QN_TRACE_GEMM_DB 7       /* backward dB^T contraction over M             */
+#define QN_TRACE_GEMM_DA 8       /* backward dA contraction over M               */
+int qn_trace_enable(int on);
+int qn_trace_read(int *kinds, float *ms, int cap);
+
 /* Human-readable name of a qn_status (static storage). */
 const char *qn_status_string(int status);
 
