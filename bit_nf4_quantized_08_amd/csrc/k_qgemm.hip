@@ -9,30 +9,32 @@
 // -> fp32 product with the block scale -> bf16 (round to nearest even) -> LDS
 // tile -> v_mfma_f32_32x32x16_bf16.
 //
-// Tiling: a workgroup computes a 256 x 128 output tile with 8 waves in two
-// roles.  Four MMA waves (one per SIMD) each own a 128 x 64 sub-tile (4 x 2
-// MFMA tiles of 32 x 32) and do nothing but LDS operand reads and MFMAs.  Four
-// producer waves load the next activation tile and weight codes from global
-// memory, dequantise, and write the next LDS stage; sharing each SIMD with an
-// MMA wave, their VALU and memory work overlaps the matrix-core work.  The
-// contraction runs in steps of 64 (one NF4 block along K).  LDS holds two
-// stages of the activation tile (256 x 64 bf16) and the dequantised weight
-// tile (128 x 64 bf16), rows padded by 16 bytes so that the MFMA operand reads
-// (ds_read_b128) are free of bank conflicts.  One barrier per step: while the
-// MMA waves read stage s, the producers fill stage s+1 and have the global
-// loads of step s+2 in flight.
+// Tiling.  A workgroup computes a 256 x 128 output tile with 8 waves in two
+// roles.
+//   * Four MMA waves (one per SIMD), each owning 64 rows x 128 columns (2 x 4
+//     MFMA tiles of 32 x 32).  A wave loads its own activation rows straight
+//     from global memory into registers in MFMA operand layout (buffer loads,
+//     one step ahead), reads the dequantised weight fragments from LDS, and
+//     issues the MFMAs.  Activations never pass through LDS, which keeps LDS
+//     traffic at the weight tile: the resource this kernel is bound by.
+//   * Four producer waves load the weight codes and block scales of the next
+//     step, dequantise them and write the next LDS stage.  Sharing each SIMD
+//     with an MMA wave, their VALU work overlaps the matrix-core work.
+// The contraction runs in steps of 64 (one NF4 block along K), double-buffered
+// in LDS with one barrier per step.  Within a step, lane half h of an MMA wave
+// covers contraction indices [32h, 32h+32) (so its activation row slice is 64
+// contiguous bytes); slice c of the four MFMA k-slices uses [32h+8c, 32h+8c+8)
+// for both operands, which leaves the contraction unchanged.
 //
-// Two weight layouts:
+// Weight layouts:
 //   NK (forward): output column n reads weight row n, contraction along K; a
-//      lane dequantises 32 consecutive codes of one row (16 bytes).
-//   KN (dX): the contraction runs over the weight's rows; a lane dequantises a
-//      4 x 8 patch (4 rows, 8 columns) and writes it transposed (8 columns x 4
-//      contraction rows, 8 bytes each).  Lanes are ordered so that the 16
-//      lanes of a write group hit 16 distinct 8-byte slots of one 128-byte row
-//      segment: no bank conflicts.
-//
-// The adapter term runs as extra contraction steps over j < r (zero-padded)
-// into the same accumulators before the bf16 store.
+//      producer lane dequantises 32 consecutive codes of one row (16 bytes).
+//   KN (dX): the contraction runs over the weight's rows; a producer lane
+//      dequantises a 4 x 8 patch (4 rows, 8 columns) and writes it transposed.
+//      Lanes are ordered so that the 16 lanes of a write group hit 16 distinct
+//      8-byte slots of one 128-byte row segment: no bank conflicts.
+// The adapter term runs as extra contraction steps over j < r into the same
+// accumulators before the bf16 store.
 
 #include <algorithm>
 
@@ -45,13 +47,23 @@ namespace {
 constexpr int kThreads = 512;            // 4 MMA waves + 4 producer waves
 constexpr int kProducers = 256;
 constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int LD = BK + 8;            // bf16 per LDS row (16 B pad)
-constexpr int WM = 128, WN = 64;      // wave tile
-constexpr int TM = WM / 32, TN = WN / 32;
-constexpr int L_TILE = BM * LD;       // bf16 elements
-constexpr int R_TILE = BN * LD;
-constexpr int STAGE = L_TILE + R_TILE;
-constexpr int L_CHUNKS = BM * 8 / kProducers;  // 16-B chunks of the activation tile per producer lane (8)
+constexpr int LD = BK + 8;               // bf16 per LDS row of the weight tile (16 B pad)
+constexpr int WM = 64;                   // rows per MMA wave
+constexpr int TM = WM / 32, TN = BN / 32;
+constexpr int R_TILE = BN * LD;          // bf16 elements per weight stage
+constexpr int kPairCopies = 16;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // a per-lane offset that always reads zero
+
+// Buffer resource over [base, base + bytes); loads beyond `bytes` (by the
+// per-lane offset) return zero, which masks ragged tile edges.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int64_t cap = 0xFFFFFFF0LL;
+  const int n = (int)(uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcFlags);
+}
 
 __device__ __forceinline__ void tile_coords(int h, int tiles_m, int tiles_n, int gm_rows, int &tm, int &tn) {
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
@@ -71,50 +83,24 @@ __device__ __forceinline__ void tile_coords(int h, int tiles_m, int tiles_n, int
   tn = in / gm;
 }
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords
-
-// Buffer resource over [base, base + bytes); loads beyond `bytes` (by the
-// per-lane offset) return zero, which masks ragged tile edges.
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
-  const int64_t cap = 0xFFFFFFF0LL;
-  const int n = (int)(uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcFlags);
-}
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // a per-lane offset that always reads zero
-
-// Byte -> (row of low nibble, row of high nibble), 16 lane-interleaved copies:
-// entry e of copy c sits at index 16e + c, so the 16 lanes that a 64-bit LDS
-// read services together (lanes l with distinct l % 16) use distinct banks.
-constexpr int kPairCopies = 16;
-
+// ------------------------------------------------------------ producer waves
 template <bool KN, bool DQ>
 struct Producer {
-  // Register set for one contraction step.
   struct Set {
-    u32x4 l[L_CHUNKS];
     uint32_t code[4];
     uint32_t q[KN ? 4 : 1];
     float st[KN ? 4 : 1];
   };
-  rsrc_t rl, rc, rq, rs;
-  uint32_t lvoff[L_CHUNKS];
+  rsrc_t rc, rq, rs;
   uint32_t cvoff[KN ? 4 : 1];
   uint32_t qvoff[KN ? 4 : 1];
-  int64_t blk_base[KN ? 4 : 1];   // block index at step 0 (per row for KN)
+  int64_t blk_base[KN ? 4 : 1];   // block index at step 0
   int64_t blk_step;               // block index advance per step
   int row_nk, half_nk, kq, nc;
-  int64_t Kc, Nout;
+  int64_t Nout;
 
-  __device__ void init(const QGemmArgs &a, int tid, int64_t m0, int64_t n0) {
-    Kc = a.Kc;
+  __device__ void init(const QGemmArgs &a, int tid, int64_t n0) {
     Nout = a.Nout;
-    rl = make_rsrc(a.L + m0 * a.ldl, (a.M - m0) * a.ldl * 2);
-#pragma unroll
-    for (int c = 0; c < L_CHUNKS; ++c) {
-      const int idx = tid + c * kProducers;
-      lvoff[c] = (uint32_t)((idx >> 3) * a.ldl * 2 + (idx & 7) * 16);
-    }
     row_nk = tid >> 1;
     half_nk = tid & 1;
     kq = tid & 15;
@@ -140,28 +126,24 @@ struct Producer {
         const int64_t e = (int64_t)(4 * kq + i) * a.Nout + 8 * nc;   // relative to n0, step 0
         cvoff[i] = in ? (uint32_t)(e / 2) : kOutOfRange;
         blk_base[i] = ((4 * kq + i) * a.Nout + n0 + 8 * nc) / 64;
+        qvoff[i] = in ? 0u : kOutOfRange;
       }
       blk_step = BK * a.Nout / 64;
       if constexpr (DQ) rq = make_rsrc(a.absmax_q, a.Kc * a.Nout / 64);
       else rq = make_rsrc(a.absmax, a.Kc * a.Nout / 64 * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qvoff[i] = in ? 0u : kOutOfRange;
     }
     if constexpr (DQ) rs = make_rsrc(a.scale2, (a.Nout * a.Kc / 64 + 255) / 256 * 4);
   }
 
   __device__ __forceinline__ void issue(Set &t, int64_t s) {
-    const int soff_l = (int)(s * BK * 2);
-#pragma unroll
-    for (int c = 0; c < L_CHUNKS; ++c) t.l[c] = __builtin_amdgcn_raw_buffer_load_b128(rl, lvoff[c], soff_l, 0);
     if constexpr (!KN) {
       const u32x4 c4 = __builtin_amdgcn_raw_buffer_load_b128(rc, cvoff[0], (int)(s * 32), 0);
       t.code[0] = c4.x; t.code[1] = c4.y; t.code[2] = c4.z; t.code[3] = c4.w;
       const int64_t b = blk_base[0] + s;
       if constexpr (DQ) {
         t.q[0] = __builtin_amdgcn_raw_buffer_load_b8(rq, qvoff[0], (int)s, 0);
-        t.st[0] = as_f32(__builtin_amdgcn_raw_buffer_load_b32(rs, qvoff[0] == kOutOfRange ? kOutOfRange
-                                                                                          : (uint32_t)((b >> 8) * 4), 0, 0));
+        t.st[0] = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
+            rs, qvoff[0] == kOutOfRange ? kOutOfRange : (uint32_t)((b >> 8) * 4), 0, 0));
       } else {
         t.q[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, qvoff[0], (int)(s * 4), 0);
       }
@@ -188,13 +170,7 @@ struct Producer {
     else return as_f32(t.q[i]);
   }
 
-  __device__ __forceinline__ void store(const Set &t, uint16_t *Ls, uint16_t *Rs, const float2 *pair, int tid,
-                                        int lane) const {
-#pragma unroll
-    for (int c = 0; c < L_CHUNKS; ++c) {
-      const int idx = tid + c * kProducers;
-      *reinterpret_cast<u32x4 *>(&Ls[(idx >> 3) * LD + (idx & 7) * 8]) = t.l[c];
-    }
+  __device__ __forceinline__ void store(const Set &t, uint16_t *Rs, const float2 *pair, int lane) const {
     const int copy = lane & (kPairCopies - 1);
     if constexpr (!KN) {
       const float A = scale(t, 0);
@@ -230,17 +206,12 @@ struct Producer {
   }
 };
 
-// Adapter-term tiles for extra contraction step `s` (j in [64s, 64s+64)),
-// zero-padded, loaded by `nt` threads starting at thread `t`.
+// Adapter-term right operand for extra contraction step `e` (j in [64e, 64e+64)),
+// zero-padded, written to a weight stage by `nt` threads starting at thread `t`.
 template <bool EPI_NK>
-__device__ __forceinline__ void load_adapter_tiles(const QGemmArgs &a, int64_t m0, int64_t n0, int64_t s,
-                                                   uint16_t *Ls, uint16_t *Rs, int t, int nt) {
-  const int64_t j0 = s * BK;
-  for (int idx = t; idx < BM * BK; idx += nt) {
-    const int row = idx >> 6, jj = idx & 63;
-    const int64_t gm = m0 + row, gj = j0 + jj;
-    Ls[row * LD + jj] = (gm < a.M && gj < a.r) ? a.L2[gm * a.ldl2 + gj] : (uint16_t)0;
-  }
+__device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n0, int64_t e, uint16_t *Rs, int t,
+                                                   int nt) {
+  const int64_t j0 = e * BK;
   for (int idx = t; idx < BN * BK; idx += nt) {
     int row, jj;
     if constexpr (EPI_NK) { row = idx >> 6; jj = idx & 63; }
@@ -252,13 +223,13 @@ __device__ __forceinline__ void load_adapter_tiles(const QGemmArgs &a, int64_t m
   }
 }
 
-// Exactly one workgroup (2 waves per SIMD) fits a CU (LDS bound), so tell the
-// compiler that higher occupancy is not reachable: it then keeps a whole
-// step's MFMA operands in registers instead of re-reading them one by one.
+// Exactly one workgroup (2 waves per SIMD) fits a CU, so tell the compiler
+// that higher occupancy is not reachable: it may then keep a whole step's
+// operands in registers instead of re-reading them one by one.
 template <bool KN, bool DQ, bool EPI_NK>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qgemm_kernel(QGemmArgs a, Code16 cb) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t wst[2 * R_TILE];
   __shared__ __attribute__((aligned(16))) float2 pair[256 * kPairCopies];
   for (int i = threadIdx.x; i < 256 * kPairCopies; i += kThreads) {
     const int e = i / kPairCopies;
@@ -271,136 +242,155 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool producer = wave >= 4;
   const int64_t steps = a.Kc / BK;
+  const int64_t epi_steps = (a.r + BK - 1) / BK;
   __syncthreads();  // pair table
 
-  f32x16 acc[TM][TN];
   if (producer) {
-    // ---------------------------------------------------------- producer waves
     const int tid = threadIdx.x - kProducers;
     Producer<KN, DQ> P;
-    P.init(a, tid, m0, n0);
+    P.init(a, tid, n0);
     typename Producer<KN, DQ>::Set s0, s1;
     if (steps > 0) P.issue(s0, 0);
     if (steps > 1) P.issue(s1, 1);
-    if (steps > 0) P.store(s0, lds, lds + L_TILE, pair, tid, lane);
+    if (steps > 0) P.store(s0, wst, pair, lane);
     if (steps > 2) P.issue(s0, 2);
     __syncthreads();
     // Step s: the MMA waves read stage s & 1; store step s+1 into the other
     // stage from its register set, then reuse that set for step s+3.
     for (int64_t s = 0; s < steps; s += 2) {
       if (s + 1 < steps) {
-        uint16_t *st1 = lds + STAGE;
-        P.store(s1, st1, st1 + L_TILE, pair, tid, lane);
+        P.store(s1, wst + R_TILE, pair, lane);
         if (s + 3 < steps) P.issue(s1, s + 3);
       }
       __syncthreads();
       if (s + 1 >= steps) break;
       if (s + 2 < steps) {
-        P.store(s0, lds, lds + L_TILE, pair, tid, lane);
+        P.store(s0, wst, pair, lane);
         if (s + 4 < steps) P.issue(s0, s + 4);
       }
       __syncthreads();
     }
-    // Adapter steps: help fill the tiles; same barrier count as the MMA waves.
-    const int64_t epi_steps = (a.r + BK - 1) / BK;
     for (int64_t e = 0; e < epi_steps; ++e) {
-      load_adapter_tiles<EPI_NK>(a, m0, n0, e, lds, lds + L_TILE, threadIdx.x, kThreads);
+      load_adapter_right<EPI_NK>(a, n0, e, wst, threadIdx.x, kThreads);
       __syncthreads();
       __syncthreads();
     }
-  } else {
-    // ---------------------------------------------------------- MMA waves
-    const int wm = wave & 1, wn = wave >> 1;
-    const int lr = lane & 31, lh = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    // Operand fragments for one 16-deep slice (kk) of a step: 4 A + 2 B, 16 B
-    // each.  The reads for the next slice are issued before the MFMAs of the
-    // current one, so LDS latency hides behind matrix-core work; at a step's
-    // last slice the barrier sits between that step's final reads and the next
-    // step's first reads.
-    struct Frag {
-      bf16x8 a[TM], b[TN];
-    };
-    auto read = [&](Frag &f, int stage, int kk) {
-      const uint16_t *Ls = lds + stage * STAGE;
-      const uint16_t *Rs = Ls + L_TILE;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        f.a[i] = *reinterpret_cast<const bf16x8 *>(&Ls[(wm * WM + i * 32 + lr) * LD + kk * 16 + lh * 8]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        f.b[j] = *reinterpret_cast<const bf16x8 *>(&Rs[(wn * WN + j * 32 + lr) * LD + kk * 16 + lh * 8]);
-    };
-    auto mma = [&](const Frag &f) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-    };
-    // One step from `stage`: f0 holds slice 0 on entry; on exit f0 holds slice 0
-    // of the next step (read after the barrier) if `more`.
-    auto step = [&](Frag &f0, Frag &f1, int stage, bool more) {
-      read(f1, stage, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f0);
-      read(f0, stage, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f1);
-      read(f1, stage, 3);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f0);
-      __syncthreads();
-      if (more) read(f0, stage ^ 1, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f1);
-    };
-    // Same barrier count as the producers: one before the loop, one per step.
-    __syncthreads();
-    Frag f0, f1;
-    if (steps > 0) read(f0, 0, 0);
-    for (int64_t s = 0; s < steps; s += 2) {
-      step(f0, f1, 0, s + 1 < steps);
-      if (s + 1 >= steps) break;
-      step(f0, f1, 1, s + 2 < steps);
-    }
-    auto compute = [&](int stage) {
-      Frag f;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        read(f, stage, kk);
-        mma(f);
-      }
-    };
-
-    // ---- adapter term: contraction over j < r (zero-padded steps of 64),
-    // tiles filled by all 8 waves into stage 0.
-    const int64_t epi_steps = (a.r + BK - 1) / BK;
-    for (int64_t e = 0; e < epi_steps; ++e) {
-      load_adapter_tiles<EPI_NK>(a, m0, n0, e, lds, lds + L_TILE, threadIdx.x, kThreads);
-      __syncthreads();
-      compute(0);
-      __syncthreads();
-    }
-
-    // ---- store bf16: element e of a 32x32 tile is row 8*(e/4)+4*lh+(e%4), column lr.
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t gn = n0 + wn * WN + j * 32 + lr;
-        if (gn >= a.Nout) continue;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t gm = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          if (gm < a.M) a.out[gm * a.ldo + gn] = f32_to_bf16(acc[i][j][e]);
-        }
-      }
+    return;
   }
+
+  // ---------------------------------------------------------- MMA waves
+  const int lr = lane & 31, lh = lane >> 5;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Activation operand: row m0 + wave*64 + i*32 + lr, contraction indices
+  // [32*lh, 32*lh + 32) of each step: 4 x 16 B per row tile.
+  const rsrc_t rl = make_rsrc(a.L + m0 * a.ldl, (a.M - m0) * a.ldl * 2);
+  uint32_t avoff[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) avoff[i] = (uint32_t)((wave * WM + i * 32 + lr) * a.ldl * 2 + lh * 64);
+  struct ASet {
+    u32x4 v[TM][4];
+  };
+  auto issue_a = [&](ASet &A, int64_t s) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        A.v[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rl, avoff[i] + 16 * c, (int)(s * BK * 2), 0);
+  };
+  struct BFrag {
+    bf16x8 b[TN];
+  };
+  auto read_b = [&](BFrag &f, int stage, int c) {
+    const uint16_t *Rs = wst + stage * R_TILE;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&Rs[(j * 32 + lr) * LD + lh * 32 + c * 8]);
+  };
+  auto mma = [&](const ASet &A, int c, const BFrag &f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, A.v[i][c]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, f.b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // One step from `stage`: b0 holds slice 0 on entry; on exit b0 holds slice 0
+  // of the next step (read after the barrier) if `more`.
+  auto step = [&](const ASet &A, BFrag &b0, BFrag &b1, int stage, bool more) {
+    read_b(b1, stage, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(A, 0, b0);
+    read_b(b0, stage, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(A, 1, b1);
+    read_b(b1, stage, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(A, 2, b0);
+    __syncthreads();
+    if (more) read_b(b0, stage ^ 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(A, 3, b1);
+  };
+
+  ASet A0, A1;
+  if (steps > 0) issue_a(A0, 0);
+  if (steps > 1) issue_a(A1, 1);
+  __syncthreads();
+  BFrag b0, b1;
+  if (steps > 0) read_b(b0, 0, 0);
+  for (int64_t s = 0; s < steps; s += 2) {
+    step(A0, b0, b1, 0, s + 1 < steps);
+    if (s + 2 < steps) issue_a(A0, s + 2);
+    if (s + 1 >= steps) break;
+    step(A1, b0, b1, 1, s + 2 < steps);
+    if (s + 3 < steps) issue_a(A1, s + 3);
+  }
+
+  // ---- adapter term: contraction over j < r, zero-padded to steps of 64.  The
+  // left operand (leading dim ldl2, readable up to column ldl2, a multiple of 8
+  // zero-padded beyond r) is loaded like the activations; the right operand
+  // goes through weight stage 0.
+  const rsrc_t rl2 = make_rsrc(a.L2 + m0 * a.ldl2, (a.M - m0) * a.ldl2 * 2);
+  for (int64_t e = 0; e < epi_steps; ++e) {
+    ASet A;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int64_t j = e * BK + lh * 32 + c * 8;
+        const uint32_t off = j < a.ldl2 ? (uint32_t)(((wave * WM + i * 32 + lr) * a.ldl2 + j) * 2) : kOutOfRange;
+        A.v[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rl2, off, 0, 0);
+      }
+    load_adapter_right<EPI_NK>(a, n0, e, wst, threadIdx.x, kThreads);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      BFrag f;
+      read_b(f, 0, c);
+      mma(A, c, f);
+    }
+    __syncthreads();
+  }
+
+  // ---- store bf16: element e of a 32x32 tile is row 8*(e/4)+4*lh+(e%4), column lr.
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t gn = n0 + j * 32 + lr;
+      if (gn >= a.Nout) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t gm = m0 + wave * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+        if (gm < a.M) a.out[gm * a.ldo + gn] = f32_to_bf16(acc[i][j][e]);
+      }
+    }
 }
 
 int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
@@ -412,8 +402,7 @@ hipError_t launch(const QGemmArgs &a0, hipStream_t st, int trace_kind) {
   a.tiles_n = (int)cdiv(a.Nout, BN);
   // Row-tile group size: each XCD runs T/8 tiles; choose the group so that an
   // XCD's share covers about as many activation bytes (rows x Kc x 2) as weight
-  // bytes (columns x Kc / 2): rows_g * 256 * 2 ~ cols_g * 128 / 2 with
-  // rows_g * cols_g = T / 8.
+  // bytes (columns x Kc / 2).
   {
     const int T8 = std::max(1, a.tiles_m * a.tiles_n / 8);
     int best = 1;
