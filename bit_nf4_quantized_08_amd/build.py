@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqlora_nf4.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "codebook.cpp", "trace.cpp", "k_codec.hip", "k_linear.hip", "k_qgemm.hip"]
+SOURCES = ["api.cpp", "codebook.cpp", "trace.cpp", "k_codec.hip", "k_linear.hip", "k_qgemm.hip", "k_lowrank.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are kept out of all device code.

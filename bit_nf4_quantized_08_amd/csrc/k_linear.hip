@@ -739,8 +739,6 @@ size_t fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
     c.take<float>((int64_t)splits * M * N);
     c.take<float>((int64_t)hsplits * M * 64);
   } else {
-    const int sp = skinny_splits(M, K);
-    c.take<float>((int64_t)sp * M * 64);
     c.take<uint16_t>(M * align_up(r, 8));
   }
   return c.off;
@@ -769,16 +767,17 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
                        y_part, splits, h_part, hsplits, a.M, a.N, a.r, a.B, a.s, a.Y, a.H_out);
     return hipGetLastError();
   }
-  // MFMA path: H = X A^T (skinny, split-K) -> sH bf16 -> tile GEMM with the
+  // MFMA path: H = X A^T (low-rank kernel) -> sH bf16 -> tile GEMM with the
   // adapter term as extra contraction steps.
-  const int sp = skinny_splits(a.M, a.K);
-  float *h_part = c.take<float>((int64_t)sp * a.M * 64);
   const int64_t rp = align_up(a.r, 8);
   uint16_t *sH = c.take<uint16_t>(a.M * rp);
-  QN_TRY(run_skinny(a.X, a.K, a.M, a.K, a.A, a.K, a.r, h_part, sp, st));
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)cdiv(a.M * 64, kThreads)), dim3(kThreads), 0, st,
-                     h_part, sp, a.M, a.M, a.r, a.s, a.H_out, false, sH, rp, (uint16_t *)nullptr, (int64_t)0);
-  QN_TRY(hipGetLastError());
+  {
+    LowRankArgs la{};
+    la.L = a.X; la.ldl = a.K; la.M = a.M; la.Kc = a.K;
+    la.P = a.A; la.ldp = a.K; la.R = a.r; la.scale = a.s;
+    la.out_f32 = a.H_out; la.out_b = sH; la.ldb = rp; la.out_t = nullptr; la.Mp = a.M;
+    QN_TRY(launch_lowrank(la, st));
+  }
   QGemmArgs g{};
   g.L = a.X; g.ldl = a.K; g.M = a.M; g.Nout = a.N; g.Kc = a.K;
   g.codes = a.codes; g.absmax = a.sc.absmax; g.absmax_q = a.sc.absmax_q; g.scale2 = a.sc.scale2;
@@ -800,13 +799,10 @@ size_t bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t rp = align_up(r, 32);
   const int64_t Mp = align_up(M, BK);
   c.take<uint16_t>(rp * N);                 // B^T
-  const int sp1 = skinny_splits(M, N), sp2 = skinny_splits(M, K);
-  c.take<float>((int64_t)std::max(sp1, sp2) * M * 64);  // skinny partials
   c.take<uint16_t>(M * rp);                 // dH bf16 [M, rp]
   c.take<uint16_t>(rp * Mp);                // dH^T bf16 [rp, Mp]
   c.take<uint16_t>(rp * Mp);                // (sH)^T bf16 [rp, Mp]
-  const int sdb = gemm_splits(cdiv(N, 128), Mp / BK), sda = gemm_splits(cdiv(K, 128), Mp / BK);
-  c.take<float>(std::max<int64_t>((int64_t)sdb * rp * N, (int64_t)sda * rp * K));
+  c.take<float>((int64_t)colred_splits(M) * r * std::max(N, K));
   return c.off;
 }
 
@@ -815,57 +811,44 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
   const int64_t rp = align_up(a.r, 32);
   const int64_t Mp = align_up(a.M, BK);
   uint16_t *Bt = c.take<uint16_t>(rp * a.N);
-  const int sp1 = skinny_splits(a.M, a.N), sp2 = skinny_splits(a.M, a.K);
-  float *part = c.take<float>((int64_t)std::max(sp1, sp2) * a.M * 64);
   uint16_t *dHb = c.take<uint16_t>(a.M * rp);
   uint16_t *dHt = c.take<uint16_t>(rp * Mp);
   uint16_t *sHt = c.take<uint16_t>(rp * Mp);
-  const int sdb = gemm_splits(cdiv(a.N, 128), Mp / BK), sda = gemm_splits(cdiv(a.K, 128), Mp / BK);
-  float *gpart = c.take<float>(std::max<int64_t>((int64_t)sdb * rp * a.N, (int64_t)sda * rp * a.K));
+  float *gpart = c.take<float>((int64_t)colred_splits(a.M) * a.r * std::max(a.N, a.K));
 
   // B^T [rp, N] (rows >= r zero) so that dH = dY (B^T)^T runs on the skinny kernel.
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(rp * a.N, kThreads)), dim3(kThreads), 0, st,
                      a.B, a.N, a.r, a.r, Bt, rp);
   QN_TRY(hipGetLastError());
   // dH = s dY B  -> dHb [M, rp], dHt [rp, Mp]
-  QN_TRY(run_skinny(a.dY, a.N, a.M, a.N, Bt, a.N, a.r, part, sp1, st));
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)cdiv(Mp * 64, kThreads)), dim3(kThreads), 0, st,
-                     part, sp1, a.M, Mp, a.r, a.s, (float *)nullptr, false, dHb, rp, dHt, rp);
-  QN_TRY(hipGetLastError());
-  // H = X A^T -> (sH)^T [rp, Mp]
-  QN_TRY(run_skinny(a.X, a.K, a.M, a.K, a.A, a.K, a.r, part, sp2, st));
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)cdiv(Mp * 64, kThreads)), dim3(kThreads), 0, st,
-                     part, sp2, a.M, Mp, a.r, a.s, (float *)nullptr, false, (uint16_t *)nullptr, (int64_t)0, sHt,
-                     rp);
-  QN_TRY(hipGetLastError());
-
-  // dB^T [r, N] = (sH)^T [rp, Mp] * dY [M, N]   (contraction over M, split-K)
   {
-    GemmArgs g{};
-    g.L = sHt; g.ldl = Mp; g.Mrows = rp; g.Nout = a.N; g.Kc = Mp; g.Kvalid = a.M;
-    g.P = a.dY; g.ldp = a.N;
-    g.out_f32 = gpart; g.ldo = a.N; g.split_stride = rp * a.N;
-    const int64_t steps = Mp / BK;
-    g.steps_per_split = cdiv(steps, sdb);
-    const int splits = (int)cdiv(steps, g.steps_per_split);
-    QN_TRY((launch_gemm<32, 128, 1, R_BF16_KN, E_NONE, true>(g, splits, st, QN_TRACE_GEMM_DB)));
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)cdiv(a.r * a.N, kThreads)), dim3(kThreads), 0, st,
-                       gpart, splits, a.r, a.N, rp * a.N, true, a.dB);
-    QN_TRY(hipGetLastError());
+    LowRankArgs la{};
+    la.L = a.dY; la.ldl = a.N; la.M = a.M; la.Kc = a.N;
+    la.P = Bt; la.ldp = a.N; la.R = a.r; la.scale = a.s;
+    la.out_b = dHb; la.ldb = rp; la.out_t = dHt; la.ldt_rows = rp; la.Mp = Mp;
+    QN_TRY(launch_lowrank(la, st));
   }
-  // dA [r, K] = dH^T [rp, Mp] * X [M, K]
+  // H = X A^T -> (sH)^T [rp, Mp]
   {
-    GemmArgs g{};
-    g.L = dHt; g.ldl = Mp; g.Mrows = rp; g.Nout = a.K; g.Kc = Mp; g.Kvalid = a.M;
-    g.P = a.X; g.ldp = a.K;
-    g.out_f32 = gpart; g.ldo = a.K; g.split_stride = rp * a.K;
-    const int64_t steps = Mp / BK;
-    g.steps_per_split = cdiv(steps, sda);
-    const int splits = (int)cdiv(steps, g.steps_per_split);
-    QN_TRY((launch_gemm<32, 128, 1, R_BF16_KN, E_NONE, true>(g, splits, st, QN_TRACE_GEMM_DA)));
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)cdiv(a.r * a.K, kThreads)), dim3(kThreads), 0, st,
-                       gpart, splits, a.r, a.K, rp * a.K, false, a.dA);
-    QN_TRY(hipGetLastError());
+    LowRankArgs la{};
+    la.L = a.X; la.ldl = a.K; la.M = a.M; la.Kc = a.K;
+    la.P = a.A; la.ldp = a.K; la.R = a.r; la.scale = a.s;
+    la.out_t = sHt; la.ldt_rows = rp; la.Mp = Mp;
+    QN_TRY(launch_lowrank(la, st));
+  }
+
+  // dB [N, r] = ((sH)^T dY)^T and dA [r, K] = dH^T X: contractions over M.
+  {
+    ColRedArgs ca{};
+    ca.Lt = sHt; ca.Mp = Mp; ca.Q = a.dY; ca.ldq = a.N; ca.M = a.M; ca.Ncols = a.N; ca.R = a.r;
+    ca.part = gpart; ca.out = a.dB; ca.transpose = true;
+    QN_TRY(launch_colred(ca, st, QN_TRACE_GEMM_DB));
+  }
+  {
+    ColRedArgs ca{};
+    ca.Lt = dHt; ca.Mp = Mp; ca.Q = a.X; ca.ldq = a.K; ca.M = a.M; ca.Ncols = a.K; ca.R = a.r;
+    ca.part = gpart; ca.out = a.dA; ca.transpose = false;
+    QN_TRY(launch_colred(ca, st, QN_TRACE_GEMM_DA));
   }
   // dX [M, K] = dY [M, N] * W_hat [N, K] + dH [M, r] * A [r, K]
   if (a.dX) {

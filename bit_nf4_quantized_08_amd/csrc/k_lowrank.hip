@@ -1,0 +1,275 @@
+// Low-rank products of the adapter path on gfx950: C[M, R] = L[M, Kc] * P[R, Kc]^T
+// with R <= 64.  Used for H = X A^T (forward and backward) and dH = dY B (with
+// P = B^T).
+//
+// "LoRA vs QLoRA: Efficient Fine-Tuning Explained", "How LoRA Works": the
+// adapter's two thin factors, B (d x r) and A (r x k), r small (8 to 64); the
+// product through them is cheap next to the base weight, and this kernel
+// streams the activations once at HBM rate.
+//
+// A workgroup of 8 waves owns 16 rows.  The contraction is cut into 32-wide
+// chunks dealt round-robin to the 8 waves; each wave accumulates its chunks with
+// v_mfma_f32_16x16x32_bf16 (lane group g = lane/16 takes indices [8g, 8g+8) of
+// a chunk for both operands), keeping sixteen chunks of loads in flight.  The 8
+// partial 16 x R results are summed in LDS in a fixed order, and the workgroup
+// writes the requested outputs directly: fp32 unscaled, bf16 scaled
+// (row-major, zero-padded to ldb columns), bf16 scaled and transposed
+// (zero-padded to ldt_rows rows and Mp columns).  No split partials in global
+// memory, no second pass.
+
+#include <algorithm>
+
+#include "qn_device.h"
+#include "qn_internal.h"
+
+namespace qn {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int ROWS = 16;
+constexpr int CHUNK = 32;
+constexpr int UNROLL = 16;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int64_t cap = 0xFFFFFFF0LL;
+  const int n = (int)(uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+template <int RT>  // 16-column tiles of the output: R <= 16 * RT
+__global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankArgs a) {
+  __shared__ float red[kWaves][ROWS][RT * 16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * ROWS;
+
+  const rsrc_t rl = make_rsrc(a.L + m0 * a.ldl, (a.M - m0) * a.ldl * 2);
+  const rsrc_t rp = make_rsrc(a.P, a.R * a.ldp * 2);
+  const uint32_t lvoff = (uint32_t)(lr * a.ldl * 2 + lg * 16);
+  uint32_t pvoff[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int j = t * 16 + lr;
+    pvoff[t] = j < a.R ? (uint32_t)(j * a.ldp * 2 + lg * 16) : kOutOfRange;
+  }
+
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t chunks = a.Kc / CHUNK;
+  for (int64_t q0 = wave; q0 < chunks; q0 += (int64_t)kWaves * UNROLL) {
+    u32x4 xv[UNROLL], pv[UNROLL][RT];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t q = q0 + (int64_t)u * kWaves;
+      const bool in = q < chunks;
+      const int soff = (int)(q * CHUNK * 2);
+      xv[u] = in ? __builtin_amdgcn_raw_buffer_load_b128(rl, lvoff, soff, 0) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        pv[u][t] = in ? __builtin_amdgcn_raw_buffer_load_b128(rp, pvoff[t], soff, 0) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[u]),
+                                                        __builtin_bit_cast(bf16x8, pv[u][t]), acc[t], 0, 0, 0);
+  }
+
+  // acc[t][e] is row 4*lg + e, column 16*t + lr.
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][4 * lg + e][16 * t + lr] = acc[t][e];
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < ROWS * RT * 16; idx += kThreads) {
+    const int row = idx / (RT * 16), j = idx % (RT * 16);
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += red[w][row][j];
+    const int64_t m = m0 + row;
+    const uint16_t b = (j < a.R) ? f32_to_bf16(v * a.scale) : (uint16_t)0;
+    if (m < a.M) {
+      if (a.out_f32 && j < a.R) a.out_f32[m * a.R + j] = v;
+      if (a.out_b && j < a.ldb) a.out_b[m * a.ldb + j] = b;
+    }
+    if (a.out_t && j < a.ldt_rows && m < a.Mp) a.out_t[(int64_t)j * a.Mp + m] = b;
+  }
+  // Columns of out_b between RT*16 and ldb (only when ldb > RT*16) are zero.
+  if (a.out_b && a.ldb > RT * 16) {
+    for (int idx = threadIdx.x; idx < ROWS * (a.ldb - RT * 16); idx += kThreads) {
+      const int row = idx / (int)(a.ldb - RT * 16), j = RT * 16 + idx % (int)(a.ldb - RT * 16);
+      const int64_t m = m0 + row;
+      if (m < a.M) a.out_b[m * a.ldb + j] = 0;
+    }
+  }
+  if (a.out_t && a.ldt_rows > RT * 16) {
+    for (int idx = threadIdx.x; idx < ROWS * (a.ldt_rows - RT * 16); idx += kThreads) {
+      const int row = idx % ROWS, j = RT * 16 + idx / ROWS;
+      const int64_t m = m0 + row;
+      if (m < a.Mp) a.out_t[(int64_t)j * a.Mp + m] = 0;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lowrank(const LowRankArgs &a, hipStream_t st) {
+  const int64_t rows = std::max(a.M, a.out_t ? a.Mp : a.M);
+  const dim3 grid((unsigned)((rows + ROWS - 1) / ROWS));
+  TraceScope tr(QN_TRACE_LOWRANK, st);
+  if (a.R <= 16) hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(kThreads), 0, st, a);
+  else if (a.R <= 32) hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(lowrank_kernel<4>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace qn
+
+// ----------------------------------------------------------------------------
+// Column-streaming reduction over rows: out[j][c] = sum_m Lt[j][m] * Q[m][c] for
+// j < R (R <= 64), used for dA = dH^T X and dB^T = (s H)^T dY, where the
+// contraction runs down the rows of the row-major activations.  Lt is [Rp, Mp]
+// bf16, zero beyond R and M.
+//
+// A workgroup (4 waves) owns 128 columns (2 per lane) and a range of RB rows;
+// each wave takes every fourth pair of rows.  Two rows of Q are paired per
+// column with one byte permute and multiplied by the pair (Lt[j][m],
+// Lt[j][m+1]) with v_dot2_f32_bf16, so Q is read exactly once.  The factor
+// slice for the row range sits in LDS as [row pair][j] dwords (broadcast
+// reads).  Per-split partial sums go to `part`; a second kernel adds the
+// splits in order and rounds to bf16.
+namespace qn {
+namespace {
+
+constexpr int CR_THREADS = 256;
+constexpr int CR_COLS = 128;
+constexpr int CR_RB = 128;        // rows per split
+constexpr int CR_PAIRS = CR_RB / 2;
+
+template <int R>
+__global__ __launch_bounds__(CR_THREADS) void colred_kernel(ColRedArgs a) {
+  constexpr int RJ = R < 16 ? R : 16;            // rows of the output reduced per pass
+  __shared__ uint32_t lt[CR_PAIRS * R];          // (Lt[j][2p], Lt[j][2p+1]) at [p][j]
+  __shared__ float red[4][RJ][CR_COLS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * CR_COLS;
+  const int split = blockIdx.y;
+  const int64_t mb = (int64_t)split * CR_RB;
+
+  // Activation loads first (all of this wave's row pairs), so their latency
+  // overlaps the factor preload below.
+  const rsrc_t rq = make_rsrc(a.Q + mb * a.ldq, (a.M - mb) * a.ldq * 2);
+  const int64_t c = c0 + 2 * lane;
+  const bool cin = c < a.Ncols;
+  const uint32_t qoff = cin ? (uint32_t)(c * 2) : kOutOfRange;
+  constexpr int U = CR_PAIRS / 4;
+  uint32_t q[U][2];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int p = wave + 4 * u;
+    const uint32_t r0 = (uint32_t)(2 * p) * (uint32_t)(a.ldq * 2);
+    q[u][0] = cin ? __builtin_amdgcn_raw_buffer_load_b32(rq, qoff + r0, 0, 0) : 0u;
+    q[u][1] = cin ? __builtin_amdgcn_raw_buffer_load_b32(rq, qoff + r0 + (uint32_t)(a.ldq * 2), 0, 0) : 0u;
+  }
+
+  // Factor slice: rows j < R, columns [mb, mb + RB) of Lt (always inside Mp).
+  for (int idx = tid; idx < CR_PAIRS * R; idx += CR_THREADS) {
+    const int j = idx / CR_PAIRS, p = idx % CR_PAIRS;
+    const int64_t m = mb + 2 * p;
+    uint32_t v = 0;
+    if (j < a.R && m < a.Mp) v = *reinterpret_cast<const uint32_t *>(a.Lt + (int64_t)j * a.Mp + m);
+    lt[p * R + j] = v;
+  }
+  __syncthreads();
+
+  float acc0[R], acc1[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) acc0[j] = acc1[j] = 0.0f;
+  {
+    const int p0 = wave;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + 4 * u;
+      // (Q[m][c], Q[m+1][c]) and (Q[m][c+1], Q[m+1][c+1])
+      const uint32_t pc0 = __builtin_amdgcn_perm(q[u][1], q[u][0], 0x05040100u);
+      const uint32_t pc1 = __builtin_amdgcn_perm(q[u][1], q[u][0], 0x07060302u);
+      const uint32_t *lrow = &lt[p * R];
+#pragma unroll
+      for (int j4 = 0; j4 < R; j4 += 4) {
+        const u32x4 l4 = *reinterpret_cast<const u32x4 *>(lrow + j4);
+        const uint32_t lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc0[j4 + t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lv[t]), __builtin_bit_cast(bf16x2, pc0),
+                                                         acc0[j4 + t], false);
+          acc1[j4 + t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lv[t]), __builtin_bit_cast(bf16x2, pc1),
+                                                         acc1[j4 + t], false);
+        }
+      }
+    }
+  }
+
+  // Add the 4 waves' partials in a fixed order, RJ output rows per pass.
+#pragma unroll
+  for (int jb = 0; jb < R; jb += RJ) {
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      red[wave][j][2 * lane] = acc0[jb + j];
+      red[wave][j][2 * lane + 1] = acc1[jb + j];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < RJ * CR_COLS; idx += CR_THREADS) {
+      const int j = idx / CR_COLS, cc = idx % CR_COLS;
+      const int64_t col = c0 + cc;
+      if (jb + j < a.R && col < a.Ncols) {
+        const float v = red[0][j][cc] + red[1][j][cc] + red[2][j][cc] + red[3][j][cc];
+        a.part[((int64_t)split * a.R + jb + j) * a.Ncols + col] = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// out = bf16(sum over splits of part), as [R][Ncols] or transposed [Ncols][R].
+__global__ __launch_bounds__(256) void colred_reduce_kernel(const float *__restrict__ part, int splits, int64_t R,
+                                                            int64_t Ncols, bool transpose, uint16_t *__restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= R * Ncols) return;
+  int64_t j, col;
+  if (transpose) { col = idx / R; j = idx % R; }
+  else { j = idx / Ncols; col = idx % Ncols; }
+  float v = 0.0f;
+  for (int s = 0; s < splits; ++s) v += part[((int64_t)s * R + j) * Ncols + col];
+  out[idx] = f32_to_bf16(v);
+}
+
+}  // namespace
+
+int colred_splits(int64_t M) { return (int)((M + CR_RB - 1) / CR_RB); }
+
+hipError_t launch_colred(const ColRedArgs &a, hipStream_t st, int trace_kind) {
+  const int splits = colred_splits(a.M);
+  const dim3 grid((unsigned)((a.Ncols + CR_COLS - 1) / CR_COLS), (unsigned)splits);
+  {
+    TraceScope tr(trace_kind, st);
+    if (a.R <= 8) hipLaunchKernelGGL(colred_kernel<8>, grid, dim3(CR_THREADS), 0, st, a);
+    else if (a.R <= 16) hipLaunchKernelGGL(colred_kernel<16>, grid, dim3(CR_THREADS), 0, st, a);
+    else if (a.R <= 32) hipLaunchKernelGGL(colred_kernel<32>, grid, dim3(CR_THREADS), 0, st, a);
+    else hipLaunchKernelGGL(colred_kernel<64>, grid, dim3(CR_THREADS), 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(colred_reduce_kernel, dim3((unsigned)((a.R * a.Ncols + 255) / 256)), dim3(256), 0, st, a.part,
+                     splits, a.R, a.Ncols, a.transpose, a.out);
+  return hipGetLastError();
+}
+
+}  // namespace qn

@@ -93,6 +93,40 @@ struct QGemmArgs {
 hipError_t launch_qgemm_fwd(const QGemmArgs &a, hipStream_t s);
 hipError_t launch_qgemm_dx(const QGemmArgs &a, hipStream_t s);
 
+// Low-rank product (k_lowrank.hip): C[M, R] = L[M, Kc] * P[R, Kc]^T, R <= 64,
+// Kc % 32 == 0.  Writes any of: out_f32 [M, R] (unscaled), out_b [M, ldb] =
+// bf16(scale * C) zero beyond R, out_t [ldt_rows, Mp] = bf16(scale * C)^T zero
+// beyond R and beyond M (Mp >= M).
+struct LowRankArgs {
+  const uint16_t *L;
+  int64_t ldl, M, Kc;
+  const uint16_t *P;
+  int64_t ldp, R;
+  float scale;
+  float *out_f32;
+  uint16_t *out_b;
+  int64_t ldb;
+  uint16_t *out_t;
+  int64_t ldt_rows, Mp;
+};
+hipError_t launch_lowrank(const LowRankArgs &a, hipStream_t s);
+
+// Column-streaming reduction over rows (k_lowrank.hip): out = bf16(sum_m
+// Lt[j][m] * Q[m][c]) for j < R <= 64, as [R][Ncols] or transposed [Ncols][R].
+// Lt is [>= R rows, Mp] bf16 zero beyond M; Q is [M, Ncols] bf16, leading dim
+// ldq.  `part` holds colred_splits(M) * R * Ncols floats.
+struct ColRedArgs {
+  const uint16_t *Lt;
+  int64_t Mp;
+  const uint16_t *Q;
+  int64_t ldq, M, Ncols, R;
+  float *part;
+  uint16_t *out;
+  bool transpose;
+};
+int colred_splits(int64_t M);
+hipError_t launch_colred(const ColRedArgs &a, hipStream_t s, int trace_kind);
+
 // Forward pieces.
 struct FwdArgs {
   const uint16_t *X;     // bf16 [M,K]

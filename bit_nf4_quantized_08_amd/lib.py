@@ -258,7 +258,7 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_
 
 
 TRACE_KINDS = {1: "quantize", 2: "double_quant", 3: "dequant", 4: "gemv", 5: "gemm_fwd", 6: "gemm_dx",
-               7: "gemm_db", 8: "gemm_da"}
+               7: "gemm_db", 8: "gemm_da", 9: "lowrank"}
 
 
 def trace_enable(on=True):

@@ -175,6 +175,7 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M,
 #define QN_TRACE_GEMM_DX 6       /* backward dX dequant-GEMM tile kernel         */
 #define QN_TRACE_GEMM_DB 7       /* backward dB^T contraction over M             */
 #define QN_TRACE_GEMM_DA 8       /* backward dA contraction over M               */
+#define QN_TRACE_LOWRANK 9       /* X A^T or dY B low-rank product               */
 int qn_trace_enable(int on);
 int qn_trace_read(int *kinds, float *ms, int cap);
 
