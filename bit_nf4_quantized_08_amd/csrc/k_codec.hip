@@ -163,72 +163,80 @@ __global__ __launch_bounds__(kThreads) void double_quant_kernel(const float *__r
 }
 
 // ---------------------------------------------------------------- dequant
-// One lane expands 32 consecutive elements (16 bytes of codes, half a block)
-// through a 256-entry byte -> (row lo, row hi) table in LDS.
+// A wave expands 2048 consecutive elements per iteration (1 KB of codes).  Its
+// 32 block scales are computed by lanes 0..31 and handed out with a lane
+// shuffle.  Each store instruction of the wave writes one contiguous 1 KB span:
+// bf16 output, 8 elements (one 32-bit word of codes) per lane per instruction;
+// fp32 output, 4 elements (16 bits of codes) per lane per instruction.  The
+// byte -> (row lo, row hi) table lives in LDS, one copy per lane of a 16-lane
+// group so that the lookups of a group hit distinct banks.
 __device__ __forceinline__ float block_scale(const ScaleSrc &sc, int64_t b) {
   if (sc.absmax_q) return (float)sc.absmax_q[b] * sc.scale2[b / QN_GROUP];
   return sc.absmax[b];
 }
 
+constexpr int kDqChunk = 2048;   // elements per wave iteration
+constexpr int kDqCopies = 16;
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ codes, ScaleSrc sc,
                                                            int64_t n, void *__restrict__ out,
                                                            CodecTables tab) {
-  __shared__ float2 pair[256];
-  {
-    const uint32_t v = threadIdx.x;
-    pair[v] = make_float2(tab.code[v & 15], tab.code[v >> 4]);
+  __shared__ float2 pair[256 * kDqCopies];
+  for (int i = threadIdx.x; i < 256 * kDqCopies; i += kThreads) {
+    const int v = i / kDqCopies;
+    pair[i] = make_float2(tab.code[v & 15], tab.code[v >> 4]);
   }
   __syncthreads();
-  const int64_t nchunks = (n + 31) / 32;
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < nchunks;
-       t += (int64_t)gridDim.x * kThreads) {
-    const int64_t e0 = t * 32;
-    const float A = block_scale(sc, e0 / QN_BLOCK);
-    if (e0 + 32 <= n) {
-      const u32x4 cw = ld_stream(codes + 16 * t);
-      const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-      if constexpr (OUT_BF16) {
-        uint32_t o[16];
+  const int lane = threadIdx.x & 63;
+  const int copy = lane & (kDqCopies - 1);
+  const int64_t wave_id = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int64_t full = n / kDqChunk;
+  for (int64_t ch = wave_id; ch < full; ch += nwaves) {
+    const int64_t base = ch * kDqChunk;
+    const float my_scale = lane < 32 ? block_scale(sc, base / QN_BLOCK + lane) : 0.0f;
+    if constexpr (OUT_BF16) {
+      uint32_t cw[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
+        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + base / 2) + i * 64 + lane);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float2 c = pair[(w[i] >> (8 * j)) & 0xFF];
-            o[4 * i + j] = pack_bf16x2(c.x * A, c.y * A);
-          }
+      for (int i = 0; i < 4; ++i) {
+        // elements base + (i*64 + lane)*8 .. +8: block (i*64 + lane)/8 of the chunk
+        const float A = __shfl(my_scale, i * 8 + (lane >> 3), 64);
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float2 c = pair[((cw[i] >> (8 * j)) & 0xFF) * kDqCopies + copy];
+          o[j] = pack_bf16x2(c.x * A, c.y * A);
         }
-        uint16_t *dst = static_cast<uint16_t *>(out) + e0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 ov = {o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
-          st_stream(dst + 8 * i, ov);
-        }
-      } else {
-        float *dst = static_cast<float *>(out) + e0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float2 c0 = pair[w[i] & 0xFF];
-          const float2 c1 = pair[(w[i] >> 8) & 0xFF];
-          const float2 c2 = pair[(w[i] >> 16) & 0xFF];
-          const float2 c3 = pair[w[i] >> 24];
-          const f32x4 o0 = {c0.x * A, c0.y * A, c1.x * A, c1.y * A};
-          const f32x4 o1 = {c2.x * A, c2.y * A, c3.x * A, c3.y * A};
-          st_stream_f4(dst + 8 * i, o0);
-          st_stream_f4(dst + 8 * i + 4, o1);
-        }
+        st_stream(static_cast<uint16_t *>(out) + base + (int64_t)(i * 64 + lane) * 8, u32x4{o[0], o[1], o[2], o[3]});
       }
     } else {
-      for (int64_t e = e0; e < n; ++e) {
-        const uint8_t byte = codes[e >> 1];
-        const uint32_t q = (e & 1) ? (byte >> 4) : (byte & 15);
-        const float w = pair[q].x * A;
-        if constexpr (OUT_BF16) {
-          static_cast<uint16_t *>(out)[e] = f32_to_bf16(w);
-        } else {
-          static_cast<float *>(out)[e] = w;
-        }
+      uint32_t cw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(codes + base / 2) + i * 64 + lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // elements base + (i*64 + lane)*4 .. +4: block (i*64 + lane)/16 of the chunk
+        const float A = __shfl(my_scale, i * 4 + (lane >> 4), 64);
+        const float2 c0 = pair[(cw[i] & 0xFF) * kDqCopies + copy];
+        const float2 c1 = pair[((cw[i] >> 8) & 0xFF) * kDqCopies + copy];
+        st_stream_f4(static_cast<float *>(out) + base + (int64_t)(i * 64 + lane) * 4,
+                     f32x4{c0.x * A, c0.y * A, c1.x * A, c1.y * A});
       }
+    }
+  }
+  // Tail (fewer than 2048 elements): one element per lane of the first wave.
+  if (wave_id == 0) {
+    for (int64_t e = full * kDqChunk + lane; e < n; e += 64) {
+      const uint8_t byte = codes[e >> 1];
+      const uint32_t q = (e & 1) ? (byte >> 4) : (byte & 15);
+      const float w = pair[q * kDqCopies].x * block_scale(sc, e / QN_BLOCK);
+      if constexpr (OUT_BF16) static_cast<uint16_t *>(out)[e] = f32_to_bf16(w);
+      else static_cast<float *>(out)[e] = w;
     }
   }
 }
@@ -278,7 +286,7 @@ hipError_t launch_dequant(const qn_nf4_weight &W, void *out, int out_bf16, hipSt
   const CodecTables &tab = codec_tables();
   const int64_t n = W.N * W.K;
   ScaleSrc sc{W.absmax, W.absmax_q, W.scale2};
-  const int grid = grid_for((n + 31) / 32);
+  const int grid = grid_for((n + 7) / 8);
   TraceScope tr(QN_TRACE_DEQUANT, s);
   if (out_bf16)
     hipLaunchKernelGGL(dequant_kernel<true>, dim3(grid), dim3(kThreads), 0, s, W.codes, sc, n, out, tab);
