@@ -1,10 +1,10 @@
 """Throughput of the NF4 / QLoRA-linear hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of the single
-4096x4096 projection workload (W ~ N(0, 0.02) as bf16, LoRA r = 16,
+4096x4096 projection workload (W ~ N(0, 0.02) in fp32, LoRA r = 16,
 alpha = 32):
 
-  quantise W (bf16 -> NF4 codes + fp32 absmax)      nf4_quantize
+  quantise W (fp32 -> NF4 codes + fp32 absmax)      nf4_quantize
   double-quantise the absmax                         nf4_double_quant
   dequantise a weight to bf16                        nf4_dequant
   decode forward, X: 1 x 4096                        qlora_linear_fwd (M = 1)
@@ -23,14 +23,27 @@ host launch gaps.  `value` is the step's algorithmic contraction work
 (prefill forward + backward + decode GEMV, FLOPs counted as 2 per
 multiply-add, dequant work not counted) divided by the step time.
 
+Each stage is then timed alone (`stages.stage_us_graph`): a graph of
+back-to-back calls of that stage, replayed between two HIP events; the
+bandwidth-bound stages cycle through more distinct buffers than the
+Infinity Cache holds.  The quantise and decode figures of `metrics` come from
+these loops (per call, so the decode figure includes its epilogue kernel).
+
 A second, eager pass over the same steps enables the library's kernel trace:
 HIP events recorded around each call's dominant kernel on its own launch
 stream.  Its per-kernel average durations give the per-stage figures in
 `stages` and the `roofline` object (for the kernel with the largest share of
 the step).  `cpu_baseline` times the CPU oracle on a bounded sample.
+
+`roofline.traffic` is the HBM bytes per launch of that kernel read from
+rocprofv3 FETCH_SIZE and WRITE_SIZE counters (table `TRAFFIC` below, each
+counter scaled by what it reads for a plain copy of known size, taken with
+`--copy-calibration`); it is null when no such measurement exists for the
+kernel source as it is now.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -45,6 +58,40 @@ PEAK_BF16_TFLOPS = 2500.0
 N, K, R, ALPHA = 4096, 4096, 16, 32.0
 M_DEC, M_PRE = 1, 2048
 SLOTS = 4
+STAGE_REPS, STAGE_REPLAYS = 8, 5
+CSRC = os.path.join(ROOT, "bit_nf4_quantized_08_amd", "csrc")
+KERNEL_SOURCE = {
+    "quantize": "k_codec.hip", "double_quant": "k_codec.hip", "dequant": "k_codec.hip",
+    "gemv": "k_linear.hip", "gemm_fwd": "k_qgemm.hip", "gemm_dx": "k_qgemm.hip",
+    "lowrank": "k_lowrank.hip", "gemm_db": "k_lowrank.hip", "gemm_da": "k_lowrank.hip",
+}
+# Measured HBM bytes per launch: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per
+# dispatch), each scaled by the ratio of known bytes to counted bytes for a 256 MiB
+# copy in the same run.  Keyed by kernel; `sha256` is that of the kernel's source
+# file and qn_device.h when the counters were taken.
+TRAFFIC = {  # profiles/qlora_step_4096_hbm_traffic.md
+    "dequant": {"bytes": 42308229, "sha256": "7cc4ff9fd5317e838f1218950094ab0df45bb777c8ffb967ded48206eed8c6c9"},
+    "double_quant": {"bytes": 1372028, "sha256": "7cc4ff9fd5317e838f1218950094ab0df45bb777c8ffb967ded48206eed8c6c9"},
+    "gemv": {"bytes": 9238715, "sha256": "e2c9c7a8c8501cd2a70a38a7a28dca8bf000a60cc63373838c8f8a4a67072ca7"},
+    "gemm_fwd": {"bytes": 85977974, "sha256": "b016d16203d871666b2270d3c09616f962d10eafb54c3bed0aea9fe8d35d5392"},
+    "gemm_dx": {"bytes": 87195201, "sha256": "b016d16203d871666b2270d3c09616f962d10eafb54c3bed0aea9fe8d35d5392"},
+    "quantize": {"bytes": 80814358, "sha256": "7cc4ff9fd5317e838f1218950094ab0df45bb777c8ffb967ded48206eed8c6c9"},
+}
+
+
+def source_sha(kind):
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE[kind], "qn_device.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic(kind):
+    t = TRAFFIC.get(kind)
+    if t is None or t["sha256"] != source_sha(kind):
+        return None
+    return t["bytes"]
 
 
 def sizes():
@@ -54,7 +101,7 @@ def sizes():
     w_bytes = n // 2 + nb + 4 * ng
     return dict(
         n=n, nb=nb, ng=ng,
-        quantize_bytes=2 * n + n // 2 + 4 * nb,
+        quantize_bytes=4 * n + n // 2 + 4 * nb,
         dq_bytes=4 * nb + nb + 4 * ng,
         dequant_bytes=w_bytes + 2 * n,
         gemv_weight_bytes=w_bytes,
@@ -67,9 +114,12 @@ def sizes():
     )
 
 
-def cpu_baseline():
-    """Time the CPU oracle on a bounded sample of the same workload: the codec on
-    four 4096x4096 bf16 weights, and the step's fp64 contractions in full."""
+def cpu_baseline(min_seconds=12.0, max_steps=24):
+    """Time the CPU oracle on a bounded sample of the same workload: whole oracle
+    steps (quantise, double quant and bf16 dequant of one 4096x4096 fp32 weight,
+    then the step's fp64 contractions: decode M=1, prefill M=2048 forward and
+    backward) repeated until `min_seconds` have passed.  The value is the step's
+    contraction FLOPs over the oracle's step time, as for the GPU figure."""
     import numpy as np
     import oracle
     from bit_nf4_quantized_08_amd import synth
@@ -78,39 +128,41 @@ def cpu_baseline():
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
-    tiles = 4
     s = sizes()
-    t_q = t_codec = 0.0
-    for t in range(tiles):
-        W = synth.bf16_values(synth.to_bf16(synth.gaussian((N, K), 0.02, synth.SEED_BULK0 + t)))
+    X = synth.bf16_values(synth.to_bf16(synth.gaussian((M_PRE, K), 1.0, synth.SEED_X)))
+    A = synth.bf16_values(synth.to_bf16(synth.gaussian((R, K), 0.01, synth.SEED_A)))
+    B = synth.bf16_values(synth.to_bf16(synth.gaussian((N, R), 0.01, synth.SEED_B)))
+    dY = synth.bf16_values(synth.to_bf16(synth.gaussian((M_PRE, N), 1.0, synth.SEED_DY)))
+    t_codec = t_q = t_mm = 0.0
+    steps = 0
+    while steps < max_steps and (steps < 2 or t_codec + t_mm < min_seconds):
+        W = synth.gaussian((N, K), 0.02, synth.SEED_BULK0 + steps)
         t0 = time.perf_counter()
         packed, absmax, _ = oracle.quantize(W)
         t1 = time.perf_counter()
         k, step = oracle.double_quant(absmax)
         Wh = oracle.dequant_bf16_weight(packed, N, K, oracle.dq_absmax(k, step))
         t2 = time.perf_counter()
+        oracle.forward(X[:M_DEC], Wh, A, B, ALPHA)
+        oracle.forward(X, Wh, A, B, ALPHA)
+        oracle.backward(dY, X, Wh, A, B, ALPHA)
+        t3 = time.perf_counter()
         t_q += t1 - t0
         t_codec += t2 - t0
-    X = synth.bf16_values(synth.to_bf16(synth.gaussian((M_PRE, K), 1.0, synth.SEED_X)))
-    A = synth.bf16_values(synth.to_bf16(synth.gaussian((R, K), 0.01, synth.SEED_A)))
-    B = synth.bf16_values(synth.to_bf16(synth.gaussian((N, R), 0.01, synth.SEED_B)))
-    dY = synth.bf16_values(synth.to_bf16(synth.gaussian((M_PRE, N), 1.0, synth.SEED_DY)))
-    t2 = time.perf_counter()
-    oracle.forward(X[:M_DEC], Wh, A, B, ALPHA)
-    oracle.forward(X, Wh, A, B, ALPHA)
-    oracle.backward(dY, X, Wh, A, B, ALPHA)
-    t3 = time.perf_counter()
+        t_mm += t3 - t2
+        steps += 1
     flops = s["gemv_flops"] + s["fwd_flops"] + s["bwd_flops"]
     return {
-        "value": flops / (t3 - t2) / 1e12,
+        "value": flops * steps / (t_codec + t_mm) / 1e12,
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": (f"codec (quantise, double quant, dequant) on {tiles} 4096x4096 bf16 weights: "
-                   f"{t_codec:.2f} s, quantise {tiles * s['quantize_bytes'] / t_q / 1e9:.3f} GB/s on 1 core; "
-                   f"the step's fp64 contractions in full (decode M=1, prefill M=2048 forward and "
-                   f"backward): {t3 - t2:.2f} s on {blas_threads} BLAS threads"),
-        "quantize_GBps": tiles * s["quantize_bytes"] / t_q / 1e9,
+        "sample": (f"{steps} whole oracle steps of the same workload in {t_codec + t_mm:.1f} s: codec "
+                   f"(quantise, double quant, bf16 dequant of a fresh 4096x4096 fp32 weight) "
+                   f"{t_codec / steps:.2f} s/step on 1 core, fp64 contractions {t_mm / steps:.2f} s/step "
+                   f"on {blas_threads} BLAS threads"),
+        "ms_per_step": (t_codec + t_mm) * 1e3 / steps,
+        "quantize_GBps": steps * s["quantize_bytes"] / t_q / 1e9,
         "host_cpus": os.cpu_count(),
     }
 
@@ -121,6 +173,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the run, copy 256 MiB three times (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -139,7 +193,7 @@ def main():
     def randn(shape, std):
         return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
 
-    Ws = [randn((N, K), 0.02) for _ in range(SLOTS)]
+    Ws = [torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02 for _ in range(SLOTS)]
     Xd = randn((M_DEC, K), 1.0)
     Xp = randn((M_PRE, K), 1.0)
     A = randn((R, K), 0.01)
@@ -211,6 +265,61 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
+    # ---- each stage alone: a graph of STAGE_REPS back-to-back calls (rotating
+    # weight slots), replayed; HIP events around the replays on the capture stream
+    def stage_fns(i):
+        w = slots[(i + 2) % SLOTS]
+        return {
+            "quantize": lambda: lib.nf4_quantize(Ws[i % SLOTS], codes=slots[i % SLOTS].codes,
+                                                 absmax=slots[i % SLOTS].absmax),
+            "double_quant": lambda: lib.nf4_double_quant(slots[i % SLOTS].absmax, absmax_q=slots[i % SLOTS].absmax_q,
+                                                         scale2=slots[i % SLOTS].scale2),
+            "dequant": lambda: lib.nf4_dequant(w, "bf16", out=deq),
+            "fwd_decode": lambda: lib.qlora_linear_fwd(Xd, w, A, B, ALPHA, Y=Yd, ws=ws_dec),
+            "fwd_prefill": lambda: lib.qlora_linear_fwd(Xp, w, A, B, ALPHA, Y=Yp, ws=ws_pre),
+            "bwd": lambda: lib.qlora_linear_bwd(dY, Xp, w, A, B, ALPHA, out=(dX, dA, dB), ws=ws_bwd),
+        }
+    # Bandwidth-bound stages cycle through more distinct buffers than the 256 MB
+    # Infinity Cache holds: 8 fp32 weights (512 MiB) to quantise, 64 NF4 weights
+    # (553 MB) to dequantise or multiply at M = 1.
+    wq_pool = [Ws[j % SLOTS].clone() for j in range(8)]
+    nf_pool = [lib.NF4Weight(slots[j % SLOTS].codes.clone(), slots[j % SLOTS].absmax.clone(),
+                             slots[j % SLOTS].absmax_q.clone(), slots[j % SLOTS].scale2.clone(), N, K)
+               for j in range(64)]
+    pool_fns = {
+        "quantize": (8, lambda i: lib.nf4_quantize(wq_pool[i], codes=slots[i % SLOTS].codes,
+                                                   absmax=slots[i % SLOTS].absmax)),
+        "dequant": (64, lambda i: lib.nf4_dequant(nf_pool[i], "bf16", out=deq)),
+        "fwd_decode": (64, lambda i: lib.qlora_linear_fwd(Xd, nf_pool[i], A, B, ALPHA, Y=Yd, ws=ws_dec)),
+    }
+    stage_us = {}
+    for name in stage_fns(0):
+        reps, fn = pool_fns.get(name, (STAGE_REPS, None))
+        sg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sg, stream=cap):
+            for i in range(reps):
+                if fn is None:
+                    stage_fns(i)[name]()
+                else:
+                    fn(i)
+        for _ in range(2):
+            sg.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(cap):
+            e0.record(cap)
+            for _ in range(STAGE_REPLAYS):
+                sg.replay()
+            e1.record(cap)
+        torch.cuda.synchronize()
+        stage_us[name] = e0.elapsed_time(e1) * 1e3 / (STAGE_REPLAYS * reps)
+        del sg
+    del wq_pool, nf_pool
+    # the quantise stages overwrote slot contents with the same values; restore order
+    for i in range(SLOTS):
+        quantize(i)
+    torch.cuda.synchronize()
+
     # ---- traced eager pass over the same steps: per-kernel durations
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     lib.trace_enable(True)
@@ -252,22 +361,24 @@ def main():
         if bound == "hbm":
             ach = amount / (avg * 1e-3) / 1e9
             return {"kernel": kind, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
-                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic(kind),
                     "avg_ms": round(avg, 5), "work_per_launch": amount}
         ach = amount / (avg * 1e-3) / 1e12
         return {"kernel": kind, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic(kind),
                 "avg_ms": round(avg, 5), "work_per_launch": amount}
 
     dominant = max((k for k in kern_per_step if k in work), key=lambda k: kern_per_step[k])
     stages = {
-        "prefill_fwd_call_TFLOPs_eager": round(s["fwd_flops"] / (stage_ms["fwd_prefill"] * 1e-3) / 1e12, 1),
+        "stage_us_graph": {k: round(v, 2) for k, v in stage_us.items()},
+        "prefill_fwd_call_TFLOPs": round(s["fwd_flops"] / (stage_us["fwd_prefill"] * 1e-6) / 1e12, 1),
         "prefill_fwd_gemm_kernel_TFLOPs": round(s["fwd_gemm_kernel_flops"] / (kern_avg["gemm_fwd"] * 1e-3) / 1e12, 1),
-        "bwd_call_TFLOPs_eager": round(s["bwd_flops"] / (stage_ms["bwd"] * 1e-3) / 1e12, 1),
-        "decode_call_weight_GBps_eager": round(s["gemv_weight_bytes"] / (stage_ms["fwd_decode"] * 1e-3) / 1e9, 1),
-        "decode_gemv_kernel_weight_GBps": round(s["gemv_weight_bytes"] / (kern_avg["gemv"] * 1e-3) / 1e9, 1),
-        "quantize_GBps": round(s["quantize_bytes"] / (kern_avg["quantize"] * 1e-3) / 1e9, 1),
-        "dequant_GBps": round(s["dequant_bytes"] / (kern_avg["dequant"] * 1e-3) / 1e9, 1),
+        "bwd_call_TFLOPs": round(s["bwd_flops"] / (stage_us["bwd"] * 1e-6) / 1e12, 1),
+        "decode_call_weight_GBps": round(s["gemv_weight_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
+        "decode_call_all_GBps": round(s["gemv_all_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
+        "quantize_GBps": round(s["quantize_bytes"] / (stage_us["quantize"] * 1e-6) / 1e9, 1),
+        "double_quant_GBps": round(s["dq_bytes"] / (stage_us["double_quant"] * 1e-6) / 1e9, 1),
+        "dequant_GBps": round(s["dequant_bytes"] / (stage_us["dequant"] * 1e-6) / 1e9, 1),
         "stage_ms_eager_traced": {k: round(v, 4) for k, v in stage_ms.items()},
         "eager_traced_ms_per_step": round((te1 - te0) * 1e3 / args.steps, 4),
         "kernel_avg_ms": {k: round(v, 5) for k, v in kern_avg.items()},
@@ -287,11 +398,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "single 4096x4096 projection: NF4 bs64 + double quant bs256, LoRA r=16 alpha=32, "
-                               "decode M=1 and prefill M=2048 forward, backward at M=2048, bf16 weight source",
+                               "decode M=1 and prefill M=2048 forward, backward at M=2048, fp32 weight source",
                    "N": N, "K": K, "r": R, "alpha": ALPHA, "M_decode": M_DEC, "M_prefill": M_PRE},
         "metrics": {
             "prefill_dequant_gemm_TFLOPs": stages["prefill_fwd_gemm_kernel_TFLOPs"],
-            "decode_gemv_weight_GBps": stages["decode_gemv_kernel_weight_GBps"],
+            "decode_gemv_weight_GBps": stages["decode_call_weight_GBps"],
             "quantize_GBps": stages["quantize_GBps"],
         },
         "roofline": roof(dominant),
@@ -300,6 +411,13 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copy calibration: 3 x 268435456 B read + written", file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":
