@@ -30,9 +30,12 @@
 //   NK (forward): output column n reads weight row n, contraction along K; a
 //      producer lane dequantises 32 consecutive codes of one row (16 bytes).
 //   KN (dX): the contraction runs over the weight's rows; a producer lane
-//      dequantises a 4 x 8 patch (4 rows, 8 columns) and writes it transposed.
-//      Lanes are ordered so that the 16 lanes of a write group hit 16 distinct
-//      8-byte slots of one 128-byte row segment: no bank conflicts.
+//      loads 32 codes of one row (16 bytes, one block), the four lanes of a
+//      quad transpose their words with DPP so that each lane holds a 4 x 8
+//      patch (4 rows, 8 columns), and the patch is written transposed.
+// The stage layout is XOR-swizzled in 16-byte chunks so that both the
+// producers' writes and the MMA waves' fragment reads are free of bank
+// conflicts.
 // The adapter term runs as extra contraction steps over j < r into the same
 // accumulators before the bf16 store.
 
@@ -83,97 +86,109 @@ __device__ __forceinline__ void tile_coords(int h, int tiles_m, int tiles_n, int
   tn = in / gm;
 }
 
+// LDS weight stage: output column `col` (a row of the stage, LD bf16 long)
+// holds contraction positions 0..63.  Position k is stored at k ^ kswz(col):
+// the XOR moves whole 8-element chunks, so every 16-byte fragment stays
+// contiguous, and it spreads the producers' writes over all 64 banks while
+// the MMA reads (16 consecutive columns per quarter wave) stay conflict-free.
+__device__ __forceinline__ int kswz(int col) { return 32 * ((col >> 4) & 1) + 8 * ((col >> 5) & 3); }
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t qperm(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
 // ------------------------------------------------------------ producer waves
+// NK: producer thread t owns output column row_nk = 16*(t>>5) + (t&15) and the
+// contraction half (t>>4)&1 of each step: 32 codes = 16 contiguous bytes.
+// KN: the weight's rows are the contraction.  Thread t = 4q + j loads the 32
+// codes of contraction row 4*(q&15) + j, columns 32*(q>>4) .. +31 (16 bytes,
+// one block), then the four lanes of a quad transpose their 4-byte words so
+// that lane j holds columns 32*(q>>4) + 8j .. +7 of all four rows: each column
+// then has 4 consecutive contraction positions, written as one 8-byte store.
 template <bool KN, bool DQ>
 struct Producer {
   struct Set {
     uint32_t code[4];
-    uint32_t q[KN ? 4 : 1];
-    float st[KN ? 4 : 1];
+    uint32_t q;
+    float st;
   };
   rsrc_t rc, rq, rs;
-  uint32_t cvoff[KN ? 4 : 1];
-  uint32_t qvoff[KN ? 4 : 1];
-  int64_t blk_base[KN ? 4 : 1];   // block index at step 0
-  int64_t blk_step;               // block index advance per step
-  int row_nk, half_nk, kq, nc;
+  uint32_t cvoff, qvoff;
+  int64_t blk_base, blk_step;
+  int soff_c;                     // code byte advance per step
+  int wr_col, wr_k;               // LDS position written by this thread
   int64_t Nout;
 
   __device__ void init(const QGemmArgs &a, int tid, int64_t n0) {
     Nout = a.Nout;
-    row_nk = tid >> 1;
-    half_nk = tid & 1;
-    kq = tid & 15;
-    nc = tid >> 4;
     if constexpr (!KN) {
+      const int row = ((tid >> 5) << 4) | (tid & 15), half = (tid >> 4) & 1;
       rc = make_rsrc(a.codes + n0 * (a.Kc / 2), (a.Nout - n0) * (a.Kc / 2));
-      cvoff[0] = (uint32_t)(row_nk * (a.Kc / 2) + half_nk * 16);
-      blk_base[0] = (n0 + row_nk) * (a.Kc / 64);
+      cvoff = (uint32_t)(row * (a.Kc / 2) + half * 16);
+      soff_c = BK / 2;
+      blk_base = (n0 + row) * (a.Kc / 64);
       blk_step = 1;
       if constexpr (DQ) {
         rq = make_rsrc(a.absmax_q + n0 * (a.Kc / 64), (a.Nout - n0) * (a.Kc / 64));
-        qvoff[0] = (uint32_t)(row_nk * (a.Kc / 64));
+        qvoff = (uint32_t)(row * (a.Kc / 64));
       } else {
         rq = make_rsrc(a.absmax + n0 * (a.Kc / 64), (a.Nout - n0) * (a.Kc / 64) * 4);
-        qvoff[0] = (uint32_t)(row_nk * (a.Kc / 64) * 4);
+        qvoff = (uint32_t)(row * (a.Kc / 64) * 4);
       }
-      if (n0 + row_nk >= a.Nout) cvoff[0] = qvoff[0] = kOutOfRange;
+      if (n0 + row >= a.Nout) cvoff = qvoff = kOutOfRange;
+      wr_col = row;
+      wr_k = half * 32;
     } else {
-      rc = make_rsrc(a.codes + n0 / 2, a.Kc * a.Nout / 2 - n0 / 2);
-      const bool in = n0 + 8 * nc < a.Nout;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t e = (int64_t)(4 * kq + i) * a.Nout + 8 * nc;   // relative to n0, step 0
-        cvoff[i] = in ? (uint32_t)(e / 2) : kOutOfRange;
-        blk_base[i] = ((4 * kq + i) * a.Nout + n0 + 8 * nc) / 64;
-        qvoff[i] = in ? 0u : kOutOfRange;
-      }
-      blk_step = BK * a.Nout / 64;
+      const int q = tid >> 2, j = tid & 3, rr = 4 * (q & 15) + j, cb = 32 * (q >> 4);
+      const bool in = n0 + cb < a.Nout;
+      const int64_t e0 = (int64_t)rr * a.Nout + n0 + cb;   // element at step 0
+      rc = make_rsrc(a.codes, a.Kc * a.Nout / 2);
+      cvoff = in ? (uint32_t)(e0 / 2) : kOutOfRange;
+      soff_c = (int)(BK / 2 * a.Nout);
+      blk_base = e0 >> 6;                                   // 32 codes lie in one block
+      blk_step = a.Nout;                                    // BK rows of Nout / 64 blocks
+      qvoff = in ? 0u : kOutOfRange;
       if constexpr (DQ) rq = make_rsrc(a.absmax_q, a.Kc * a.Nout / 64);
       else rq = make_rsrc(a.absmax, a.Kc * a.Nout / 64 * 4);
+      wr_col = cb + 8 * j;
+      wr_k = 4 * (q & 15);
     }
     if constexpr (DQ) rs = make_rsrc(a.scale2, (a.Nout * a.Kc / 64 + 255) / 256 * 4);
   }
 
   __device__ __forceinline__ void issue(Set &t, int64_t s) {
+    const u32x4 c4 = __builtin_amdgcn_raw_buffer_load_b128(rc, cvoff, (int)(s * soff_c), 0);
+    t.code[0] = c4.x; t.code[1] = c4.y; t.code[2] = c4.z; t.code[3] = c4.w;
+    const int64_t b = blk_base + s * blk_step;
     if constexpr (!KN) {
-      const u32x4 c4 = __builtin_amdgcn_raw_buffer_load_b128(rc, cvoff[0], (int)(s * 32), 0);
-      t.code[0] = c4.x; t.code[1] = c4.y; t.code[2] = c4.z; t.code[3] = c4.w;
-      const int64_t b = blk_base[0] + s;
       if constexpr (DQ) {
-        t.q[0] = __builtin_amdgcn_raw_buffer_load_b8(rq, qvoff[0], (int)s, 0);
-        t.st[0] = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
-            rs, qvoff[0] == kOutOfRange ? kOutOfRange : (uint32_t)((b >> 8) * 4), 0, 0));
+        t.q = __builtin_amdgcn_raw_buffer_load_b8(rq, qvoff, (int)s, 0);
+        t.st = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
+            rs, qvoff == kOutOfRange ? kOutOfRange : (uint32_t)((b >> 8) * 4), 0, 0));
       } else {
-        t.q[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, qvoff[0], (int)(s * 4), 0);
+        t.q = __builtin_amdgcn_raw_buffer_load_b32(rq, qvoff, (int)(s * 4), 0);
       }
     } else {
-      const int soff_c = (int)(s * (BK / 2) * Nout);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        t.code[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvoff[i], soff_c, 0);
-        const int64_t b = blk_base[i] + s * blk_step;
-        if constexpr (DQ) {
-          t.q[i] = __builtin_amdgcn_raw_buffer_load_b8(rq, qvoff[i] == kOutOfRange ? kOutOfRange : (uint32_t)b, 0, 0);
-          t.st[i] = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
-              rs, qvoff[i] == kOutOfRange ? kOutOfRange : (uint32_t)((b >> 8) * 4), 0, 0));
-        } else {
-          t.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, qvoff[i] == kOutOfRange ? kOutOfRange : (uint32_t)(b * 4),
-                                                        0, 0);
-        }
+      if constexpr (DQ) {
+        t.q = __builtin_amdgcn_raw_buffer_load_b8(rq, qvoff == kOutOfRange ? kOutOfRange : (uint32_t)b, 0, 0);
+        t.st = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
+            rs, qvoff == kOutOfRange ? kOutOfRange : (uint32_t)((b >> 8) * 4), 0, 0));
+      } else {
+        t.q = __builtin_amdgcn_raw_buffer_load_b32(rq, qvoff == kOutOfRange ? kOutOfRange : (uint32_t)(b * 4), 0, 0);
       }
     }
   }
 
-  __device__ __forceinline__ float scale(const Set &t, int i) const {
-    if constexpr (DQ) return (float)t.q[i] * t.st[i];
-    else return as_f32(t.q[i]);
+  __device__ __forceinline__ float scale(const Set &t) const {
+    if constexpr (DQ) return (float)t.q * t.st;
+    else return as_f32(t.q);
   }
 
   __device__ __forceinline__ void store(const Set &t, uint16_t *Rs, const float2 *pair, int lane) const {
     const int copy = lane & (kPairCopies - 1);
+    const float A = scale(t);
     if constexpr (!KN) {
-      const float A = scale(t, 0);
       uint32_t o[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -182,26 +197,45 @@ struct Producer {
           const float2 p = pair[((t.code[i] >> (8 * j)) & 0xFF) * kPairCopies + copy];
           o[4 * i + j] = pack_bf16x2(p.x * A, p.y * A);
         }
-      u32x4 *dst = reinterpret_cast<u32x4 *>(&Rs[row_nk * LD + half_nk * 32]);
+      uint16_t *row = Rs + wr_col * LD;
+      const int sw = kswz(wr_col);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4 *>(&row[(wr_k + 8 * i) ^ sw]) = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
     } else {
-      float w[4][8];
+      // 4 x 4 transpose of words within the quad: w[i] of lane j <- word j of lane i.
+      uint32_t w0 = t.code[0], w1 = t.code[1], w2 = t.code[2], w3 = t.code[3];
+      const bool odd = lane & 1, hi = lane & 2;
+      {
+        uint32_t x = odd ? w0 : w1, y = odd ? w2 : w3;
+        x = qperm<0xB1>(x);
+        y = qperm<0xB1>(y);
+        if (odd) { w0 = x; w2 = y; } else { w1 = x; w3 = y; }
+      }
+      {
+        uint32_t x = hi ? w0 : w2, y = hi ? w1 : w3;
+        x = qperm<0x4E>(x);
+        y = qperm<0x4E>(y);
+        if (hi) { w0 = x; w1 = y; } else { w2 = x; w3 = y; }
+      }
+      const uint32_t au = as_u32(A);
+      const float S[4] = {as_f32(qperm<0x00>(au)), as_f32(qperm<0x55>(au)), as_f32(qperm<0xAA>(au)),
+                          as_f32(qperm<0xFF>(au))};
+      const uint32_t wv[4] = {w0, w1, w2, w3};
+      float v[4][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float A = scale(t, i);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float2 p = pair[((t.code[i] >> (8 * j)) & 0xFF) * kPairCopies + copy];
-          w[i][2 * j] = p.x * A;
-          w[i][2 * j + 1] = p.y * A;
+        for (int m = 0; m < 4; ++m) {
+          const float2 p = pair[((wv[i] >> (8 * m)) & 0xFF) * kPairCopies + copy];
+          v[i][2 * m] = p.x * S[i];
+          v[i][2 * m + 1] = p.y * S[i];
         }
-      }
+      const int k = wr_k ^ kswz(wr_col);
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const u32x2 v = {pack_bf16x2(w[0][n], w[1][n]), pack_bf16x2(w[2][n], w[3][n])};
-        *reinterpret_cast<u32x2 *>(&Rs[(8 * nc + n) * LD + 4 * kq]) = v;
-      }
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<u32x2 *>(&Rs[(wr_col + c) * LD + k]) =
+            u32x2{pack_bf16x2(v[0][c], v[1][c]), pack_bf16x2(v[2][c], v[3][c])};
     }
   }
 };
@@ -219,7 +253,7 @@ __device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n
     const int64_t gn = n0 + row, gj = j0 + jj;
     uint16_t v = 0;
     if (gj < a.r && gn < a.Nout) v = EPI_NK ? a.R2[gn * a.ldr2 + gj] : a.R2[gj * a.ldr2 + gn];
-    Rs[row * LD + jj] = v;
+    Rs[row * LD + (jj ^ kswz(row))] = v;
   }
 }
 
@@ -307,10 +341,12 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
   struct BFrag {
     bf16x8 b[TN];
   };
+  // Column 32j + lr, positions 32lh + 8c .. +7, stored at 32(lh ^ (lr >> 4)) + 8(c ^ j).
+  const int rb = lr * LD + 32 * (lh ^ (lr >> 4));
   auto read_b = [&](BFrag &f, int stage, int c) {
-    const uint16_t *Rs = wst + stage * R_TILE;
+    const uint16_t *Rs = wst + stage * R_TILE + rb;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&Rs[(j * 32 + lr) * LD + lh * 32 + c * 8]);
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&Rs[j * 32 * LD + 8 * (c ^ j)]);
   };
   auto mma = [&](const ASet &A, int c, const BFrag &f) {
 #pragma unroll
