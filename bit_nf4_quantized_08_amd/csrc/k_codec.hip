@@ -23,15 +23,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float dpp_quad_xor1(float v) {
-  // quad_perm [1,0,3,2]
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_quad_xor2(float v) {
-  // quad_perm [2,3,0,1]
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
-}
-
 // Row index of one normalised value: bucket lookup plus one compare.
 __device__ __forceinline__ uint32_t nearest_row(float nrm, const float2 *lut) {
   int b = (int)__builtin_fmaf(nrm, 16.0f, 16.0f);
@@ -42,9 +33,73 @@ __device__ __forceinline__ uint32_t nearest_row(float nrm, const float2 *lut) {
 }
 
 // ---------------------------------------------------------------- quantise
-// One lane handles 16 consecutive elements; four neighbouring lanes (a DPP
-// quad) form one block of 64, reduce its absmax with two quad permutes, and
-// each lane stores its 8 bytes of packed codes.
+// A wave takes 1024 consecutive elements (16 blocks) per iteration.  Its load
+// instructions are fully coalesced (lane l reads the l-th 16 bytes of a 1 KB
+// span), so a block is spread over consecutive lanes: 16 lanes for fp32 input
+// (4 elements each), 8 lanes for bf16 input (8 elements each).  The block
+// absmax is reduced across those lanes with DPP (quad permutes, then a row
+// rotation or half-row mirror); one correctly rounded reciprocal per block;
+// codes are stored from registers as 2 or 4 bytes per lane.  The last partial
+// wave span (fewer than 1024 elements) is done by one wave, 16 elements per
+// lane, with bounds checks.
+constexpr int kQChunk = 1024;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Codes of `cnt` normalised values x[i] * rho (or x[i] / a when 1/a overflows),
+// packed low nibble first.
+template <int CNT>
+__device__ __forceinline__ uint32_t encode(const float *x, float am, const float2 *lut) {
+  // Correctly rounded reciprocal, once per block (infinite when 1/a overflows).
+  const float rho = am > 0.0f ? 1.0f / am : 0.0f;
+  uint32_t w = 0;
+  if (!__builtin_isinf(rho)) {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) w |= nearest_row(x[i] * rho, lut) << (4 * i);
+  } else {
+    // 1/a overflows fp32 (a < 2^-128): divide each weight by a instead.
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) w |= nearest_row(x[i] / am, lut) << (4 * i);
+  }
+  return w;
+}
+
+template <bool BF16>
+__device__ void quantize_tail(const void *__restrict__ W, int64_t n, int64_t start, uint8_t *__restrict__ codes,
+                              float *__restrict__ absmax, const float2 *lut, int lane) {
+  const int64_t e0 = start + 16 * lane;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t e = e0 + i;
+    float x = 0.0f;
+    if (e < n) {
+      if constexpr (BF16) x = bf16_to_f32(static_cast<const uint16_t *>(W)[e]);
+      else x = static_cast<const float *>(W)[e];
+    }
+    v[i] = x;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
+  am = fmaxf(am, dpp_f32<0xB1>(am));
+  am = fmaxf(am, dpp_f32<0x4E>(am));
+  if ((lane & 3) == 0 && e0 < n) absmax[e0 / QN_BLOCK] = am;
+  const uint32_t lo = encode<8>(v, am, lut), hi = encode<8>(v + 8, am, lut);
+  if (e0 < n) {
+    // Elements past n were zeros whose row index is the zero row; clear those
+    // nibbles so the padding nibble of an odd count is 0.
+    const int64_t valid = n - e0;
+    uint64_t word = ((uint64_t)hi << 32) | lo;
+    if (valid < 16) word &= (1ull << (4 * valid)) - 1ull;
+    const int64_t nbytes = (n + 1) / 2, b0 = e0 / 2;
+    for (int i = 0; i < 8 && b0 + i < nbytes; ++i) codes[b0 + i] = (uint8_t)(word >> (8 * i));
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restrict__ W, int64_t n,
                                                             uint8_t *__restrict__ codes,
@@ -55,82 +110,63 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
     lut[threadIdx.x] = make_float2(tab.thr[threadIdx.x], __builtin_bit_cast(float, tab.base[threadIdx.x]));
   }
   __syncthreads();
-
-  const int64_t nchunks = (n + 15) / 16;
-  const int64_t nbytes = (n + 1) / 2;
-  for (int64_t t0 = (int64_t)blockIdx.x * kThreads; t0 < nchunks; t0 += (int64_t)gridDim.x * kThreads) {
-    const int64_t t = t0 + threadIdx.x;
-    const int64_t e0 = t * 16;
-    float v[16];
-    const bool full = e0 + 16 <= n;
-    if (full) {
-      if constexpr (BF16) {
-        const uint16_t *p = static_cast<const uint16_t *>(W) + e0;
-        const u32x4 a = ld_stream(p);
-        const u32x4 b = ld_stream(p + 8);
-        uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_id = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int64_t full = n / kQChunk;
+  for (int64_t ch = wave_id; ch < full; ch += nwaves) {
+    const int64_t base = ch * kQChunk;
+    if constexpr (!BF16) {
+      // instruction i: elements base + 4 (64 i + lane) .. +4, block 4 i + lane / 16
+      const float *p = static_cast<const float *>(W) + base;
+      u32x4 raw[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          v[2 * i] = bf16_lo(w[i]);
-          v[2 * i + 1] = bf16_hi(w[i]);
-        }
-      } else {
-        const float *p = static_cast<const float *>(W) + e0;
+      for (int i = 0; i < 4; ++i) raw[i] = ld_stream(p + 4 * (64 * i + lane));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 a = ld_stream(p + 4 * i);
-          // Copy components to scalars before reinterpreting them: a bit_cast
-          // applied directly to a vector component reads the wrong element.
-          const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+      for (int i = 0; i < 4; ++i) {
+        // Copy components to scalars before reinterpreting them: a bit_cast
+        // applied directly to a vector component reads the wrong element.
+        const uint32_t u[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+        float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[4 * i + j] = as_f32(u[j]);
-        }
+        for (int j = 0; j < 4; ++j) v[j] = as_f32(u[j]);
+        float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        am = fmaxf(am, dpp_f32<0xB1>(am));    // quad xor 1
+        am = fmaxf(am, dpp_f32<0x4E>(am));    // quad xor 2
+        am = fmaxf(am, dpp_f32<0x124>(am));   // row rotate by 4
+        am = fmaxf(am, dpp_f32<0x128>(am));   // row rotate by 8
+        if ((lane & 15) == 0) absmax[base / QN_BLOCK + 4 * i + (lane >> 4)] = am;
+        const uint32_t w = encode<4>(v, am, lut);
+        *reinterpret_cast<uint16_t *>(codes + base / 2 + 2 * (64 * i + lane)) = (uint16_t)w;
       }
     } else {
+      // instruction i: elements base + 8 (64 i + lane) .. +8, block 8 i + lane / 8
+      const uint16_t *p = static_cast<const uint16_t *>(W) + base;
+      u32x4 raw[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t e = e0 + i;
-        float x = 0.0f;
-        if (e < n) {
-          if constexpr (BF16) x = bf16_to_f32(static_cast<const uint16_t *>(W)[e]);
-          else x = static_cast<const float *>(W)[e];
+      for (int i = 0; i < 2; ++i) raw[i] = ld_stream(p + 8 * (64 * i + lane));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t u[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = bf16_lo(u[j]);
+          v[2 * j + 1] = bf16_hi(u[j]);
         }
-        v[i] = x;
+        float am = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+        am = fmaxf(am, dpp_f32<0xB1>(am));    // quad xor 1
+        am = fmaxf(am, dpp_f32<0x4E>(am));    // quad xor 2
+        am = fmaxf(am, dpp_f32<0x141>(am));   // half-row mirror: the other quad of 8
+        if ((lane & 7) == 0) absmax[base / QN_BLOCK + 8 * i + (lane >> 3)] = am;
+        const uint32_t w = encode<8>(v, am, lut);
+        *reinterpret_cast<uint32_t *>(codes + base / 2 + 4 * (64 * i + lane)) = w;
       }
-    }
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
-    am = fmaxf(am, dpp_quad_xor1(am));
-    am = fmaxf(am, dpp_quad_xor2(am));
-    if ((threadIdx.x & 3) == 0 && e0 < n) absmax[t >> 2] = am;
-    // Correctly rounded reciprocal, once per block (infinite when 1/a overflows).
-    const float rho = am > 0.0f ? 1.0f / am : 0.0f;
-
-    uint32_t lo = 0, hi = 0;
-    if (!__builtin_isinf(rho)) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) lo |= nearest_row(v[i] * rho, lut) << (4 * i);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) hi |= nearest_row(v[8 + i] * rho, lut) << (4 * i);
-    } else {
-      // 1/a overflows fp32 (a < 2^-128): divide each weight by a instead.
-      for (int i = 0; i < 8; ++i) lo |= nearest_row(v[i] / am, lut) << (4 * i);
-      for (int i = 0; i < 8; ++i) hi |= nearest_row(v[8 + i] / am, lut) << (4 * i);
-    }
-
-    if (full) {
-      *reinterpret_cast<uint2 *>(codes + 8 * t) = make_uint2(lo, hi);
-    } else if (e0 < n) {
-      // Partial chunk: elements past n were zeros whose row index is the zero
-      // row; clear those nibbles so the padding nibble of an odd count is 0.
-      const int valid = (int)(n - e0);  // 1..15
-      uint64_t word = ((uint64_t)hi << 32) | lo;
-      if (valid < 16) word &= (valid == 0) ? 0ull : ((1ull << (4 * valid)) - 1ull);
-      const int64_t b0 = 8 * t;
-      for (int i = 0; i < 8 && b0 + i < nbytes; ++i) codes[b0 + i] = (uint8_t)(word >> (8 * i));
     }
   }
+  if (full * kQChunk < n && wave_id == nwaves - 1) quantize_tail<BF16>(W, n, full * kQChunk, codes, absmax, lut, lane);
 }
 
 // ------------------------------------------------------------ double quant
@@ -263,8 +299,7 @@ int grid_for(int64_t work_items, int per_cu_waves = 8) {
 hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, uint8_t *codes, float *absmax,
                            hipStream_t s) {
   const CodecTables &tab = codec_tables();
-  const int64_t nchunks = (n + 15) / 16;
-  const int grid = grid_for(nchunks);
+  const int grid = grid_for((n + kQChunk - 1) / kQChunk * 64);
   TraceScope tr(QN_TRACE_QUANTIZE, s);
   if (w_is_bf16)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(kThreads), 0, s, W, n, codes, absmax, tab);
