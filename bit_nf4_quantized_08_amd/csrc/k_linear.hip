@@ -802,7 +802,8 @@ size_t bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
   c.take<uint16_t>(M * rp);                 // dH bf16 [M, rp]
   c.take<uint16_t>(rp * Mp);                // dH^T bf16 [rp, Mp]
   c.take<uint16_t>(rp * Mp);                // (sH)^T bf16 [rp, Mp]
-  c.take<float>((int64_t)colred_splits(M) * r * std::max(N, K));
+  c.take<float>((int64_t)colred_splits(M) * r * N);   // dB partials
+  c.take<float>((int64_t)colred_splits(M) * r * K);   // dA partials
   return c.off;
 }
 
@@ -814,41 +815,33 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
   uint16_t *dHb = c.take<uint16_t>(a.M * rp);
   uint16_t *dHt = c.take<uint16_t>(rp * Mp);
   uint16_t *sHt = c.take<uint16_t>(rp * Mp);
-  float *gpart = c.take<float>((int64_t)colred_splits(a.M) * a.r * std::max(a.N, a.K));
+  float *bpart = c.take<float>((int64_t)colred_splits(a.M) * a.r * a.N);
+  float *apart = c.take<float>((int64_t)colred_splits(a.M) * a.r * a.K);
 
   // B^T [rp, N] (rows >= r zero) so that dH = dY (B^T)^T runs on the skinny kernel.
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(rp * a.N, kThreads)), dim3(kThreads), 0, st,
                      a.B, a.N, a.r, a.r, Bt, rp);
   QN_TRY(hipGetLastError());
-  // dH = s dY B  -> dHb [M, rp], dHt [rp, Mp]
+  // One launch: dH = s dY B -> dHb [M, rp], dHt [rp, Mp]; H = X A^T -> (sH)^T [rp, Mp].
   {
-    LowRankArgs la{};
-    la.L = a.dY; la.ldl = a.N; la.M = a.M; la.Kc = a.N;
-    la.P = Bt; la.ldp = a.N; la.R = a.r; la.scale = a.s;
-    la.out_b = dHb; la.ldb = rp; la.out_t = dHt; la.ldt_rows = rp; la.Mp = Mp;
-    QN_TRY(launch_lowrank(la, st));
-  }
-  // H = X A^T -> (sH)^T [rp, Mp]
-  {
-    LowRankArgs la{};
-    la.L = a.X; la.ldl = a.K; la.M = a.M; la.Kc = a.K;
-    la.P = a.A; la.ldp = a.K; la.R = a.r; la.scale = a.s;
-    la.out_t = sHt; la.ldt_rows = rp; la.Mp = Mp;
-    QN_TRY(launch_lowrank(la, st));
+    LowRankArgs ld{}, lh{};
+    ld.L = a.dY; ld.ldl = a.N; ld.M = a.M; ld.Kc = a.N;
+    ld.P = Bt; ld.ldp = a.N; ld.R = a.r; ld.scale = a.s;
+    ld.out_b = dHb; ld.ldb = rp; ld.out_t = dHt; ld.ldt_rows = rp; ld.Mp = Mp;
+    lh.L = a.X; lh.ldl = a.K; lh.M = a.M; lh.Kc = a.K;
+    lh.P = a.A; lh.ldp = a.K; lh.R = a.r; lh.scale = a.s;
+    lh.out_t = sHt; lh.ldt_rows = rp; lh.Mp = Mp;
+    QN_TRY(launch_lowrank2(ld, &lh, st));
   }
 
-  // dB [N, r] = ((sH)^T dY)^T and dA [r, K] = dH^T X: contractions over M.
+  // One launch: dB [N, r] = ((sH)^T dY)^T and dA [r, K] = dH^T X, contractions over M.
   {
-    ColRedArgs ca{};
-    ca.Lt = sHt; ca.Mp = Mp; ca.Q = a.dY; ca.ldq = a.N; ca.M = a.M; ca.Ncols = a.N; ca.R = a.r;
-    ca.part = gpart; ca.out = a.dB; ca.transpose = true;
-    QN_TRY(launch_colred(ca, st, QN_TRACE_GEMM_DB));
-  }
-  {
-    ColRedArgs ca{};
+    ColRedArgs cb{}, ca{};
+    cb.Lt = sHt; cb.Mp = Mp; cb.Q = a.dY; cb.ldq = a.N; cb.M = a.M; cb.Ncols = a.N; cb.R = a.r;
+    cb.part = bpart; cb.out = a.dB; cb.transpose = true;
     ca.Lt = dHt; ca.Mp = Mp; ca.Q = a.X; ca.ldq = a.K; ca.M = a.M; ca.Ncols = a.K; ca.R = a.r;
-    ca.part = gpart; ca.out = a.dA; ca.transpose = false;
-    QN_TRY(launch_colred(ca, st, QN_TRACE_GEMM_DA));
+    ca.part = apart; ca.out = a.dA; ca.transpose = false;
+    QN_TRY(launch_colred2(cb, &ca, st, QN_TRACE_GEMM_DB));
   }
   // dX [M, K] = dY [M, N] * W_hat [N, K] + dH [M, r] * A [r, K]
   if (a.dX) {

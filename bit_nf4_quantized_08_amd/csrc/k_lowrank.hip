@@ -10,12 +10,13 @@
 // A workgroup of 8 waves owns 16 rows.  The contraction is cut into 32-wide
 // chunks dealt round-robin to the 8 waves; each wave accumulates its chunks with
 // v_mfma_f32_16x16x32_bf16 (lane group g = lane/16 takes indices [8g, 8g+8) of
-// a chunk for both operands), keeping sixteen chunks of loads in flight.  The 8
+// a chunk for both operands), keeping 16 / RT chunks of loads in flight.  The 8
 // partial 16 x R results are summed in LDS in a fixed order, and the workgroup
 // writes the requested outputs directly: fp32 unscaled, bf16 scaled
 // (row-major, zero-padded to ldb columns), bf16 scaled and transposed
 // (zero-padded to ldt_rows rows and Mp columns).  No split partials in global
-// memory, no second pass.
+// memory, no second pass.  One launch can carry two independent products
+// (blockIdx.y selects the argument set), which the backward uses for H and dH.
 
 #include <algorithm>
 
@@ -40,12 +41,18 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 
+__host__ __device__ inline int64_t lowrank_rows(const LowRankArgs &a) {
+  return a.out_t && a.Mp > a.M ? a.Mp : a.M;
+}
+
 template <int RT>  // 16-column tiles of the output: R <= 16 * RT
-__global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankArgs a) {
+__global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankArgs a0, LowRankArgs a1) {
   __shared__ float red[kWaves][ROWS][RT * 16];
+  const LowRankArgs &a = blockIdx.y ? a1 : a0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * ROWS;
+  if (m0 >= lowrank_rows(a)) return;   // the other product has more rows
 
   const rsrc_t rl = make_rsrc(a.L + m0 * a.ldl, (a.M - m0) * a.ldl * 2);
   const rsrc_t rp = make_rsrc(a.P, a.R * a.ldp * 2);
@@ -62,10 +69,11 @@ __global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankArgs a) {
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int64_t chunks = a.Kc / CHUNK;
-  for (int64_t q0 = wave; q0 < chunks; q0 += (int64_t)kWaves * UNROLL) {
-    u32x4 xv[UNROLL], pv[UNROLL][RT];
+  constexpr int U = UNROLL / RT;   // chunks of loads in flight per wave (registers: 4 * U * (1 + RT))
+  for (int64_t q0 = wave; q0 < chunks; q0 += (int64_t)kWaves * U) {
+    u32x4 xv[U], pv[U][RT];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t q = q0 + (int64_t)u * kWaves;
       const bool in = q < chunks;
       const int soff = (int)(q * CHUNK * 2);
@@ -75,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankArgs a) {
         pv[u][t] = in ? __builtin_amdgcn_raw_buffer_load_b128(rp, pvoff[t], soff, 0) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int t = 0; t < RT; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[u]),
@@ -121,15 +129,19 @@ __global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankArgs a) {
 
 }  // namespace
 
-hipError_t launch_lowrank(const LowRankArgs &a, hipStream_t st) {
-  const int64_t rows = std::max(a.M, a.out_t ? a.Mp : a.M);
-  const dim3 grid((unsigned)((rows + ROWS - 1) / ROWS));
+hipError_t launch_lowrank2(const LowRankArgs &a, const LowRankArgs *b, hipStream_t st) {
+  const int64_t rows = std::max(lowrank_rows(a), b ? lowrank_rows(*b) : 0);
+  const int64_t R = std::max(a.R, b ? b->R : 0);
+  const dim3 grid((unsigned)((rows + ROWS - 1) / ROWS), b ? 2u : 1u);
+  const LowRankArgs &a1 = b ? *b : a;
   TraceScope tr(QN_TRACE_LOWRANK, st);
-  if (a.R <= 16) hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(kThreads), 0, st, a);
-  else if (a.R <= 32) hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(lowrank_kernel<4>, grid, dim3(kThreads), 0, st, a);
+  if (R <= 16) hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(kThreads), 0, st, a, a1);
+  else if (R <= 32) hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(kThreads), 0, st, a, a1);
+  else hipLaunchKernelGGL(lowrank_kernel<4>, grid, dim3(kThreads), 0, st, a, a1);
   return hipGetLastError();
 }
+
+hipError_t launch_lowrank(const LowRankArgs &a, hipStream_t st) { return launch_lowrank2(a, nullptr, st); }
 
 }  // namespace qn
 
@@ -145,7 +157,8 @@ hipError_t launch_lowrank(const LowRankArgs &a, hipStream_t st) {
 // Lt[j][m+1]) with v_dot2_f32_bf16, so Q is read exactly once.  The factor
 // slice for the row range sits in LDS as [row pair][j] dwords (broadcast
 // reads).  Per-split partial sums go to `part`; a second kernel adds the
-// splits in order and rounds to bf16.
+// splits in order and rounds to bf16.  Like the low-rank product, one launch
+// can carry two independent reductions over the same rows (blockIdx.z).
 namespace qn {
 namespace {
 
@@ -155,12 +168,14 @@ constexpr int CR_RB = 128;        // rows per split
 constexpr int CR_PAIRS = CR_RB / 2;
 
 template <int R>
-__global__ __launch_bounds__(CR_THREADS) void colred_kernel(ColRedArgs a) {
+__global__ __launch_bounds__(CR_THREADS) void colred_kernel(ColRedArgs a0, ColRedArgs a1) {
   constexpr int RJ = R < 16 ? R : 16;            // rows of the output reduced per pass
   __shared__ uint32_t lt[CR_PAIRS * R];          // (Lt[j][2p], Lt[j][2p+1]) at [p][j]
   __shared__ float red[4][RJ][CR_COLS];
+  const ColRedArgs &a = blockIdx.z ? a1 : a0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * CR_COLS;
+  if (c0 >= a.Ncols) return;                     // the other reduction is wider
   const int split = blockIdx.y;
   const int64_t mb = (int64_t)split * CR_RB;
 
@@ -239,37 +254,55 @@ __global__ __launch_bounds__(CR_THREADS) void colred_kernel(ColRedArgs a) {
 }
 
 // out = bf16(sum over splits of part), as [R][Ncols] or transposed [Ncols][R].
-__global__ __launch_bounds__(256) void colred_reduce_kernel(const float *__restrict__ part, int splits, int64_t R,
-                                                            int64_t Ncols, bool transpose, uint16_t *__restrict__ out) {
+// One thread per output element, columns fastest: the partial reads are
+// coalesced; the splits are added in order.
+__global__ __launch_bounds__(256) void colred_reduce_kernel(ColRedArgs a0, ColRedArgs a1, int splits) {
+  const ColRedArgs &a = blockIdx.y ? a1 : a0;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= R * Ncols) return;
-  int64_t j, col;
-  if (transpose) { col = idx / R; j = idx % R; }
-  else { j = idx / Ncols; col = idx % Ncols; }
+  if (idx >= a.R * a.Ncols) return;
+  const int64_t j = idx / a.Ncols, col = idx % a.Ncols;
+  const int64_t stride = a.R * a.Ncols;
+  const float *p = a.part + idx;
   float v = 0.0f;
-  for (int s = 0; s < splits; ++s) v += part[((int64_t)s * R + j) * Ncols + col];
-  out[idx] = f32_to_bf16(v);
+  int s = 0;
+  for (; s + 4 <= splits; s += 4) {
+    const float x0 = p[(s + 0) * stride], x1 = p[(s + 1) * stride], x2 = p[(s + 2) * stride], x3 = p[(s + 3) * stride];
+    v += x0;
+    v += x1;
+    v += x2;
+    v += x3;
+  }
+  for (; s < splits; ++s) v += p[s * stride];
+  a.out[a.transpose ? col * a.R + j : idx] = f32_to_bf16(v);
 }
 
 }  // namespace
 
 int colred_splits(int64_t M) { return (int)((M + CR_RB - 1) / CR_RB); }
 
-hipError_t launch_colred(const ColRedArgs &a, hipStream_t st, int trace_kind) {
+hipError_t launch_colred2(const ColRedArgs &a, const ColRedArgs *b, hipStream_t st, int trace_kind) {
   const int splits = colred_splits(a.M);
-  const dim3 grid((unsigned)((a.Ncols + CR_COLS - 1) / CR_COLS), (unsigned)splits);
+  const int64_t ncols = std::max(a.Ncols, b ? b->Ncols : 0);
+  const int64_t R = std::max(a.R, b ? b->R : 0);
+  const ColRedArgs &a1 = b ? *b : a;
+  const dim3 grid((unsigned)((ncols + CR_COLS - 1) / CR_COLS), (unsigned)splits, b ? 2u : 1u);
   {
     TraceScope tr(trace_kind, st);
-    if (a.R <= 8) hipLaunchKernelGGL(colred_kernel<8>, grid, dim3(CR_THREADS), 0, st, a);
-    else if (a.R <= 16) hipLaunchKernelGGL(colred_kernel<16>, grid, dim3(CR_THREADS), 0, st, a);
-    else if (a.R <= 32) hipLaunchKernelGGL(colred_kernel<32>, grid, dim3(CR_THREADS), 0, st, a);
-    else hipLaunchKernelGGL(colred_kernel<64>, grid, dim3(CR_THREADS), 0, st, a);
+    if (R <= 8) hipLaunchKernelGGL(colred_kernel<8>, grid, dim3(CR_THREADS), 0, st, a, a1);
+    else if (R <= 16) hipLaunchKernelGGL(colred_kernel<16>, grid, dim3(CR_THREADS), 0, st, a, a1);
+    else if (R <= 32) hipLaunchKernelGGL(colred_kernel<32>, grid, dim3(CR_THREADS), 0, st, a, a1);
+    else hipLaunchKernelGGL(colred_kernel<64>, grid, dim3(CR_THREADS), 0, st, a, a1);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(colred_reduce_kernel, dim3((unsigned)((a.R * a.Ncols + 255) / 256)), dim3(256), 0, st, a.part,
-                     splits, a.R, a.Ncols, a.transpose, a.out);
+  const int64_t elems = std::max(a.R * a.Ncols, b ? b->R * b->Ncols : 0);
+  hipLaunchKernelGGL(colred_reduce_kernel, dim3((unsigned)((elems + 255) / 256), b ? 2u : 1u), dim3(256), 0, st, a,
+                     a1, splits);
   return hipGetLastError();
+}
+
+hipError_t launch_colred(const ColRedArgs &a, hipStream_t st, int trace_kind) {
+  return launch_colred2(a, nullptr, st, trace_kind);
 }
 
 }  // namespace qn

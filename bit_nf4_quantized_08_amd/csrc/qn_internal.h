@@ -110,6 +110,8 @@ struct LowRankArgs {
   int64_t ldt_rows, Mp;
 };
 hipError_t launch_lowrank(const LowRankArgs &a, hipStream_t s);
+// Two independent products with the same rank bucket in one launch (b may be null).
+hipError_t launch_lowrank2(const LowRankArgs &a, const LowRankArgs *b, hipStream_t s);
 
 // Column-streaming reduction over rows (k_lowrank.hip): out = bf16(sum_m
 // Lt[j][m] * Q[m][c]) for j < R <= 64, as [R][Ncols] or transposed [Ncols][R].
@@ -126,6 +128,9 @@ struct ColRedArgs {
 };
 int colred_splits(int64_t M);
 hipError_t launch_colred(const ColRedArgs &a, hipStream_t s, int trace_kind);
+// Two independent reductions over the same M in one launch (b may be null);
+// each needs its own `part`.
+hipError_t launch_colred2(const ColRedArgs &a, const ColRedArgs *b, hipStream_t s, int trace_kind);
 
 // Forward pieces.
 struct FwdArgs {

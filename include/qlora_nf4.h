@@ -173,8 +173,9 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M,
 #define QN_TRACE_GEMV 4          /* decode-path streaming kernel (fwd, M <= 8)   */
 #define QN_TRACE_GEMM_FWD 5      /* forward dequant-GEMM tile kernel (M > 8)     */
 #define QN_TRACE_GEMM_DX 6       /* backward dX dequant-GEMM tile kernel         */
-#define QN_TRACE_GEMM_DB 7       /* backward dB^T contraction over M             */
-#define QN_TRACE_GEMM_DA 8       /* backward dA contraction over M               */
+#define QN_TRACE_GEMM_DB 7       /* backward dA and dB contractions over M (one  */
+                                 /* launch carries both)                         */
+#define QN_TRACE_GEMM_DA 8       /* reserved (dA shares the launch of kind 7)    */
 #define QN_TRACE_LOWRANK 9       /* X A^T or dY B low-rank product               */
 int qn_trace_enable(int on);
 int qn_trace_read(int *kinds, float *ms, int cap);
