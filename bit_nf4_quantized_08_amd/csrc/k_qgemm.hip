@@ -54,7 +54,9 @@ constexpr int LD = BK + 8;               // bf16 per LDS row of the weight tile 
 constexpr int WM = 64;                   // rows per MMA wave
 constexpr int TM = WM / 32, TN = BN / 32;
 constexpr int R_TILE = BN * LD;          // bf16 elements per weight stage
-constexpr int kPairCopies = 16;
+constexpr int kPairCopies = 8;
+constexpr int XW = WM * BK;             // bf16 per wave per activation stage (8 KB)
+constexpr int XSTAGE = 4 * XW;           // bf16 per activation stage (4 MMA waves)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dwords
@@ -66,6 +68,28 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
   const int64_t cap = 0xFFFFFFF0LL;
   const int n = (int)(uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcFlags);
+}
+
+// Direct-to-LDS 16-byte load (each lane's 16 bytes land at lds_base + 16 *
+// lane).  Issued from inline assembly so that the compiler neither waits for
+// it at every LDS access nor at barriers: the issuing wave is the only reader
+// of what it loads and orders its reads with explicit vmcnt waits.  `desc` is a
+// raw buffer descriptor built from wave-uniform values (scalar registers).
+__device__ __forceinline__ u32x4 raw_desc(const void *base, int64_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  const int64_t cap = 0xFFFFFFF0LL;
+  const uint32_t n = (uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) & 0xFFFFu;
+  const uint32_t nr = (uint32_t)__builtin_amdgcn_readfirstlane((int)n);
+  return u32x4{lo, hi, nr, (uint32_t)kRsrcFlags};
+}
+__device__ __forceinline__ void dma_lds16(u32x4 desc, uint32_t lds_base, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }
 
 __device__ __forceinline__ void tile_coords(int h, int tiles_m, int tiles_n, int gm_rows, int &tm, int &tn) {
@@ -257,13 +281,28 @@ __device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n
   }
 }
 
+// Workgroup barrier that orders the waves' own LDS reads and writes only:
+// global loads issued before it stay in flight, including the direct-to-LDS
+// activation loads of an MMA wave, which only that wave reads and which it
+// waits for itself (a compiler-generated LDS fence would wait for them here).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Exactly one workgroup (2 waves per SIMD) fits a CU, so tell the compiler
 // that higher occupancy is not reachable: it may then keep a whole step's
 // operands in registers instead of re-reading them one by one.
 template <bool KN, bool DQ, bool EPI_NK>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qgemm_kernel(QGemmArgs a, Code16 cb) {
-  __shared__ __attribute__((aligned(16))) uint16_t wst[2 * R_TILE];
+  // Separate arrays per stage: the compiler then tracks the direct-to-LDS
+  // loads into each activation stage on their own and waits only for the
+  // stage a fragment read touches.
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[XSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[XSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t xs2[XSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t ws0[R_TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t ws1[R_TILE];
   __shared__ __attribute__((aligned(16))) float2 pair[256 * kPairCopies];
   for (int i = threadIdx.x; i < 256 * kPairCopies; i += kThreads) {
     const int e = i / kPairCopies;
@@ -275,9 +314,9 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool producer = wave >= 4;
-  const int64_t steps = a.Kc / BK;
+  const int64_t steps = __builtin_amdgcn_readfirstlane((int)(a.Kc / BK));
   const int64_t epi_steps = (a.r + BK - 1) / BK;
-  __syncthreads();  // pair table
+  lds_barrier();  // pair table
 
   if (producer) {
     const int tid = threadIdx.x - kProducers;
@@ -286,34 +325,35 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     typename Producer<KN, DQ>::Set s0, s1;
     if (steps > 0) P.issue(s0, 0);
     if (steps > 1) P.issue(s1, 1);
-    if (steps > 0) P.store(s0, wst, pair, lane);
+    if (steps > 0) P.store(s0, ws0, pair, lane);
     if (steps > 2) P.issue(s0, 2);
-    __syncthreads();
+    lds_barrier();
     // Step s: the MMA waves read stage s & 1; store step s+1 into the other
     // stage from its register set, then reuse that set for step s+3.
     for (int64_t s = 0; s < steps; s += 2) {
       if (s + 1 < steps) {
-        P.store(s1, wst + R_TILE, pair, lane);
+        P.store(s1, ws1, pair, lane);
         if (s + 3 < steps) P.issue(s1, s + 3);
       }
-      __syncthreads();
+      lds_barrier();
       if (s + 1 >= steps) break;
       if (s + 2 < steps) {
-        P.store(s0, wst, pair, lane);
+        P.store(s0, ws0, pair, lane);
         if (s + 4 < steps) P.issue(s0, s + 4);
       }
-      __syncthreads();
+      lds_barrier();
     }
     for (int64_t e = 0; e < epi_steps; ++e) {
-      load_adapter_right<EPI_NK>(a, n0, e, wst, threadIdx.x, kThreads);
-      __syncthreads();
-      __syncthreads();
+      load_adapter_right<EPI_NK>(a, n0, e, ws0, threadIdx.x, kThreads);
+      lds_barrier();
+      lds_barrier();
     }
     return;
   }
 
   // ---------------------------------------------------------- MMA waves
   const int lr = lane & 31, lh = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -322,96 +362,130 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Activation operand: row m0 + wave*64 + i*32 + lr, contraction indices
-  // [32*lh, 32*lh + 32) of each step: 4 x 16 B per row tile.
-  const rsrc_t rl = make_rsrc(a.L + m0 * a.ldl, (a.M - m0) * a.ldl * 2);
-  uint32_t avoff[TM];
+  // Activation rows of this wave go global -> LDS with direct-to-LDS loads,
+  // three stages of 64 rows x 64 contraction indices (8 KB), two steps ahead;
+  // only this wave reads them.  Chunk k (16 bytes) of stage row r sits at slot
+  // k ^ ((r >> 1) & 7), so the fragment reads of 16 consecutive rows hit 16
+  // distinct bank groups.  Load instruction g fills rows 8g..8g+7 (1 KB in lane
+  // order): lane l writes slot l & 7 of row 8g + l / 8, i.e. every 8 lanes read
+  // one 128-byte line.
+  const int64_t wrow0 = m0 + (int64_t)wave_u * WM;
+  const u32x4 xdesc = raw_desc(a.L + wrow0 * a.ldl, (a.M - wrow0) * a.ldl * 2);
+  uint32_t xoff[8];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) avoff[i] = (uint32_t)((wave * WM + i * 32 + lr) * a.ldl * 2 + lh * 64);
-  struct ASet {
-    u32x4 v[TM][4];
+  for (int g = 0; g < 8; ++g) {
+    const int row = 8 * g + (lane >> 3), slot = lane & 7;
+    xoff[g] = (uint32_t)(row * a.ldl * 2 + ((slot ^ ((row >> 1) & 7)) * 16));
+  }
+  auto issue_x = [&](int64_t s, uint16_t *stage) {
+    const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(stage + wave_u * XW));
+    const int soff = __builtin_amdgcn_readfirstlane((int)(s * BK * 2));
+#pragma unroll
+    for (int g = 0; g < 8; ++g) dma_lds16(xdesc, dst + g * 1024, xoff[g], soff);
   };
-  auto issue_a = [&](ASet &A, int64_t s) {
+  // Wait until the activation stage of the next step has landed: the only
+  // vector memory operations of an MMA wave in the main loop are these loads,
+  // 8 per step, and at most the group issued after it may still be in flight.
+  auto wait_x = [&](bool later_group_in_flight) {
+    if (later_group_in_flight) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  // Fragment offsets: A (activations) tile i, slice c: row 32i + lr, chunk 4lh + c;
+  // B (weights) column 32j + lr, positions 32lh + 8c .. +7, stored at 32(lh ^ (lr >> 4)) + 8(c ^ j).
+  uint32_t aoff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) aoff[c] = (uint32_t)(wave_u * XW + lr * BK + (((4 * lh + c) ^ ((lr >> 1) & 7)) * 8));
+  const int rb = lr * LD + 32 * (lh ^ (lr >> 4));
+  struct Frag {
+    bf16x8 a[TM];
+    bf16x8 b[TN];
+  };
+  auto read_b = [&](bf16x8 *b, const uint16_t *wc, int c) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * (c ^ j)]);
+  };
+  auto read_f = [&](Frag &f, const uint16_t *xc, const uint16_t *wc, int c) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(&xc[aoff[c] + i * 32 * BK]);
+    read_b(f.b, wc, c);
+  };
+  auto mma = [&](const Frag &f) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        A.v[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rl, avoff[i] + 16 * c, (int)(s * BK * 2), 0);
-  };
-  struct BFrag {
-    bf16x8 b[TN];
-  };
-  // Column 32j + lr, positions 32lh + 8c .. +7, stored at 32(lh ^ (lr >> 4)) + 8(c ^ j).
-  const int rb = lr * LD + 32 * (lh ^ (lr >> 4));
-  auto read_b = [&](BFrag &f, int stage, int c) {
-    const uint16_t *Rs = wst + stage * R_TILE + rb;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&Rs[j * 32 * LD + 8 * (c ^ j)]);
-  };
-  auto mma = [&](const ASet &A, int c, const BFrag &f) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, A.v[i][c]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, f.b[j], acc[i][j], 0, 0, 0);
-    }
-  };
-  // One step from `stage`: b0 holds slice 0 on entry; on exit b0 holds slice 0
-  // of the next step (read after the barrier) if `more`.
-  auto step = [&](const ASet &A, BFrag &b0, BFrag &b1, int stage, bool more) {
-    read_b(b1, stage, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(A, 0, b0);
-    read_b(b0, stage, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(A, 1, b1);
-    read_b(b1, stage, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(A, 2, b0);
-    __syncthreads();
-    if (more) read_b(b0, stage ^ 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(A, 3, b1);
+      for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
-  ASet A0, A1;
-  if (steps > 0) issue_a(A0, 0);
-  if (steps > 1) issue_a(A1, 1);
-  __syncthreads();
-  BFrag b0, b1;
-  if (steps > 0) read_b(b0, 0, 0);
-  for (int64_t s = 0; s < steps; s += 2) {
-    step(A0, b0, b1, 0, s + 1 < steps);
-    if (s + 2 < steps) issue_a(A0, s + 2);
+  Frag f0, f1;
+  // One step: stages (xc, wc) now, (xn, wn) next, x2 is refilled for step s + 2
+  // (it was last read in step s - 1).  f0 holds slice 0 of step s on entry and
+  // slice 0 of step s + 1 on exit.
+  auto step = [&](int64_t s, const uint16_t *xc, const uint16_t *wc, const uint16_t *xn, const uint16_t *wn,
+                  uint16_t *x2) {
+    if (s + 2 < steps) issue_x(s + 2, x2);
+    read_f(f1, xc, wc, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    read_f(f0, xc, wc, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    read_f(f1, xc, wc, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    if (s + 1 < steps) wait_x(s + 2 < steps);
+    lds_barrier();
+    if (s + 1 < steps) read_f(f0, xn, wn, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+  };
+  if (steps > 0) issue_x(0, xs0);
+  if (steps > 1) issue_x(1, xs1);
+  if (steps > 0) wait_x(steps > 1);
+  lds_barrier();
+  if (steps > 0) read_f(f0, xs0, ws0, 0);
+  // Step s uses activation stage s % 3 and weight stage s % 2.
+  for (int64_t s = 0; s < steps; s += 6) {
+    step(s, xs0, ws0, xs1, ws1, xs2);
     if (s + 1 >= steps) break;
-    step(A1, b0, b1, 1, s + 2 < steps);
-    if (s + 3 < steps) issue_a(A1, s + 3);
+    step(s + 1, xs1, ws1, xs2, ws0, xs0);
+    if (s + 2 >= steps) break;
+    step(s + 2, xs2, ws0, xs0, ws1, xs1);
+    if (s + 3 >= steps) break;
+    step(s + 3, xs0, ws1, xs1, ws0, xs2);
+    if (s + 4 >= steps) break;
+    step(s + 4, xs1, ws0, xs2, ws1, xs0);
+    if (s + 5 >= steps) break;
+    step(s + 5, xs2, ws1, xs0, ws0, xs1);
   }
 
   // ---- adapter term: contraction over j < r, zero-padded to steps of 64.  The
   // left operand (leading dim ldl2, readable up to column ldl2, a multiple of 8
-  // zero-padded beyond r) is loaded like the activations; the right operand
-  // goes through weight stage 0.
+  // zero-padded beyond r) is loaded straight into registers in operand layout
+  // (lane half lh takes j in [32 lh, 32 lh + 32)); the right operand goes
+  // through weight stage 0.
   const rsrc_t rl2 = make_rsrc(a.L2 + m0 * a.ldl2, (a.M - m0) * a.ldl2 * 2);
   for (int64_t e = 0; e < epi_steps; ++e) {
-    ASet A;
+    u32x4 av[TM][4];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int64_t j = e * BK + lh * 32 + c * 8;
         const uint32_t off = j < a.ldl2 ? (uint32_t)(((wave * WM + i * 32 + lr) * a.ldl2 + j) * 2) : kOutOfRange;
-        A.v[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rl2, off, 0, 0);
+        av[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rl2, off, 0, 0);
       }
-    load_adapter_right<EPI_NK>(a, n0, e, wst, threadIdx.x, kThreads);
-    __syncthreads();
+    load_adapter_right<EPI_NK>(a, n0, e, ws0, threadIdx.x, kThreads);
+    lds_barrier();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      BFrag f;
-      read_b(f, 0, c);
-      mma(A, c, f);
+      Frag f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) f.a[i] = __builtin_bit_cast(bf16x8, av[i][c]);
+      read_b(f.b, ws0, c);
+      mma(f);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- store bf16: element e of a 32x32 tile is row 8*(e/4)+4*lh+(e%4), column lr.
