@@ -64,10 +64,17 @@ constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // a per-lane offset that always 
 
 // Buffer resource over [base, base + bytes); loads beyond `bytes` (by the
 // per-lane offset) return zero, which masks ragged tile edges.
+// Every resource of this kernel is wave-uniform; building it from values read
+// out of the first lane keeps it in scalar registers (a resource the compiler
+// takes for divergent turns each access into a loop, and then it can no
+// longer count outstanding loads and waits for all of them).
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
   const int64_t cap = 0xFFFFFFF0LL;
-  const int n = (int)(uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcFlags);
+  const uint64_t p = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)(uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n, kRsrcFlags);
 }
 
 // Direct-to-LDS 16-byte load (each lane's 16 bytes land at lds_base + 16 *
@@ -209,18 +216,46 @@ struct Producer {
     else return as_f32(t.q);
   }
 
-  __device__ __forceinline__ void store(const Set &t, uint16_t *Rs, const float2 *pair, int lane) const {
+  __device__ __forceinline__ void store(const Set &t, uint16_t *Rs, const float2 *pair, const float *cv,
+                                        int lane) const {
     const int copy = lane & (kPairCopies - 1);
     const float A = scale(t);
     if constexpr (!KN) {
+      // All 32 codes share one block scale: build the block's sixteen bf16
+      // products bf16(fl32(c[q] * A)) once, split into a low-byte and a
+      // high-byte plane (4 words each, entries 4m..4m+3 in word m), and look the
+      // codes up four at a time with byte permutes (no LDS traffic).
+      uint32_t P[8], LO[4], HI[4];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) P[k] = pack_bf16x2(cv[2 * k] * A, cv[2 * k + 1] * A);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        LO[m] = __builtin_amdgcn_perm(P[2 * m + 1], P[2 * m], 0x06040200u);
+        HI[m] = __builtin_amdgcn_perm(P[2 * m + 1], P[2 * m], 0x07050301u);
+      }
+      // x: four codes, one per byte -> low and high bytes of their products.
+      auto look = [&](uint32_t x, uint32_t &lo, uint32_t &hi) {
+        const uint32_t s7 = x & 0x07070707u;
+        const uint32_t upper = ((x >> 3) & 0x01010101u) * 0xFFu;   // 0xFF where the code is >= 8
+        const uint32_t l0 = __builtin_amdgcn_perm(LO[1], LO[0], s7), l1 = __builtin_amdgcn_perm(LO[3], LO[2], s7);
+        const uint32_t h0 = __builtin_amdgcn_perm(HI[1], HI[0], s7), h1 = __builtin_amdgcn_perm(HI[3], HI[2], s7);
+        lo = (upper & l1) | (~upper & l0);
+        hi = (upper & h1) | (~upper & h0);
+      };
       uint32_t o[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float2 p = pair[((t.code[i] >> (8 * j)) & 0xFF) * kPairCopies + copy];
-          o[4 * i + j] = pack_bf16x2(p.x * A, p.y * A);
-        }
+      for (int i = 0; i < 4; ++i) {
+        // byte b of the word: element 2b in the low nibble, 2b + 1 in the high one
+        uint32_t le, he, lo, ho;
+        look(t.code[i] & 0x0F0F0F0Fu, le, he);
+        look((t.code[i] >> 4) & 0x0F0F0F0Fu, lo, ho);
+        const uint32_t e01 = __builtin_amdgcn_perm(he, le, 0x05010400u), e23 = __builtin_amdgcn_perm(he, le, 0x07030602u);
+        const uint32_t d01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u), d23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);
+        o[4 * i + 0] = __builtin_amdgcn_perm(d01, e01, 0x05040100u);
+        o[4 * i + 1] = __builtin_amdgcn_perm(d01, e01, 0x07060302u);
+        o[4 * i + 2] = __builtin_amdgcn_perm(d23, e23, 0x05040100u);
+        o[4 * i + 3] = __builtin_amdgcn_perm(d23, e23, 0x07060302u);
+      }
       uint16_t *row = Rs + wr_col * LD;
       const int sw = kswz(wr_col);
 #pragma unroll
@@ -303,8 +338,9 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
   __shared__ __attribute__((aligned(16))) uint16_t xs2[XSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t ws0[R_TILE];
   __shared__ __attribute__((aligned(16))) uint16_t ws1[R_TILE];
-  __shared__ __attribute__((aligned(16))) float2 pair[256 * kPairCopies];
-  for (int i = threadIdx.x; i < 256 * kPairCopies; i += kThreads) {
+  // Byte -> (row lo, row hi) table for the transposed-weight producers.
+  __shared__ __attribute__((aligned(16))) float2 pair[KN ? 256 * kPairCopies : 1];
+  for (int i = threadIdx.x; KN && i < 256 * kPairCopies; i += kThreads) {
     const int e = i / kPairCopies;
     pair[i] = make_float2(cb.v[e & 15], cb.v[e >> 4]);
   }
@@ -323,24 +359,24 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     Producer<KN, DQ> P;
     P.init(a, tid, n0);
     typename Producer<KN, DQ>::Set s0, s1;
-    if (steps > 0) P.issue(s0, 0);
-    if (steps > 1) P.issue(s1, 1);
-    if (steps > 0) P.store(s0, ws0, pair, lane);
-    if (steps > 2) P.issue(s0, 2);
+    // Loads are issued unconditionally (steps past the end re-read the last
+    // step), so that every path has the same loads in flight and the compiler
+    // waits only for the set a store consumes, two steps after its issue.
+    const int64_t last = steps - 1;   // steps >= 1
+    P.issue(s0, 0);
+    P.issue(s1, min<int64_t>(1, last));
+    P.store(s0, ws0, pair, cb.v, lane);
+    P.issue(s0, min<int64_t>(2, last));
     lds_barrier();
     // Step s: the MMA waves read stage s & 1; store step s+1 into the other
     // stage from its register set, then reuse that set for step s+3.
     for (int64_t s = 0; s < steps; s += 2) {
-      if (s + 1 < steps) {
-        P.store(s1, ws1, pair, lane);
-        if (s + 3 < steps) P.issue(s1, s + 3);
-      }
+      if (s + 1 < steps) P.store(s1, ws1, pair, cb.v, lane);
+      P.issue(s1, min<int64_t>(s + 3, last));
       lds_barrier();
       if (s + 1 >= steps) break;
-      if (s + 2 < steps) {
-        P.store(s0, ws0, pair, lane);
-        if (s + 4 < steps) P.issue(s0, s + 4);
-      }
+      if (s + 2 < steps) P.store(s0, ws0, pair, cb.v, lane);
+      P.issue(s0, min<int64_t>(s + 4, last));
       lds_barrier();
     }
     for (int64_t e = 0; e < epi_steps; ++e) {
@@ -417,46 +453,51 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
       for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
-  Frag f0, f1;
-  // One step: stages (xc, wc) now, (xn, wn) next, x2 is refilled for step s + 2
-  // (it was last read in step s - 1).  f0 holds slice 0 of step s on entry and
-  // slice 0 of step s + 1 on exit.
+  // Fragment reads run two slices ahead of the MFMAs that use them (three
+  // fragment buffers rotate).  One step: stages (xc, wc) now, (xn, wn) next,
+  // x2 is refilled for step s + 2 (it was last read in step s - 1).  On entry
+  // F0 and F1 hold slices 0 and 1 of step s; on exit F1 and F2 hold slices 0
+  // and 1 of step s + 1, so the next step takes (F1, F2, F0).
   auto step = [&](int64_t s, const uint16_t *xc, const uint16_t *wc, const uint16_t *xn, const uint16_t *wn,
-                  uint16_t *x2) {
+                  uint16_t *x2, Frag &F0, Frag &F1, Frag &F2) {
     if (s + 2 < steps) issue_x(s + 2, x2);
-    read_f(f1, xc, wc, 1);
+    read_f(F2, xc, wc, 2);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f0);
-    read_f(f0, xc, wc, 2);
+    mma(F0);
+    read_f(F0, xc, wc, 3);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f1);
-    read_f(f1, xc, wc, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f0);
+    mma(F1);
     if (s + 1 < steps) wait_x(s + 2 < steps);
     lds_barrier();
-    if (s + 1 < steps) read_f(f0, xn, wn, 0);
+    if (s + 1 < steps) read_f(F1, xn, wn, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f1);
+    mma(F2);
+    if (s + 1 < steps) read_f(F2, xn, wn, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(F0);
   };
+  Frag fa, fb, fc;
   if (steps > 0) issue_x(0, xs0);
   if (steps > 1) issue_x(1, xs1);
   if (steps > 0) wait_x(steps > 1);
   lds_barrier();
-  if (steps > 0) read_f(f0, xs0, ws0, 0);
+  if (steps > 0) {
+    read_f(fa, xs0, ws0, 0);
+    read_f(fb, xs0, ws0, 1);
+  }
   // Step s uses activation stage s % 3 and weight stage s % 2.
   for (int64_t s = 0; s < steps; s += 6) {
-    step(s, xs0, ws0, xs1, ws1, xs2);
+    step(s, xs0, ws0, xs1, ws1, xs2, fa, fb, fc);
     if (s + 1 >= steps) break;
-    step(s + 1, xs1, ws1, xs2, ws0, xs0);
+    step(s + 1, xs1, ws1, xs2, ws0, xs0, fb, fc, fa);
     if (s + 2 >= steps) break;
-    step(s + 2, xs2, ws0, xs0, ws1, xs1);
+    step(s + 2, xs2, ws0, xs0, ws1, xs1, fc, fa, fb);
     if (s + 3 >= steps) break;
-    step(s + 3, xs0, ws1, xs1, ws0, xs2);
+    step(s + 3, xs0, ws1, xs1, ws0, xs2, fa, fb, fc);
     if (s + 4 >= steps) break;
-    step(s + 4, xs1, ws0, xs2, ws1, xs0);
+    step(s + 4, xs1, ws0, xs2, ws1, xs0, fb, fc, fa);
     if (s + 5 >= steps) break;
-    step(s + 5, xs2, ws1, xs0, ws0, xs1);
+    step(s + 5, xs2, ws1, xs0, ws0, xs1, fc, fa, fb);
   }
 
   // ---- adapter term: contraction over j < r, zero-padded to steps of 64.  The
