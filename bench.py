@@ -70,12 +70,12 @@ KERNEL_SOURCE = {
 # copy in the same run.  Keyed by kernel; `sha256` is that of the kernel's source
 # file and qn_device.h when the counters were taken.
 TRAFFIC = {  # profiles/qlora_step_4096_hbm_traffic.md
-    "dequant": {"bytes": 42308229, "sha256": "7cc4ff9fd5317e838f1218950094ab0df45bb777c8ffb967ded48206eed8c6c9"},
-    "double_quant": {"bytes": 1372028, "sha256": "7cc4ff9fd5317e838f1218950094ab0df45bb777c8ffb967ded48206eed8c6c9"},
-    "gemv": {"bytes": 9238715, "sha256": "e2c9c7a8c8501cd2a70a38a7a28dca8bf000a60cc63373838c8f8a4a67072ca7"},
-    "gemm_fwd": {"bytes": 85977974, "sha256": "b016d16203d871666b2270d3c09616f962d10eafb54c3bed0aea9fe8d35d5392"},
-    "gemm_dx": {"bytes": 87195201, "sha256": "b016d16203d871666b2270d3c09616f962d10eafb54c3bed0aea9fe8d35d5392"},
-    "quantize": {"bytes": 80814358, "sha256": "7cc4ff9fd5317e838f1218950094ab0df45bb777c8ffb967ded48206eed8c6c9"},
+    "dequant": {"bytes": 42279778, "sha256": "685b727f3ace0ab5baaab7fae7caf0296154c3b8716331c186555fdff73fad46"},
+    "double_quant": {"bytes": 1372099, "sha256": "685b727f3ace0ab5baaab7fae7caf0296154c3b8716331c186555fdff73fad46"},
+    "gemv": {"bytes": 9237535, "sha256": "cffe7974ae6c99da4466ac54b0a8dbee87026feb7db37c7d4b5d809cddaa771f"},
+    "gemm_fwd": {"bytes": 86018856, "sha256": "f3a0594cd5ac799e766bba0da0f12316bc8f0a488dbe66fe665bb208c56eddf5"},
+    "gemm_dx": {"bytes": 87200466, "sha256": "f3a0594cd5ac799e766bba0da0f12316bc8f0a488dbe66fe665bb208c56eddf5"},
+    "quantize": {"bytes": 76629216, "sha256": "685b727f3ace0ab5baaab7fae7caf0296154c3b8716331c186555fdff73fad46"},
 }
 
 
