@@ -180,3 +180,32 @@ def test_70b_layer_shapes_sampled():
     _check("Y decode", host(Y), Yref)
     run_full_size_sampled(N, K, L["M_prefill"], L["r"], L["alpha"], w_std=L["w_std"], outliers=True,
                           bwd=False, seed=4, rows=32)
+
+
+def test_qwen_gate_sampled():
+    q = synth.QWEN7B
+    N, K = q["linears"]["gate"]
+    say(f"qwen gate {N}x{K} M=4096 fwd+bwd")
+    run_full_size_sampled(N, K, q["M"], q["r"], q["alpha"], seed=5, rows=16)
+
+
+@pytest.mark.parametrize("name", ["gate", "down"])
+def test_70b_large_linears(name):
+    """The two largest 70B-layer linears: decode (every output checked) and the
+    M=4096 forward on sampled rows; the down projection has the longest
+    contraction (28672)."""
+    L = synth.L70B
+    N, K = L["linears"][name]
+    say(f"70b {name} {N}x{K} M=1 and M=4096 fwd")
+    c = Case(N, K, 1, L["r"], L["alpha"], seed=6, w_std=L["w_std"], outliers=True)
+    w, X, A, B, _ = c.device()
+    Wh = c.oracle_weight()
+    Y = lib.qlora_linear_fwd(X, w, A, B, c.alpha)
+    Yref, _ = oracle.forward(c.X, Wh, c.A, c.B, c.alpha)
+    _check("Y decode", host(Y), Yref)
+    M = L["M_prefill"]
+    Xp = synth.to_bf16(synth.gaussian((M, K), 1.0, synth.SEED_X + 60))
+    sel = _sampled_rows(M, 16, 61)
+    Yp = lib.qlora_linear_fwd(Xp.to(dev()), w, A, B, c.alpha)
+    Yref, _ = oracle.forward(synth.bf16_values(Xp)[sel], Wh, c.A, c.B, c.alpha)
+    _check("Y prefill rows", host(Yp)[sel], Yref)
