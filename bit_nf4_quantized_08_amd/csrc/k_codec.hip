@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void double_quant_kernel(const float *__r
 // shuffle.  Each store instruction of the wave writes one contiguous 1 KB span:
 // bf16 output, 8 elements (one 32-bit word of codes) per lane per instruction;
 // fp32 output, 4 elements (16 bits of codes) per lane per instruction.  The
-// byte -> (row lo, row hi) table lives in LDS, one copy per lane of a 16-lane
+// byte -> (row lo, row hi) table lives in LDS, one copy per lane of an 8-lane
 // group so that the lookups of a group hit distinct banks.
 __device__ __forceinline__ float block_scale(const ScaleSrc &sc, int64_t b) {
   if (sc.absmax_q) return (float)sc.absmax_q[b] * sc.scale2[b / QN_GROUP];
@@ -212,7 +212,7 @@ __device__ __forceinline__ float block_scale(const ScaleSrc &sc, int64_t b) {
 }
 
 constexpr int kDqChunk = 2048;   // elements per wave iteration
-constexpr int kDqCopies = 16;
+constexpr int kDqCopies = 8;
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ codes, ScaleSrc sc,
@@ -321,7 +321,7 @@ hipError_t launch_dequant(const qn_nf4_weight &W, void *out, int out_bf16, hipSt
   const CodecTables &tab = codec_tables();
   const int64_t n = W.N * W.K;
   ScaleSrc sc{W.absmax, W.absmax_q, W.scale2};
-  const int grid = grid_for((n + 7) / 8);
+  const int grid = grid_for((n + 7) / 8, 4);   // a few resident workgroups per CU, each building its table once
   TraceScope tr(QN_TRACE_DEQUANT, s);
   if (out_bf16)
     hipLaunchKernelGGL(dequant_kernel<true>, dim3(grid), dim3(kThreads), 0, s, W.codes, sc, n, out, tab);
