@@ -5,26 +5,31 @@
 // expansion cannot be skipped": for every multiply the kernel reads the 4-bit
 // codes of a block of weights, looks each up in the sixteen-row table,
 // multiplies by the block's scale, writes the bf16 result to on-chip memory,
-// and only then feeds the matrix unit.  Here: codes -> byte-pair table in LDS
-// -> fp32 product with the block scale -> bf16 (round to nearest even) -> LDS
-// tile -> v_mfma_f32_32x32x16_bf16.
+// and only then feeds the matrix unit.  Here every code becomes
+// bf16(fl32(c[q] * A)) (round to nearest even) in an LDS tile that feeds
+// v_mfma_f32_32x32x16_bf16: row-major weights through byte permutes in
+// registers, transposed weights through a byte-pair table in LDS.
 //
 // Tiling.  A workgroup computes a 256 x 128 output tile with 8 waves in two
 // roles.
 //   * Four MMA waves (one per SIMD), each owning 64 rows x 128 columns (2 x 4
-//     MFMA tiles of 32 x 32).  A wave loads its own activation rows straight
-//     from global memory into registers in MFMA operand layout (buffer loads,
-//     one step ahead), reads the dequantised weight fragments from LDS, and
-//     issues the MFMAs.  Activations never pass through LDS, which keeps LDS
-//     traffic at the weight tile: the resource this kernel is bound by.
-//   * Four producer waves load the weight codes and block scales of the next
-//     step, dequantise them and write the next LDS stage.  Sharing each SIMD
-//     with an MMA wave, their VALU work overlaps the matrix-core work.
-// The contraction runs in steps of 64 (one NF4 block along K), double-buffered
-// in LDS with one barrier per step.  Within a step, lane half h of an MMA wave
-// covers contraction indices [32h, 32h+32) (so its activation row slice is 64
-// contiguous bytes); slice c of the four MFMA k-slices uses [32h+8c, 32h+8c+8)
-// for both operands, which leaves the contraction unchanged.
+//     MFMA tiles of 32 x 32).  A wave moves its own activation rows from
+//     global memory into LDS with direct-to-LDS loads (three stages, two steps
+//     ahead, waited for with explicit vmcnt), reads the operand fragments from
+//     LDS two k-slices ahead of the MFMAs that use them, and issues the MFMAs.
+//   * Four producer waves load the weight codes and block scales two steps
+//     ahead into registers, dequantise them and write the next weight stage.
+//     Sharing each SIMD with an MMA wave, their VALU work overlaps the
+//     matrix-core work.
+// The contraction runs in steps of 64 (one NF4 block along K), the weight
+// stage double-buffered in LDS, one barrier per step.  Within a step, lane
+// half h of an MMA wave covers contraction indices [32h, 32h+32); slice c of
+// the four MFMA k-slices uses [32h+8c, 32h+8c+8) for both operands, which
+// leaves the contraction unchanged.
+// The adapter term is one more step after the last weight step: its left
+// operand (H or dH, zero beyond ldl2) comes through the activation stages and
+// its right operand (B or A, zero beyond r) through the weight stage, into
+// the same accumulators before the bf16 store.
 //
 // Weight layouts:
 //   NK (forward): output column n reads weight row n, contraction along K; a
@@ -33,11 +38,9 @@
 //      loads 32 codes of one row (16 bytes, one block), the four lanes of a
 //      quad transpose their words with DPP so that each lane holds a 4 x 8
 //      patch (4 rows, 8 columns), and the patch is written transposed.
-// The stage layout is XOR-swizzled in 16-byte chunks so that both the
-// producers' writes and the MMA waves' fragment reads are free of bank
-// conflicts.
-// The adapter term runs as extra contraction steps over j < r into the same
-// accumulators before the bf16 store.
+// Both stage layouts are XOR-swizzled in 16-byte chunks so that the fragment
+// reads and the weight-stage writes are free of bank conflicts (see kswz and
+// the activation-stage comment below).
 
 #include <algorithm>
 
@@ -312,21 +315,33 @@ struct Producer {
   }
 };
 
-// Adapter-term right operand for extra contraction step `e` (j in [64e, 64e+64)),
-// zero-padded, written to a weight stage by `nt` threads starting at thread `t`.
+// Adapter term as one more contraction step (r <= 64 = BK): its right operand,
+// positions j < r of the tile's 128 columns (zero beyond r and beyond Nout),
+// is fetched by the producers into registers when the kernel starts and
+// written to the weight stage after the last weight step.  Producer thread t
+// owns column t & 127, positions 32 (t >> 7) .. +31: 32 independent 2-byte
+// loads (R2 need not be 16-byte aligned), one latency in all.
 template <bool EPI_NK>
-__device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n0, int64_t e, uint16_t *Rs, int t,
-                                                   int nt) {
-  const int64_t j0 = e * BK;
-  for (int idx = t; idx < BN * BK; idx += nt) {
-    int row, jj;
-    if constexpr (EPI_NK) { row = idx >> 6; jj = idx & 63; }
-    else { jj = idx / BN; row = idx % BN; }
-    const int64_t gn = n0 + row, gj = j0 + jj;
-    uint16_t v = 0;
-    if (gj < a.r && gn < a.Nout) v = EPI_NK ? a.R2[gn * a.ldr2 + gj] : a.R2[gj * a.ldr2 + gn];
-    Rs[row * LD + (jj ^ kswz(row))] = v;
+__device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n0, int t, uint32_t (&v)[16]) {
+  const int row = t & (BN - 1), j0 = 32 * (t >> 7);
+  const int64_t gn = n0 + row;
+  const rsrc_t rr = make_rsrc(a.R2, EPI_NK ? a.Nout * a.ldr2 * 2 : a.r * a.ldr2 * 2);
+  uint32_t h[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int64_t j = j0 + i;
+    const bool in = j < a.r && gn < a.Nout;
+    const uint32_t off = in ? (uint32_t)((EPI_NK ? gn * a.ldr2 + j : j * a.ldr2 + gn) * 2) : kOutOfRange;
+    h[i] = __builtin_amdgcn_raw_buffer_load_b16(rr, off, 0, 0);
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = (h[2 * i] & 0xFFFFu) | (h[2 * i + 1] << 16);
+}
+__device__ __forceinline__ void store_adapter_right(const uint32_t (&v)[16], uint16_t *Rs, int t) {
+  const int row = t & (BN - 1), j0 = 32 * (t >> 7);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<u32x4 *>(&Rs[row * LD + ((j0 + 8 * q) ^ kswz(row))]) = u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
 }
 
 // Workgroup barrier that orders the waves' own LDS reads and writes only:
@@ -372,7 +387,9 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool producer = wave >= 4;
   const int64_t steps = __builtin_amdgcn_readfirstlane((int)(a.Kc / BK));
-  const int64_t epi_steps = (a.r + BK - 1) / BK;
+  // Contraction steps of 64: Kc / 64 weight steps, then one adapter step
+  // (left operand L2, zero beyond ldl2; right operand R2 restricted to j < r).
+  const int64_t total = steps + 1;
   lds_barrier();  // pair table
 
   if (producer) {
@@ -390,6 +407,8 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     // sets in flight in the same order as at its back edge (set 0 older; the
     // scheduling barrier keeps them in that order), so the compiler waits only
     // for the older set at each store.
+    uint32_t adapter[16];
+    load_adapter_right<EPI_NK>(a, n0, tid, adapter);
     P.issue(s0, 0);
     __builtin_amdgcn_sched_barrier(0);
     P.issue(s1, __builtin_amdgcn_readfirstlane(min(1, last)));
@@ -398,15 +417,15 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
       P.issue(s0, min(s + 2, last));
       lds_barrier();
       if (s + 1 < nsteps) P.store(s1, ws1, pair, cb.v, lane);
+      else store_adapter_right(adapter, ws1, tid);   // step nsteps (odd) goes to stage 1
       P.issue(s1, min(s + 3, last));
       lds_barrier();
     }
-    if ((nsteps & 1) == 0) lds_barrier();   // the MMA waves' barrier after the last step
-    for (int64_t e = 0; e < epi_steps; ++e) {
-      load_adapter_right<EPI_NK>(a, n0, e, ws0, threadIdx.x, kThreads);
-      lds_barrier();
+    if ((nsteps & 1) == 0) {
+      store_adapter_right(adapter, ws0, tid);        // step nsteps (even) goes to stage 0
       lds_barrier();
     }
+    lds_barrier();   // the MMA waves' barrier after the adapter step
     return;
   }
 
@@ -436,11 +455,28 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     const int row = 8 * g + (lane >> 3), slot = lane & 7;
     xoff[g] = (uint32_t)(row * a.ldl * 2 + ((slot ^ ((row >> 1) & 7)) * 16));
   }
+  // Step `steps` (the adapter step) takes its left operand, columns 0..63 of
+  // L2, through the same stages; columns at or beyond ldl2 read as zero.
+  const u32x4 l2desc = raw_desc(a.L2 + wrow0 * a.ldl2, (a.M - wrow0) * a.ldl2 * 2);
   auto issue_x = [&](int64_t s, uint16_t *stage) {
     const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(stage + wave_u * XW));
-    const int soff = __builtin_amdgcn_readfirstlane((int)(s * BK * 2));
+    if (s < steps) {
+      const int soff = __builtin_amdgcn_readfirstlane((int)(s * BK * 2));
 #pragma unroll
-    for (int g = 0; g < 8; ++g) dma_lds16(xdesc, dst + g * 1024, xoff[g], soff);
+      for (int g = 0; g < 8; ++g) dma_lds16(xdesc, dst + g * 1024, xoff[g], soff);
+    } else {
+      // The lane index passes through an empty asm so that these eight offsets
+      // are computed here, once, instead of being hoisted out of the loop and
+      // held in registers through every step.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int row = 8 * g + (ln >> 3), col = 8 * ((ln & 7) ^ ((row >> 1) & 7));
+        const uint32_t off = col < a.ldl2 ? (uint32_t)((row * a.ldl2 + col) * 2) : kOutOfRange;
+        dma_lds16(l2desc, dst + g * 1024, off, 0);
+      }
+    }
   };
   // Wait until the activation stage of the next step has landed: the only
   // vector memory operations of an MMA wave in the main loop are these loads,
@@ -484,14 +520,14 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
   // and 1 of step s + 1, so the next step takes (F1, F2, F0).
   auto step = [&](int64_t s, const uint16_t *xc, const uint16_t *wc, const uint16_t *xn, const uint16_t *wn,
                   uint16_t *x2, Frag &F0, Frag &F1, Frag &F2) {
-    if (s + 2 < steps) issue_x(s + 2, x2);
+    if (s + 2 < total) issue_x(s + 2, x2);
     read_f(F2, xc, wc, 2);
     __builtin_amdgcn_sched_barrier(0);
     mma(F0);
     read_f(F0, xc, wc, 3);
     __builtin_amdgcn_sched_barrier(0);
     mma(F1);
-    if (s + 1 < steps) wait_x(s + 2 < steps);
+    if (s + 1 < steps) wait_x(s + 2 < total);
     lds_barrier();
     if (s + 1 < steps) read_f(F1, xn, wn, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -501,14 +537,12 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     mma(F0);
   };
   Frag fa, fb, fc;
-  if (steps > 0) issue_x(0, xs0);
-  if (steps > 1) issue_x(1, xs1);
-  if (steps > 0) wait_x(steps > 1);
+  issue_x(0, xs0);   // steps >= 1; step 1 may be the adapter step
+  issue_x(1, xs1);
+  wait_x(true);
   lds_barrier();
-  if (steps > 0) {
-    read_f(fa, xs0, ws0, 0);
-    read_f(fb, xs0, ws0, 1);
-  }
+  read_f(fa, xs0, ws0, 0);
+  read_f(fb, xs0, ws0, 1);
   // Step s uses activation stage s % 3 and weight stage s % 2.
   for (int64_t s = 0; s < steps; s += 6) {
     step(s, xs0, ws0, xs1, ws1, xs2, fa, fb, fc);
@@ -524,48 +558,64 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     step(s + 5, xs2, ws1, xs0, ws0, xs1, fc, fa, fb);
   }
 
-  // ---- adapter term: contraction over j < r, zero-padded to steps of 64.  The
-  // left operand (leading dim ldl2, readable up to column ldl2, a multiple of 8
-  // zero-padded beyond r) is loaded straight into registers in operand layout
-  // (lane half lh takes j in [32 lh, 32 lh + 32)); the right operand goes
-  // through weight stage 0.
-  const rsrc_t rl2 = make_rsrc(a.L2 + m0 * a.ldl2, (a.M - m0) * a.ldl2 * 2);
+  // ---- adapter step: its left operand (direct-to-LDS, issued two steps
+  // ago) sits in activation stage steps % 3, its right operand in weight stage
+  // steps & 1 (written by the producers before the main loop's last barrier).
+  // The trip count is written in terms of r (it is 1 for every 1 <= r <= 64):
+  // with a constant count the code after the main loop becomes straight-line
+  // and the register allocator then spills the accumulators inside the loop.
+  const int64_t epi_steps = (a.r + BK - 1) / BK;
   for (int64_t e = 0; e < epi_steps; ++e) {
-    u32x4 av[TM][4];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int64_t j = e * BK + lh * 32 + c * 8;
-        const uint32_t off = j < a.ldl2 ? (uint32_t)(((wave * WM + i * 32 + lr) * a.ldl2 + j) * 2) : kOutOfRange;
-        av[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rl2, off, 0, 0);
-      }
-    load_adapter_right<EPI_NK>(a, n0, e, ws0, threadIdx.x, kThreads);
-    lds_barrier();
+    const int xi = (int)(steps % 3);
+    const uint16_t *xa = xi == 0 ? xs0 : (xi == 1 ? xs1 : xs2);
+    const uint16_t *wa = (steps & 1) ? ws1 : ws0;
+    wait_x(false);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       Frag f;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) f.a[i] = __builtin_bit_cast(bf16x8, av[i][c]);
-      read_b(f.b, ws0, c);
+      read_f(f, xa, wa, c);
       mma(f);
     }
-    lds_barrier();
+    lds_barrier();   // pairs with the producers' last barrier
   }
 
-  // ---- store bf16: element e of a 32x32 tile is row 8*(e/4)+4*lh+(e%4), column lr.
+  // ---- store bf16 through LDS.  Element e of a 32 x 32 accumulator tile is
+  // row 8*(e/4) + 4*lh + (e%4), column lr: stored straight to global memory
+  // that is 2 bytes per lane and 128 stores per lane.  Instead each wave
+  // writes its two 32 x 128 blocks into the activation stages (all LDS reads
+  // ended at the barrier above; only this wave touches its blocks) with a row
+  // pitch of kOutPitch (rows r and r + 4 land 16 banks apart), then reads back
+  // 16-byte row chunks and stores them whole: 16 row-contiguous stores per
+  // wave.  Rows at or beyond M fall outside the buffer and are dropped;
+  // columns beyond Nout (or an output not 16-byte aligned) take element stores.
+  constexpr int kOutPitch = BN + 8;
+  static_assert(3 * 32 * kOutPitch <= XSTAGE, "three output blocks per activation stage");
+  const rsrc_t rout = make_rsrc(a.out + m0 * a.ldo, (a.M - m0) * a.ldo * 2);
+  const bool vec_ok = (a.ldo & 7) == 0 && ((uint64_t)a.out & 15) == 0;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    const int k = 2 * wave_u + i;   // output block 0..7: three per activation stage
+    uint16_t *blk = (k < 3 ? xs0 : (k < 6 ? xs1 : xs2)) + (k % 3) * 32 * kOutPitch;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t gn = n0 + j * 32 + lr;
-      if (gn >= a.Nout) continue;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t gm = m0 + wave * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-        if (gm < a.M) a.out[gm * a.ldo + gn] = f32_to_bf16(acc[i][j][e]);
+      for (int e = 0; e < 16; ++e)
+        blk[(8 * (e >> 2) + 4 * lh + (e & 3)) * kOutPitch + j * 32 + lr] = f32_to_bf16(acc[i][j][e]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 4 * q + (lane >> 4), c8 = 8 * (lane & 15);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&blk[row * kOutPitch + c8]);
+      const int64_t lrow = (int64_t)wave_u * WM + i * 32 + row, gn = n0 + c8;
+      if (vec_ok && gn + 8 <= a.Nout) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, rout, (uint32_t)((lrow * a.ldo + gn) * 2), 0, 0);
+      } else if (m0 + lrow < a.M) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (gn + t < a.Nout) a.out[(m0 + lrow) * a.ldo + gn + t] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
       }
     }
+  }
 }
 
 int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
@@ -573,6 +623,9 @@ int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
 template <bool KN, bool EPI_NK>
 hipError_t launch(const QGemmArgs &a0, hipStream_t st, int trace_kind) {
   QGemmArgs a = a0;
+  // The adapter term is exactly one extra contraction step, and the producer
+  // and MMA waves count their barriers on that: reject any other rank here.
+  if (a.r < 1 || a.r > BK || a.Kc < BK || a.Kc % BK != 0) return hipErrorInvalidValue;
   a.tiles_m = (int)cdiv(a.M, BM);
   a.tiles_n = (int)cdiv(a.Nout, BN);
   // Row-tile group size: each XCD runs T/8 tiles; choose the group so that an
