@@ -449,12 +449,14 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
   // one 128-byte line.
   const int64_t wrow0 = m0 + (int64_t)wave_u * WM;
   const u32x4 xdesc = raw_desc(a.L + wrow0 * a.ldl, (a.M - wrow0) * a.ldl * 2);
-  uint32_t xoff[8];
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int row = 8 * g + (lane >> 3), slot = lane & 7;
-    xoff[g] = (uint32_t)(row * a.ldl * 2 + ((slot ^ ((row >> 1) & 7)) * 16));
-  }
+  // Load g covers rows 8g + lane/8; the chunk swizzle (row >> 1) & 7 equals
+  // (lane >> 4) ^ 4 (g & 1), so the eight per-lane offsets are two bases (even
+  // and odd g) plus 8g rows.  They are formed at issue time from the bases
+  // (kept opaque to the compiler, which would otherwise hold all eight in
+  // registers through the loop).
+  const uint32_t xbase0 = (uint32_t)((lane >> 3) * a.ldl * 2 + (((lane & 7) ^ (lane >> 4)) * 16));
+  const uint32_t xbase1 = xbase0 ^ 64u;   // chunk index ^ 4
+  const uint32_t xrow8 = (uint32_t)(8 * a.ldl * 2);
   // Step `steps` (the adapter step) takes its left operand, columns 0..63 of
   // L2, through the same stages; columns at or beyond ldl2 read as zero.
   const u32x4 l2desc = raw_desc(a.L2 + wrow0 * a.ldl2, (a.M - wrow0) * a.ldl2 * 2);
@@ -462,8 +464,10 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(stage + wave_u * XW));
     if (s < steps) {
       const int soff = __builtin_amdgcn_readfirstlane((int)(s * BK * 2));
+      uint32_t b0 = xbase0, b1 = xbase1;
+      asm volatile("" : "+v"(b0), "+v"(b1));
 #pragma unroll
-      for (int g = 0; g < 8; ++g) dma_lds16(xdesc, dst + g * 1024, xoff[g], soff);
+      for (int g = 0; g < 8; ++g) dma_lds16(xdesc, dst + g * 1024, ((g & 1) ? b1 : b0) + (uint32_t)g * xrow8, soff);
     } else {
       // The lane index passes through an empty asm so that these eight offsets
       // are computed here, once, instead of being hoisted out of the loop and
