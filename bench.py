@@ -70,12 +70,12 @@ KERNEL_SOURCE = {
 # copy in the same run.  Keyed by kernel; `sha256` is that of the kernel's source
 # file and qn_device.h when the counters were taken.
 TRAFFIC = {  # profiles/qlora_step_4096_hbm_traffic.md
-    "dequant": {"bytes": 42279778, "sha256": "685b727f3ace0ab5baaab7fae7caf0296154c3b8716331c186555fdff73fad46"},
-    "double_quant": {"bytes": 1372099, "sha256": "685b727f3ace0ab5baaab7fae7caf0296154c3b8716331c186555fdff73fad46"},
-    "gemv": {"bytes": 9237535, "sha256": "cffe7974ae6c99da4466ac54b0a8dbee87026feb7db37c7d4b5d809cddaa771f"},
-    "gemm_fwd": {"bytes": 86018856, "sha256": "f3a0594cd5ac799e766bba0da0f12316bc8f0a488dbe66fe665bb208c56eddf5"},
-    "gemm_dx": {"bytes": 87200466, "sha256": "f3a0594cd5ac799e766bba0da0f12316bc8f0a488dbe66fe665bb208c56eddf5"},
-    "quantize": {"bytes": 76629216, "sha256": "685b727f3ace0ab5baaab7fae7caf0296154c3b8716331c186555fdff73fad46"},
+    "dequant": {"bytes": 42278069, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
+    "double_quant": {"bytes": 1372128, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
+    "gemv": {"bytes": 9237570, "sha256": "965c98b0480111aae938d1ca83002854798ba89c043e8789d3525341bef1dc55"},
+    "gemm_fwd": {"bytes": 86031408, "sha256": "fd5184e4f1a3da72b425b9c62892c16a91290e6636a11a41c0aa1dd080da009b"},
+    "gemm_dx": {"bytes": 87225254, "sha256": "fd5184e4f1a3da72b425b9c62892c16a91290e6636a11a41c0aa1dd080da009b"},
+    "quantize": {"bytes": 76629733, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
 }
 
 
