@@ -92,6 +92,15 @@ def test_mfma_path(M, N, r):
     run_fwd_bwd(Case(N, 512, M, r, 2.0 * r, seed=M + N))
 
 
+@pytest.mark.parametrize("K,N", [(64, 128), (128, 64), (192, 192), (320, 128), (256, 320)])
+def test_mfma_path_short_contraction(K, N):
+    """1 to 5 contraction steps of 64 in the forward (over K) and in dX (over
+    N): the pipeline's prologue, its last steps and the adapter step at every
+    phase of the stage rotation."""
+    say(f"mfma path short contraction K={K} N={N}")
+    run_fwd_bwd(Case(N, K, 77, 8, 16.0, seed=K + N))
+
+
 @pytest.mark.parametrize("M", [4, 200])
 def test_adapter_term_alone(M):
     """W = 0: the output is only (alpha/r) (X A^T) B^T, checked on its own scale."""
