@@ -478,8 +478,11 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float *__
 // the block scale applied to each 32-weight partial sum.  Lane l of a wave owns
 // 32 consecutive k of every 2048-wide chunk (16 bytes of codes).  A wave works on
 // RPW rows at once so that each lane's x registers are reused RPW times.
-// Blocks with blockIdx.x >= gemv_blocks instead compute H partials:
-// h_part[split][m][j] = sum_k x[m][k] * A[j][k].
+// The first h_blocks blocks instead compute H partials,
+// h_part[split][m][j] = sum over the split's K-range of x[m][k] * A[j][k]:
+// block b takes K-range b % hsplits and adapter rows 4 (b / hsplits) .. +3,
+// one per wave, so that every wave makes a single pass and H is spread over
+// many short blocks that start first.
 constexpr int GEMV_RPW = 4;                       // rows per wave
 constexpr int GEMV_ROWS = GEMV_RPW * (kThreads / 64);  // rows per workgroup
 
@@ -494,7 +497,8 @@ struct GemvArgs {
   float *h_part;      // [hsplits][M][64]
   int64_t k_per_split;   // multiple of 2048 (or K)
   int splits;
-  int gemv_blocks;    // row-blocks * splits
+  int h_blocks;       // hsplits * ceil(r / 4)
+  int hsplits;
   int64_t hk_per_split;  // H partial K-range per block (multiple of 2048 or K)
 };
 
@@ -532,13 +536,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
   __syncthreads();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  if ((int)blockIdx.x >= a.gemv_blocks) {
-    // ---- H partials: this block covers K-range hb of length hk_per_split.
-    const int hb = blockIdx.x - a.gemv_blocks;
+  if ((int)blockIdx.x < a.h_blocks) {
+    // ---- H partials (see above).
+    const int hb = (int)blockIdx.x % a.hsplits;
     const int64_t kb = (int64_t)hb * a.hk_per_split;
     const int64_t ke = min(a.K, kb + a.hk_per_split);
-    // Wave w handles adapter rows j = w, w+4, ...
-    for (int j = wave; j < a.r; j += kThreads / 64) {
+    const int j = 4 * ((int)blockIdx.x / a.hsplits) + wave;
+    if (j < a.r) {
       float hm[MM];
 #pragma unroll
       for (int m = 0; m < MM; ++m) hm[m] = 0.0f;
@@ -567,8 +571,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
     return;
   }
 
-  const int rb = blockIdx.x / a.splits;
-  const int split = blockIdx.x % a.splits;
+  const int gb = (int)blockIdx.x - a.h_blocks;
+  const int rb = gb / a.splits;
+  const int split = gb % a.splits;
   const int64_t n_base = (int64_t)rb * GEMV_ROWS + wave * GEMV_RPW;
   const int64_t kb = (int64_t)split * a.k_per_split;
   const int64_t ke = min(a.K, kb + a.k_per_split);
@@ -753,9 +758,10 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
     float *y_part = c.take<float>((int64_t)splits * a.M * a.N);
     float *h_part = c.take<float>((int64_t)hsplits * a.M * 64);
     const int row_blocks = (int)cdiv(a.N, GEMV_ROWS);
+    const int h_blocks = hsplits * (int)cdiv(a.r, 4);
     GemvArgs ga{a.X, a.M, a.N, a.K, a.codes, a.sc, a.A, a.r, y_part, h_part, kps, splits,
-                row_blocks * splits, hkps};
-    dim3 grid((unsigned)(row_blocks * splits + hsplits));
+                h_blocks, hsplits, hkps};
+    dim3 grid((unsigned)(h_blocks + row_blocks * splits));
     const Code16 cb = code16();
     TraceScope tr(QN_TRACE_GEMV, st);
     if (a.M == 1) hipLaunchKernelGGL(gemv_kernel<1>, grid, dim3(kThreads), 0, st, ga, cb);

@@ -86,6 +86,14 @@ def test_decode_path_small_M(M):
     run_fwd_bwd(Case(256, 512, M, 8, 16.0, seed=M), bwd=(M == 5))
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 192, 3584), (2, 64, 2560), (3, 320, 6208), (1, 1024, 8192)])
+def test_decode_path_ragged(M, N, K):
+    """Contraction lengths that are not a multiple of the decode path's
+    2048-wide chunk (its out-of-range loads), and one that is."""
+    say(f"decode path ragged M={M} N={N} K={K}")
+    run_fwd_bwd(Case(N, K, M, 16, 32.0, seed=N + K), bwd=False)
+
+
 @pytest.mark.parametrize("M,N,r", [(9, 256, 8), (64, 256, 16), (77, 192, 24), (300, 320, 64), (130, 64, 1)])
 def test_mfma_path(M, N, r):
     say(f"mfma path M={M} N={N} r={r}")
