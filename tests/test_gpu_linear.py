@@ -94,6 +94,14 @@ def test_decode_path_ragged(M, N, K):
     run_fwd_bwd(Case(N, K, M, 16, 32.0, seed=N + K), bwd=False)
 
 
+@pytest.mark.parametrize("M,r", [(1, 1), (2, 7), (1, 64), (8, 40)])
+def test_decode_path_ranks(M, r):
+    """Adapter ranks that are and are not a multiple of 8 (the decode
+    epilogue's vector and scalar reads of B)."""
+    say(f"decode path M={M} r={r}")
+    run_fwd_bwd(Case(320, 1024, M, r, 2.0 * r, seed=100 + r), bwd=False)
+
+
 @pytest.mark.parametrize("M,N,r", [(9, 256, 8), (64, 256, 16), (77, 192, 24), (300, 320, 64), (130, 64, 1)])
 def test_mfma_path(M, N, r):
     say(f"mfma path M={M} N={N} r={r}")
