@@ -322,11 +322,10 @@ struct Producer {
 // owns column t & 127, positions 32 (t >> 7) .. +31: 32 independent 2-byte
 // loads (R2 need not be 16-byte aligned), one latency in all.
 template <bool EPI_NK>
-__device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n0, int t, uint32_t (&v)[16]) {
+__device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n0, int t, uint32_t (&h)[32]) {
   const int row = t & (BN - 1), j0 = 32 * (t >> 7);
   const int64_t gn = n0 + row;
   const rsrc_t rr = make_rsrc(a.R2, EPI_NK ? a.Nout * a.ldr2 * 2 : a.r * a.ldr2 * 2);
-  uint32_t h[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const int64_t j = j0 + i;
@@ -334,11 +333,14 @@ __device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n
     const uint32_t off = in ? (uint32_t)((EPI_NK ? gn * a.ldr2 + j : j * a.ldr2 + gn) * 2) : kOutOfRange;
     h[i] = __builtin_amdgcn_raw_buffer_load_b16(rr, off, 0, 0);
   }
+}
+// The 2-byte values are packed only here, at the use, so that the wait for
+// the loads falls at the end of the main loop.
+__device__ __forceinline__ void store_adapter_right(const uint32_t (&h)[32], uint16_t *Rs, int t) {
+  const int row = t & (BN - 1), j0 = 32 * (t >> 7);
+  uint32_t v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = (h[2 * i] & 0xFFFFu) | (h[2 * i + 1] << 16);
-}
-__device__ __forceinline__ void store_adapter_right(const uint32_t (&v)[16], uint16_t *Rs, int t) {
-  const int row = t & (BN - 1), j0 = 32 * (t >> 7);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     *reinterpret_cast<u32x4 *>(&Rs[row * LD + ((j0 + 8 * q) ^ kswz(row))]) = u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
@@ -354,6 +356,10 @@ __device__ __forceinline__ void store_adapter_right(const uint32_t (&v)[16], uin
 // in order that also waits for the fragment reads issued since.  The empty
 // asm and the asm barrier (both memory clobbers) keep LDS accesses on their
 // side of the wait.
+// s_waitcnt with vmcnt(n), the other counters unconstrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not constrained
@@ -397,34 +403,93 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     Producer<KN, DQ> P;
     P.init(a, tid, n0);
     typename Producer<KN, DQ>::Set s0, s1;
-    // Loads are issued unconditionally (steps past the end re-read the last
-    // step), so that every path has the same loads in flight and the compiler
-    // waits only for the set a store consumes, two steps after its issue.
     const int nsteps = __builtin_amdgcn_readfirstlane((int)steps), last = nsteps - 1;   // nsteps >= 1
-    // Step t goes to stage t & 1 from register set t & 1 before the t-th
-    // barrier (the MMA waves read it after that barrier), and the set is then
-    // reloaded for step t + 2.  The loop is entered with the loads of both
-    // sets in flight in the same order as at its back edge (set 0 older; the
-    // scheduling barrier keeps them in that order), so the compiler waits only
-    // for the older set at each store.
-    uint32_t adapter[16];
+    const int ntotal = nsteps + 1;   // contraction steps including the adapter step
+
+    // Activation stages.  Producer wave p moves the 64 rows of MMA wave p from
+    // global memory into LDS with direct-to-LDS loads (the compiler sees them,
+    // so its waits for the code sets stay exact).  Chunk k (16 bytes) of stage
+    // row r sits at slot k ^ ((r >> 1) & 7), so the fragment reads of 16
+    // consecutive rows hit 16 distinct bank groups.  Load g fills rows 8g ..
+    // 8g + 7 (1 KB in lane order): lane l writes slot l & 7 of row 8g + l / 8,
+    // every 8 lanes reading one 128-byte line; the swizzle (row >> 1) & 7 is
+    // (lane >> 4) ^ 4 (g & 1), so the offsets are two per-lane bases plus 8g
+    // rows.  Step `nsteps` (the adapter step) takes columns 0..63 of L2 (zero
+    // at or beyond ldl2) the same way.
+    const int pw = wave - 4;
+    const int64_t wrow0 = m0 + (int64_t)pw * WM;
+    const rsrc_t xr = make_rsrc(a.L + wrow0 * a.ldl, (a.M - wrow0) * a.ldl * 2);
+    const rsrc_t l2r = make_rsrc(a.L2 + wrow0 * a.ldl2, (a.M - wrow0) * a.ldl2 * 2);
+    const uint32_t c0 = (uint32_t)((lane & 7) ^ (lane >> 4));   // chunk for even g; odd g: c0 ^ 4
+    const uint32_t xbase0 = (uint32_t)((lane >> 3) * a.ldl * 2 + c0 * 16);
+    const uint32_t xbase1 = (uint32_t)((lane >> 3) * a.ldl * 2 + (c0 ^ 4u) * 16);
+    const uint32_t xrow8 = (uint32_t)(8 * a.ldl * 2);
+    // The adapter step reads L2 the same way (row pitch ldl2, columns at or
+    // beyond ldl2 zero); loads at t >= ntotal read zero (every offset out of
+    // range) into a slot that no one reads again, which keeps the number of
+    // loads per half-step fixed.  One branch-free issue path for all three:
+    // the resource and the scalar offset are chosen uniformly, the per-lane
+    // offset from precomputed bases.
+    const uint32_t l2base0 = (uint32_t)((lane >> 3) * a.ldl2 * 2 + c0 * 16);
+    const uint32_t l2base1 = (uint32_t)((lane >> 3) * a.ldl2 * 2 + (c0 ^ 4u) * 16);
+    const bool l2ok0 = 8 * (int64_t)c0 < a.ldl2, l2ok1 = 8 * (int64_t)(c0 ^ 4u) < a.ldl2;
+    const uint32_t l2row8 = (uint32_t)(8 * a.ldl2 * 2);
+    auto issue_x = [&](int t) {
+      const int i = t % 3;
+      const uint32_t base =
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr((i == 0 ? xs0 : (i == 1 ? xs1 : xs2)) + pw * XW));
+      const bool main_step = t < nsteps, live = t < ntotal;
+      const rsrc_t r = main_step ? xr : l2r;
+      const int soff = main_step ? t * BK * 2 : 0;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const bool odd = g & 1;
+        const uint32_t l2off =
+            live && (odd ? l2ok1 : l2ok0) ? (odd ? l2base1 : l2base0) + (uint32_t)g * l2row8 : kOutOfRange;
+        const uint32_t off = main_step ? (odd ? xbase1 : xbase0) + (uint32_t)g * xrow8 : l2off;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(size_t)(base + g * 1024),
+                                                 16, off, soff, 0, 0);
+      }
+    };
+
+    // Half-step t (t = 0 .. nsteps) ends with barrier t.  It issues activation
+    // stage t + 1 (its slot was last read before barrier t - 1), writes weight
+    // step t (t = nsteps: the adapter's right operand) to stage t & 1 from
+    // register set t & 1, reloads that set for step t + 2, and before the
+    // barrier waits for activation stage t, issued in the previous half-step:
+    // the loads issued after it are that half-step's reload (3), stage t + 1
+    // (8) and this half-step's reload (3).  Every half-step issues the same
+    // loads (code loads past the end re-read the last step, activation loads
+    // past the end read zero), and the prologue issues code set 0, stage 0 and
+    // code set 1 in that order, so the loop is entered with the loads in the
+    // order of its back edge and the compiler's own waits for the code sets
+    // stay exact.
+    uint32_t adapter[32];
     load_adapter_right<EPI_NK>(a, n0, tid, adapter);
+    __builtin_amdgcn_sched_barrier(0);
     P.issue(s0, 0);
     __builtin_amdgcn_sched_barrier(0);
+    issue_x(0);
+    __builtin_amdgcn_sched_barrier(0);
     P.issue(s1, __builtin_amdgcn_readfirstlane(min(1, last)));
-    for (int s = 0; s < nsteps; s += 2) {
-      P.store(s0, ws0, pair, cb.v, lane);
-      P.issue(s0, min(s + 2, last));
+    __builtin_amdgcn_sched_barrier(0);
+    auto half = [&](int t, typename Producer<KN, DQ>::Set &set, uint16_t *wdst) {
+      issue_x(t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t < nsteps) P.store(set, wdst, pair, cb.v, lane);
+      else store_adapter_right(adapter, wdst, tid);
+      P.issue(set, min(t + 2, last));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(14));
       lds_barrier();
-      if (s + 1 < nsteps) P.store(s1, ws1, pair, cb.v, lane);
-      else store_adapter_right(adapter, ws1, tid);   // step nsteps (odd) goes to stage 1
-      P.issue(s1, min(s + 3, last));
-      lds_barrier();
+    };
+    for (int t = 0; t <= nsteps; t += 2) {
+      half(t, s0, ws0);
+      if (t + 1 > nsteps) break;
+      half(t + 1, s1, ws1);
     }
-    if ((nsteps & 1) == 0) {
-      store_adapter_right(adapter, ws0, tid);        // step nsteps (even) goes to stage 0
-      lds_barrier();
-    }
+    // Nothing may land in LDS after the MMA waves start staging the output.
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     lds_barrier();   // the MMA waves' barrier after the adapter step
     return;
   }
@@ -440,56 +505,8 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Activation rows of this wave go global -> LDS with direct-to-LDS loads,
-  // three stages of 64 rows x 64 contraction indices (8 KB), two steps ahead;
-  // only this wave reads them.  Chunk k (16 bytes) of stage row r sits at slot
-  // k ^ ((r >> 1) & 7), so the fragment reads of 16 consecutive rows hit 16
-  // distinct bank groups.  Load instruction g fills rows 8g..8g+7 (1 KB in lane
-  // order): lane l writes slot l & 7 of row 8g + l / 8, i.e. every 8 lanes read
-  // one 128-byte line.
-  const int64_t wrow0 = m0 + (int64_t)wave_u * WM;
-  const u32x4 xdesc = raw_desc(a.L + wrow0 * a.ldl, (a.M - wrow0) * a.ldl * 2);
-  // Load g covers rows 8g + lane/8; the chunk swizzle (row >> 1) & 7 equals
-  // (lane >> 4) ^ 4 (g & 1), so the eight per-lane offsets are two bases (even
-  // and odd g) plus 8g rows.  They are formed at issue time from the bases
-  // (kept opaque to the compiler, which would otherwise hold all eight in
-  // registers through the loop).
-  const uint32_t xbase0 = (uint32_t)((lane >> 3) * a.ldl * 2 + (((lane & 7) ^ (lane >> 4)) * 16));
-  const uint32_t xbase1 = xbase0 ^ 64u;   // chunk index ^ 4
-  const uint32_t xrow8 = (uint32_t)(8 * a.ldl * 2);
-  // Step `steps` (the adapter step) takes its left operand, columns 0..63 of
-  // L2, through the same stages; columns at or beyond ldl2 read as zero.
-  const u32x4 l2desc = raw_desc(a.L2 + wrow0 * a.ldl2, (a.M - wrow0) * a.ldl2 * 2);
-  auto issue_x = [&](int64_t s, uint16_t *stage) {
-    const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(stage + wave_u * XW));
-    if (s < steps) {
-      const int soff = __builtin_amdgcn_readfirstlane((int)(s * BK * 2));
-      uint32_t b0 = xbase0, b1 = xbase1;
-      asm volatile("" : "+v"(b0), "+v"(b1));
-#pragma unroll
-      for (int g = 0; g < 8; ++g) dma_lds16(xdesc, dst + g * 1024, ((g & 1) ? b1 : b0) + (uint32_t)g * xrow8, soff);
-    } else {
-      // The lane index passes through an empty asm so that these eight offsets
-      // are computed here, once, instead of being hoisted out of the loop and
-      // held in registers through every step.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const int row = 8 * g + (ln >> 3), col = 8 * ((ln & 7) ^ ((row >> 1) & 7));
-        const uint32_t off = col < a.ldl2 ? (uint32_t)((row * a.ldl2 + col) * 2) : kOutOfRange;
-        dma_lds16(l2desc, dst + g * 1024, off, 0);
-      }
-    }
-  };
-  // Wait until the activation stage of the next step has landed: the only
-  // vector memory operations of an MMA wave in the main loop are these loads,
-  // 8 per step, and at most the group issued after it may still be in flight.
-  auto wait_x = [&](bool later_group_in_flight) {
-    if (later_group_in_flight) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
-
+  // Activation stages are filled by the producer waves (see there); this
+  // wave only reads them, after the barrier that follows their loads.
   // Fragment offsets: A (activations) tile i, slice c: row 32i + lr, chunk 4lh + c;
   // B (weights) column 32j + lr, positions 32lh + 8c .. +7, stored at 32(lh ^ g) + 8(c ^ j),
   // g = bit 3 ^ bit 4 of lr.
@@ -524,14 +541,13 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
   // and 1 of step s + 1, so the next step takes (F1, F2, F0).
   auto step = [&](int64_t s, const uint16_t *xc, const uint16_t *wc, const uint16_t *xn, const uint16_t *wn,
                   uint16_t *x2, Frag &F0, Frag &F1, Frag &F2) {
-    if (s + 2 < total) issue_x(s + 2, x2);
+    (void)x2;
     read_f(F2, xc, wc, 2);
     __builtin_amdgcn_sched_barrier(0);
     mma(F0);
     read_f(F0, xc, wc, 3);
     __builtin_amdgcn_sched_barrier(0);
     mma(F1);
-    if (s + 1 < steps) wait_x(s + 2 < total);
     lds_barrier();
     if (s + 1 < steps) read_f(F1, xn, wn, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -541,9 +557,6 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     mma(F0);
   };
   Frag fa, fb, fc;
-  issue_x(0, xs0);   // steps >= 1; step 1 may be the adapter step
-  issue_x(1, xs1);
-  wait_x(true);
   lds_barrier();
   read_f(fa, xs0, ws0, 0);
   read_f(fb, xs0, ws0, 1);
@@ -573,7 +586,6 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     const int xi = (int)(steps % 3);
     const uint16_t *xa = xi == 0 ? xs0 : (xi == 1 ? xs1 : xs2);
     const uint16_t *wa = (steps & 1) ? ws1 : ws0;
-    wait_x(false);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       Frag f;
