@@ -70,12 +70,12 @@ KERNEL_SOURCE = {
 # copy in the same run.  Keyed by kernel; `sha256` is that of the kernel's source
 # file and qn_device.h when the counters were taken.
 TRAFFIC = {  # profiles/qlora_step_4096_hbm_traffic.md
-    "dequant": {"bytes": 42278069, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
-    "double_quant": {"bytes": 1372128, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
-    "gemv": {"bytes": 9237570, "sha256": "965c98b0480111aae938d1ca83002854798ba89c043e8789d3525341bef1dc55"},
-    "gemm_fwd": {"bytes": 86031408, "sha256": "fd5184e4f1a3da72b425b9c62892c16a91290e6636a11a41c0aa1dd080da009b"},
-    "gemm_dx": {"bytes": 87225254, "sha256": "fd5184e4f1a3da72b425b9c62892c16a91290e6636a11a41c0aa1dd080da009b"},
-    "quantize": {"bytes": 76629733, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
+    "dequant": {"bytes": 42277779, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
+    "double_quant": {"bytes": 1372103, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
+    "gemv": {"bytes": 9238727, "sha256": "15e1ddfec7528d9da0019ee53d2c72df303464a350f15dcbdd97744927f601d4"},
+    "gemm_fwd": {"bytes": 85957734, "sha256": "fe1ebf613a574152b13d6feddb4d12ef56597fbbb1a274443d21911f2a5c9e0f"},
+    "gemm_dx": {"bytes": 87151576, "sha256": "fe1ebf613a574152b13d6feddb4d12ef56597fbbb1a274443d21911f2a5c9e0f"},
+    "quantize": {"bytes": 76629694, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
 }
 
 
