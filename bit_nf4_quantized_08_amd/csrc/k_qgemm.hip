@@ -469,7 +469,17 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     __builtin_amdgcn_sched_barrier(0);
     P.issue(s0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    issue_x(0);
+    {
+      // Stage 0 is always a weight step (nsteps >= 1): the same eight loads as
+      // issue_x(0) without its selects, which the compiler would otherwise
+      // turn into branches with different load counts on each side (and then
+      // wait conservatively inside the loop).
+      const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(xs0 + pw * XW));
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void *)(size_t)(base + g * 1024), 16,
+                                                 ((g & 1) ? xbase1 : xbase0) + (uint32_t)g * xrow8, 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     P.issue(s1, __builtin_amdgcn_readfirstlane(min(1, last)));
     __builtin_amdgcn_sched_barrier(0);
@@ -483,11 +493,16 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
       __builtin_amdgcn_s_waitcnt(vmcnt_only(14));
       lds_barrier();
     };
-    for (int t = 0; t <= nsteps; t += 2) {
+    // Half-steps 0 .. nsteps in pairs, then the odd one out.  No exit from
+    // the middle of the loop body: the compiler would give that exit a block
+    // shared with the back edge, and its wait counts would then assume that
+    // path into the next pair as well.
+    int t = 0;
+    for (; t + 1 <= nsteps; t += 2) {
       half(t, s0, ws0);
-      if (t + 1 > nsteps) break;
       half(t + 1, s1, ws1);
     }
+    if (t <= nsteps) half(t, s0, ws0);
     // Nothing may land in LDS after the MMA waves start staging the output.
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     lds_barrier();   // the MMA waves' barrier after the adapter step
