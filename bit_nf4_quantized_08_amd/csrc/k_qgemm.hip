@@ -228,8 +228,12 @@ struct Producer {
     else return as_f32(t.q);
   }
 
+  // hook(i), i = 0..3, is called at four evenly spaced points of the work
+  // (the caller issues its own memory operations there; each call is fenced
+  // off from the scheduler so that it stays where it is).
+  template <typename Hook>
   __device__ __forceinline__ void store(const Set &t, uint16_t *Rs, const float2 *pair, const float *cv,
-                                        int lane) const {
+                                        int lane, Hook &&hook) const {
     const int copy = lane & (kPairCopies - 1);
     const float A = scale(t);
     if constexpr (!KN) {
@@ -260,6 +264,9 @@ struct Producer {
       uint32_t o[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        hook(i);
+        __builtin_amdgcn_sched_barrier(0);
         // Byte b of the word holds element 2b (low nibble) and 2b + 1 (high
         // nibble).  Interleave the word with itself shifted by a nibble so that
         // each byte's low nibble is one element, in element order.
@@ -271,6 +278,9 @@ struct Producer {
           o[4 * i + 2 * h + 0] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
           o[4 * i + 2 * h + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
         }
+        // Pin this chunk's results here (the compiler would otherwise sink
+        // the arithmetic to the stores below, past every hook).
+        asm volatile("" : "+v"(o[4 * i]), "+v"(o[4 * i + 1]), "+v"(o[4 * i + 2]), "+v"(o[4 * i + 3]));
       }
       uint16_t *row = Rs + wr_col * LD;
       const int sw = kswz(wr_col);
@@ -299,13 +309,17 @@ struct Producer {
       const uint32_t wv[4] = {w0, w1, w2, w3};
       float v[4][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        hook(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const float2 p = pair[((wv[i] >> (8 * m)) & 0xFF) * kPairCopies + copy];
           v[i][2 * m] = p.x * S[i];
           v[i][2 * m + 1] = p.y * S[i];
         }
+      }
       const int k = wr_k ^ kswz(wr_col);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
@@ -434,7 +448,8 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     const uint32_t l2base1 = (uint32_t)((lane >> 3) * a.ldl2 * 2 + (c0 ^ 4u) * 16);
     const bool l2ok0 = 8 * (int64_t)c0 < a.ldl2, l2ok1 = 8 * (int64_t)(c0 ^ 4u) < a.ldl2;
     const uint32_t l2row8 = (uint32_t)(8 * a.ldl2 * 2);
-    auto issue_x = [&](int t) {
+    // Loads 2q and 2q + 1 of activation stage t (q = 0..3).
+    auto issue_x = [&](int t, int q) {
       const int i = t % 3;
       const uint32_t base =
           (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr((i == 0 ? xs0 : (i == 1 ? xs1 : xs2)) + pw * XW));
@@ -442,7 +457,7 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
       const rsrc_t r = main_step ? xr : l2r;
       const int soff = main_step ? t * BK * 2 : 0;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
+      for (int g = 2 * q; g < 2 * q + 2; ++g) {
         const bool odd = g & 1;
         const uint32_t l2off =
             live && (odd ? l2ok1 : l2ok0) ? (odd ? l2base1 : l2base0) + (uint32_t)g * l2row8 : kOutOfRange;
@@ -483,29 +498,38 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     __builtin_amdgcn_sched_barrier(0);
     P.issue(s1, __builtin_amdgcn_readfirstlane(min(1, last)));
     __builtin_amdgcn_sched_barrier(0);
-    auto half = [&](int t, typename Producer<KN, DQ>::Set &set, uint16_t *wdst) {
-      issue_x(t + 1);
+    // The eight activation loads are spread over the dequantisation: issued
+    // back to back, the four producer waves' loads fill the CU's vector memory
+    // path for several hundred cycles, and each wave would sit at its next
+    // load instead of dequantising.
+    auto half = [&](int t, typename Producer<KN, DQ>::Set &set, uint16_t *wdst) {   // t < nsteps
+      P.store(set, wdst, pair, cb.v, lane, [&](int q) { issue_x(t + 1, q); });
       __builtin_amdgcn_sched_barrier(0);
-      if (t < nsteps) P.store(set, wdst, pair, cb.v, lane);
-      else store_adapter_right(adapter, wdst, tid);
       P.issue(set, min(t + 2, last));
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(vmcnt_only(14));
       lds_barrier();
     };
-    // Half-steps 0 .. nsteps in pairs, then the odd one out.  No exit from
-    // the middle of the loop body: the compiler would give that exit a block
-    // shared with the back edge, and its wait counts would then assume that
-    // path into the next pair as well.
+    // Weight half-steps in pairs, then the odd one out.  Neither an exit from
+    // the middle of the loop body nor a branch between two arms that both
+    // load: the compiler gives such control flow a path that skips the loads
+    // (or leaves the loop body early), and its wait counts then assume that
+    // path and wait for loads that are still a half-step early.
     int t = 0;
-    for (; t + 1 <= nsteps; t += 2) {
+    for (; t + 2 <= nsteps; t += 2) {
       half(t, s0, ws0);
       half(t + 1, s1, ws1);
     }
-    if (t <= nsteps) half(t, s0, ws0);
-    // Nothing may land in LDS after the MMA waves start staging the output.
+    if (t < nsteps) {
+      half(t, s0, ws0);
+      ++t;
+    }
+    // Half-step nsteps: the adapter's right operand; its left operand is
+    // activation stage nsteps, issued in the last weight half-step.
+    store_adapter_right(adapter, (t & 1) ? ws1 : ws0, tid);
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-    lds_barrier();   // the MMA waves' barrier after the adapter step
+    lds_barrier();
+    lds_barrier();   // the MMA waves' barrier after the adapter step: nothing is in flight
     return;
   }
 
