@@ -472,8 +472,8 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     // step t (t = nsteps: the adapter's right operand) to stage t & 1 from
     // register set t & 1, reloads that set for step t + 2, and before the
     // barrier waits for activation stage t, issued in the previous half-step:
-    // the loads issued after it are that half-step's reload (3), stage t + 1
-    // (8) and this half-step's reload (3).  Every half-step issues the same
+    // the loads issued after it are that half-step's reload (kReload), stage
+    // t + 1 (8) and this half-step's reload.  Every half-step issues the same
     // loads (code loads past the end re-read the last step, activation loads
     // past the end read zero), and the prologue issues code set 0, stage 0 and
     // code set 1 in that order, so the loop is entered with the loads in the
@@ -502,12 +502,15 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
     // back to back, the four producer waves' loads fill the CU's vector memory
     // path for several hundred cycles, and each wave would sit at its next
     // load instead of dequantising.
+    // A half-step's reload is the code set plus its block scale: the
+    // quantised scale and the group step, or one fp32 scale.
+    constexpr int kReload = DQ ? 3 : 2;
     auto half = [&](int t, typename Producer<KN, DQ>::Set &set, uint16_t *wdst) {   // t < nsteps
       P.store(set, wdst, pair, cb.v, lane, [&](int q) { issue_x(t + 1, q); });
       __builtin_amdgcn_sched_barrier(0);
       P.issue(set, min(t + 2, last));
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(14));
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload + 8 + kReload));
       lds_barrier();
     };
     // Weight half-steps in pairs, then the odd one out.  Neither an exit from
