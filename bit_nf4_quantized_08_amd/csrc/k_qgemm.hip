@@ -13,14 +13,15 @@
 // Tiling.  A workgroup computes a 256 x 128 output tile with 8 waves in two
 // roles.
 //   * Four MMA waves (one per SIMD), each owning 64 rows x 128 columns (2 x 4
-//     MFMA tiles of 32 x 32).  A wave moves its own activation rows from
-//     global memory into LDS with direct-to-LDS loads (three stages, two steps
-//     ahead, waited for with explicit vmcnt), reads the operand fragments from
-//     LDS two k-slices ahead of the MFMAs that use them, and issues the MFMAs.
-//   * Four producer waves load the weight codes and block scales two steps
-//     ahead into registers, dequantise them and write the next weight stage.
-//     Sharing each SIMD with an MMA wave, their VALU work overlaps the
-//     matrix-core work.
+//     MFMA tiles of 32 x 32).  A wave issues no global loads: it reads the
+//     operand fragments from LDS two k-slices ahead of the MFMAs that use
+//     them and issues the MFMAs.
+//   * Four producer waves, one per MMA wave, move that wave's activation rows
+//     into LDS with direct-to-LDS loads (three stages, one step ahead of the
+//     stage being read, waited for with explicit vmcnt before the barrier),
+//     load the weight codes and block scales two steps ahead into registers,
+//     dequantise them and write the next weight stage.  Sharing each SIMD with
+//     an MMA wave, their VALU work overlaps the matrix-core work.
 // The contraction runs in steps of 64 (one NF4 block along K), the weight
 // stage double-buffered in LDS, one barrier per step.  Within a step, lane
 // half h of an MMA wave covers contraction indices [32h, 32h+32); slice c of
@@ -80,24 +81,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n, kRsrcFlags);
 }
 
-// Direct-to-LDS 16-byte load (each lane's 16 bytes land at lds_base + 16 *
-// lane).  Issued from inline assembly so that the compiler neither waits for
-// it at every LDS access nor at barriers: the issuing wave is the only reader
-// of what it loads and orders its reads with explicit vmcnt waits.  `desc` is a
-// raw buffer descriptor built from wave-uniform values (scalar registers).
-__device__ __forceinline__ u32x4 raw_desc(const void *base, int64_t bytes) {
-  const uint64_t p = (uint64_t)base;
-  const int64_t cap = 0xFFFFFFF0LL;
-  const uint32_t n = (uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) & 0xFFFFu;
-  const uint32_t nr = (uint32_t)__builtin_amdgcn_readfirstlane((int)n);
-  return u32x4{lo, hi, nr, (uint32_t)kRsrcFlags};
-}
-__device__ __forceinline__ void dma_lds16(u32x4 desc, uint32_t lds_base, uint32_t voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds_base), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
-}
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }
@@ -361,9 +344,10 @@ __device__ __forceinline__ void store_adapter_right(const uint32_t (&h)[32], uin
 }
 
 // Workgroup barrier that orders the waves' own LDS reads and writes only:
-// global loads issued before it stay in flight, including the direct-to-LDS
-// activation loads of an MMA wave, which only that wave reads and which it
-// waits for itself (a compiler-generated LDS fence would wait for them here).
+// global loads issued before it stay in flight, including the producers'
+// direct-to-LDS activation loads for later stages, which they wait for with
+// explicit counts before the barrier that publishes each stage (a
+// compiler-generated LDS fence would wait for all of them here).
 // The LDS wait is the builtin, not asm, so that the compiler's own wait
 // tracking knows every LDS read issued before the barrier has completed;
 // otherwise it re-waits for them after the barrier, and since the counter is
