@@ -70,12 +70,12 @@ KERNEL_SOURCE = {
 # copy in the same run.  Keyed by kernel; `sha256` is that of the kernel's source
 # file and qn_device.h when the counters were taken.
 TRAFFIC = {  # profiles/qlora_step_4096_hbm_traffic.md
-    "dequant": {"bytes": 42277779, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
-    "double_quant": {"bytes": 1372103, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
-    "gemv": {"bytes": 9238727, "sha256": "15e1ddfec7528d9da0019ee53d2c72df303464a350f15dcbdd97744927f601d4"},
-    "gemm_fwd": {"bytes": 85957734, "sha256": "fe1ebf613a574152b13d6feddb4d12ef56597fbbb1a274443d21911f2a5c9e0f"},
-    "gemm_dx": {"bytes": 87151576, "sha256": "fe1ebf613a574152b13d6feddb4d12ef56597fbbb1a274443d21911f2a5c9e0f"},
-    "quantize": {"bytes": 76629694, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
+    "dequant": {"bytes": 42277971, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
+    "double_quant": {"bytes": 1372125, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
+    "gemv": {"bytes": 9238695, "sha256": "608064ae571d2fca48c9f1e620330b3eb0c13065ad6907a24059543686e0c284"},
+    "gemm_fwd": {"bytes": 85964666, "sha256": "a2a3370f8763a396d8a12159f88d6692a8a160dde4b3237fa6fc8f8e4ef0410b"},
+    "gemm_dx": {"bytes": 87147262, "sha256": "a2a3370f8763a396d8a12159f88d6692a8a160dde4b3237fa6fc8f8e4ef0410b"},
+    "quantize": {"bytes": 76629421, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
 }
 
 
