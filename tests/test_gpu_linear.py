@@ -149,20 +149,20 @@ def _sampled_rows(M, k, seed):
     return np.sort(np.random.default_rng(seed).choice(M, size=min(k, M), replace=False))
 
 
-def run_full_size_sampled(N, K, M, r, alpha, w_std=0.02, outliers=False, bwd=True, seed=0, rows=64):
+def run_full_size_sampled(N, K, M, r, alpha, w_std=0.02, outliers=False, bwd=True, seed=0, rows=64, dq=True):
     """Full-size GPU run; the oracle checks a seeded subset of output rows of Y and
     dX, and dA / dB in full (their reductions over M are cheap in fp64)."""
     c = Case(N, K, M, r, alpha, seed=seed, w_std=w_std, outliers=outliers)
     w, X, A, B, dY = c.device()
-    Wh = c.oracle_weight(True)
+    Wh = c.oracle_weight(dq)
     sel = _sampled_rows(M, rows, seed + 1)
-    Y, H = lib.qlora_linear_fwd(X, w, A, B, alpha, want_H=True)
+    Y, H = lib.qlora_linear_fwd(X, w, A, B, alpha, want_H=True, use_double_quant=dq)
     Yref, Href = oracle.forward(c.X[sel], Wh, c.A, c.B, alpha)
     _check("Y rows", host(Y)[sel], Yref)
     _check("H rows", host(H)[sel], Href)
     if not bwd:
         return
-    dX, dA, dB = lib.qlora_linear_bwd(dY, X, w, A, B, alpha)
+    dX, dA, dB = lib.qlora_linear_bwd(dY, X, w, A, B, alpha, use_double_quant=dq)
     _, dAr, dBr = oracle.backward(c.dY, c.X, None, c.A, c.B, alpha, want_dX=False)
     _check("dA", host(dA), dAr)
     _check("dB", host(dB), dBr)
@@ -184,6 +184,14 @@ def test_proj4096_prefill_sampled():
     say("4096x4096 M=2048 prefill fwd+bwd")
     p = synth.PROJ4096
     run_full_size_sampled(4096, 4096, 2048, p["r"], p["alpha"])
+
+
+def test_proj4096_prefill_fp32_scales_sampled():
+    """The same at full size with fp32 block scales (no double quantisation):
+    the kernels whose per-step reload is one load shorter."""
+    say("4096x4096 M=2048 prefill fwd+bwd, fp32 block scales")
+    p = synth.PROJ4096
+    run_full_size_sampled(4096, 4096, 2048, p["r"], p["alpha"], seed=11, dq=False)
 
 
 def test_qwen_layer_shapes_sampled():
