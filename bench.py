@@ -76,6 +76,8 @@ TRAFFIC = {  # profiles/qlora_step_4096_hbm_traffic.md
     "gemm_fwd": {"bytes": 85964666, "sha256": "a2a3370f8763a396d8a12159f88d6692a8a160dde4b3237fa6fc8f8e4ef0410b"},
     "gemm_dx": {"bytes": 87147262, "sha256": "a2a3370f8763a396d8a12159f88d6692a8a160dde4b3237fa6fc8f8e4ef0410b"},
     "quantize": {"bytes": 76629421, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
+    "lowrank": {"bytes": 27061116, "sha256": "0587280805dc337581ae803574baa2f2398fc9fae7da96d91f1c6910fbda4453"},
+    "gemm_db": {"bytes": 43088798, "sha256": "0587280805dc337581ae803574baa2f2398fc9fae7da96d91f1c6910fbda4453"},
 }
 
 
@@ -111,6 +113,15 @@ def sizes():
         fwd_gemm_kernel_flops=2 * M_PRE * N * K + 2 * M_PRE * R * N,
         bwd_flops=2 * M_PRE * N * K + 4 * M_PRE * N * R + 4 * M_PRE * R * K,
         dx_gemm_kernel_flops=2 * M_PRE * N * K + 2 * M_PRE * R * K,
+        # low-rank products: one launch in the forward (H = X A^T -> s H bf16), one
+        # in the backward (dH = s dY B -> dH and dH^T; H -> (s H)^T); operands read
+        # once, outputs written once.  The trace averages the two launches.
+        lowrank_fwd_bytes=2 * M_PRE * K + 2 * R * K + 2 * M_PRE * R,
+        lowrank_bwd_bytes=(2 * M_PRE * N + 2 * R * N + 4 * M_PRE * R) + (2 * M_PRE * K + 2 * R * K + 2 * M_PRE * R),
+        # column reductions dA = dH^T X and dB = (s H)^T dY in one launch: X, dY
+        # and the two transposed factors read once (its per-split partial sums are
+        # an implementation choice, not counted)
+        colred_bytes=2 * M_PRE * (K + N) + 4 * R * M_PRE,
     )
 
 
@@ -353,6 +364,8 @@ def main():
         "gemv": (s["gemv_all_bytes"], "hbm"),
         "gemm_fwd": (s["fwd_gemm_kernel_flops"], "mfma"),
         "gemm_dx": (s["dx_gemm_kernel_flops"], "mfma"),
+        "lowrank": ((s["lowrank_fwd_bytes"] + s["lowrank_bwd_bytes"]) // 2, "hbm"),
+        "gemm_db": (s["colred_bytes"], "hbm"),
     }
 
     def roof(kind):
