@@ -18,7 +18,7 @@ int check_weight(const qn_nf4_weight *W) {
   if (W->N <= 0 || W->K <= 0 || W->N > kMaxElems / W->K) return QN_ERR_SHAPE;
   if (W->absmax_q) {
     if (!W->scale2) return QN_ERR_NULL;
-    if (!aligned(W->scale2, 4)) return QN_ERR_ALIGN;
+    if (!aligned(W->absmax_q, 4) || !aligned(W->scale2, 4)) return QN_ERR_ALIGN;
   } else {
     if (!W->absmax) return QN_ERR_NULL;
     if (!aligned(W->absmax, 4)) return QN_ERR_ALIGN;

@@ -19,6 +19,9 @@
 //   gemv_epilogue_kernel  adds the split partials and the adapter term.
 //   transpose_bf16_kernel B^T for the backward's dH = dY B.
 
+#include <map>
+#include <mutex>
+
 #include "qn_device.h"
 #include "qn_internal.h"
 
@@ -27,10 +30,26 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int BK = 64;        // contraction step: one NF4 block along K
-__device__ __forceinline__ float scale_of(const ScaleSrc &sc, int64_t b) {
-  if (sc.absmax_q) return (float)sc.absmax_q[b] * sc.scale2[b / QN_GROUP];
-  return sc.absmax[b];
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;          // raw buffer, 32-bit dwords
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // a per-lane offset that always reads zero
+constexpr int kNontemporal = 2;                 // cache policy of data read once
+
+// Buffer resource over [base, base + bytes): loads beyond `bytes` (by the
+// per-lane offset) return zero.  Built from the first lane's values so that it
+// stays in scalar registers even where the compiler takes the base for
+// divergent (it depends on the wave index).
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int64_t cap = 0xFFFFFFF0LL;
+  const uint64_t p = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)(uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n, kRsrcFlags);
 }
+
+__device__ __forceinline__ int64_t cdiv_d(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Transpose a small bf16 matrix: out[c][r] = in[r][c] for c < C, rows of out
 // beyond C (up to out_rows) zero.  in is [R, C] with leading dim ldi.
@@ -44,17 +63,28 @@ __global__ __launch_bounds__(kThreads) void transpose_bf16_kernel(const uint16_t
 }
 
 // ================================================================ GEMV (decode)
-// y_part[split][m][n] = sum over this split's K-range of x[m][k] * W_hat[n][k],
-// the block scale applied to each 32-weight partial sum.  Lane l of a wave owns
-// 32 consecutive k of every 2048-wide chunk (16 bytes of codes).  A wave works on
-// RPW rows at once so that each lane's x registers are reused RPW times.
+// y_part[split][m][n] = sum over the split's K-segment of x[m][k] * W_hat[n][k],
+// the block scale applied to each 32-weight partial sum.  A wave owns one
+// K-segment of KW 2048-wide chunks and holds its activations in registers for
+// the whole kernel; lane l owns 32 consecutive k of each chunk (16 bytes of
+// codes).  The wave then walks rows n = v, v + row_waves, ...: each row is
+// one contiguous read of KW KB of codes (rows of neighbouring waves are
+// neighbours in memory), and the next row is requested before the current one
+// is multiplied.
 // The first h_blocks blocks instead compute H partials,
 // h_part[split][m][j] = sum over the split's K-range of x[m][k] * A[j][k]:
 // block b takes K-range b % hsplits and adapter rows 4 (b / hsplits) .. +3,
 // one per wave, so that every wave makes a single pass and H is spread over
 // many short blocks that start first.
-constexpr int GEMV_RPW = 4;                       // rows per wave
-constexpr int GEMV_ROWS = GEMV_RPW * (kThreads / 64);  // rows per workgroup
+// 2048-wide chunks per wave segment (KW): the activations of a segment take
+// 16 * KW * MM registers per lane, at most 64 (128 for MM = 8, KW = 1), and a
+// segment is no longer than the row needs.
+int gemv_kw(int mm, int64_t chunks) {
+  const int cap = mm == 1 ? 4 : (mm == 2 ? 2 : 1);
+  int kw = 1;
+  while (kw < cap && kw < chunks) kw *= 2;
+  return kw;
+}
 
 struct GemvArgs {
   const uint16_t *X;  // [M, K]
@@ -65,27 +95,27 @@ struct GemvArgs {
   int64_t r;
   float *y_part;      // [splits][M][N]
   float *h_part;      // [hsplits][M][64]
-  int64_t k_per_split;   // multiple of 2048 (or K)
-  int splits;
+  int64_t k_per_split;   // KW * 2048: the K-segment of one wave
+  int splits;            // K-segments
+  int64_t row_waves;     // waves per K-segment; wave v takes rows v, v + row_waves, ...
   int h_blocks;       // hsplits * ceil(r / 4)
   int hsplits;
   int64_t hk_per_split;  // H partial K-range per block (multiple of 2048 or K)
 };
 
+// 32 activations of each row m at column k (k must be in range).  Rows m >= M
+// read row M - 1 instead, so that every load is unconditional; their results
+// are never stored.
 template <int MM>
-__device__ __forceinline__ void load_x_chunk(const GemvArgs &a, int64_t k, bool valid, uint32_t (&x)[MM][16]) {
+__device__ __forceinline__ void load_x_chunk(const GemvArgs &a, int64_t k, uint32_t (&x)[MM][16]) {
 #pragma unroll
   for (int m = 0; m < MM; ++m) {
-    if (valid && m < a.M) {
-      const u32x4 *p = reinterpret_cast<const u32x4 *>(a.X + m * a.K + k);
+    const int64_t mr = min((int64_t)m, a.M - 1);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(a.X + mr * a.K + k);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 v = p[c];
-        x[m][4 * c] = v.x; x[m][4 * c + 1] = v.y; x[m][4 * c + 2] = v.z; x[m][4 * c + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) x[m][c] = 0;
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 v = p[c];
+      x[m][4 * c] = v.x; x[m][4 * c + 1] = v.y; x[m][4 * c + 2] = v.z; x[m][4 * c + 3] = v.w;
     }
   }
 }
@@ -96,7 +126,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int MM>
+template <int MM, bool DQ, int KW>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
   __shared__ uint32_t pairs[256];  // byte -> bf16(row lo) | bf16(row hi) << 16
   {
@@ -118,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
       for (int m = 0; m < MM; ++m) hm[m] = 0.0f;
       for (int64_t k = kb + lane * 32; k < ke; k += 2048) {
         uint32_t x[MM][16];
-        load_x_chunk<MM>(a, k, true, x);
+        load_x_chunk<MM>(a, k, x);
         const u32x4 *pa = reinterpret_cast<const u32x4 *>(a.A + j * a.K + k);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -141,32 +171,85 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
     return;
   }
 
-  const int gb = (int)blockIdx.x - a.h_blocks;
-  const int rb = gb / a.splits;
-  const int split = gb % a.splits;
-  const int64_t n_base = (int64_t)rb * GEMV_ROWS + wave * GEMV_RPW;
+  static_assert(KW * MM <= 4 || KW == 1, "activation registers");
+  const int64_t v = (int64_t)((int)blockIdx.x - a.h_blocks) * (kThreads / 64) + wave;
+  const int split = (int)(v % a.splits);
+  const int64_t n_first = v / a.splits;
+  if (n_first >= a.row_waves) return;
   const int64_t kb = (int64_t)split * a.k_per_split;
   const int64_t ke = min(a.K, kb + a.k_per_split);
+  const int64_t bpr = a.K / QN_BLOCK;  // blocks per row
+  static_assert(QN_BLOCK == 64 && QN_GROUP == 256, "shifts below");
 
-  float acc[GEMV_RPW][MM];
+  // Activations of the segment, zero past its end (rows m >= M read row M - 1
+  // and are never stored).
+  uint32_t x[KW][MM][16];
 #pragma unroll
-  for (int i = 0; i < GEMV_RPW; ++i)
+  for (int c = 0; c < KW; ++c) {
+    const int64_t k = kb + c * 2048 + lane * 32;
+    const bool in = k < ke;
+    const int64_t ks = in ? k : kb;
 #pragma unroll
-    for (int m = 0; m < MM; ++m) acc[i][m] = 0.0f;
+    for (int m = 0; m < MM; ++m) {
+      const u32x4 *p = reinterpret_cast<const u32x4 *>(a.X + min((int64_t)m, a.M - 1) * a.K + ks);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 w = p[q];
+        x[c][m][4 * q] = in ? w.x : 0u; x[c][m][4 * q + 1] = in ? w.y : 0u;
+        x[c][m][4 * q + 2] = in ? w.z : 0u; x[c][m][4 * q + 3] = in ? w.w : 0u;
+      }
+    }
+  }
+  const rsrc_t rs2 = make_rsrc(a.sc.scale2, DQ ? cdiv_d(a.N * bpr, QN_GROUP) * 4 : 0);
 
-  for (int64_t kc = kb; kc < ke; kc += 2048) {
-    const int64_t k = kc + lane * 32;
-    const bool kvalid = k < ke;
-    uint32_t x[MM][16];
-    load_x_chunk<MM>(a, k, kvalid, x);
+  // One row's codes and raw block scales: the aligned dword holding each 8-bit
+  // scale code plus its group step, or the fp32 scale's bits.  Buffer
+  // resources over the row alone; a row n >= N gets empty ones, so that its
+  // loads (the prefetch after the last row) read zeros without touching
+  // memory, and so do lanes past the segment.
+  struct Row {
+    u32x4 cw[KW];
+    uint32_t sa[KW];
+    float sb[KW];
+  };
+  auto load_row = [&](Row &R, int64_t n) {
+    const bool nin = n < a.N;
+    const int64_t nn = nin ? n : 0;
+    const int64_t b0 = nn * bpr;  // first block of the row
+    const rsrc_t rc = make_rsrc(a.codes + nn * (a.K / 2), nin ? a.K / 2 : 0);
+    const rsrc_t rs = DQ ? make_rsrc(a.sc.absmax_q + (b0 & ~3LL), nin ? ((b0 & 3) + bpr + 3) & ~3LL : 0)
+                         : make_rsrc(a.sc.absmax + b0, nin ? bpr * 4 : 0);
 #pragma unroll
-    for (int i = 0; i < GEMV_RPW; ++i) {
-      const int64_t n = n_base + i;
-      if (!kvalid || n >= a.N) continue;
-      const int64_t e = n * a.K + k;
-      const u32x4 cw = ld_stream(a.codes + (e >> 1));
-      const float A = scale_of(a.sc, e >> 6);
-      const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+    for (int c = 0; c < KW; ++c) {
+      const int64_t k = kb + c * 2048 + lane * 32;
+      const bool in = k < ke;
+      R.cw[c] = __builtin_amdgcn_raw_buffer_load_b128(rc, in ? (uint32_t)(k >> 1) : kOutOfRange, 0, kNontemporal);
+      if constexpr (DQ) {
+        const uint32_t off = (uint32_t)(b0 & 3) + (uint32_t)(k >> 6);
+        R.sa[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, in ? off & ~3u : kOutOfRange, 0, 0);
+        R.sb[c] = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
+            rs2, in ? (uint32_t)((uint64_t)(b0 + (k >> 6)) >> 8) * 4 : kOutOfRange, 0, 0));
+      } else {
+        R.sa[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, in ? (uint32_t)(k >> 6) * 4 : kOutOfRange, 0, 0);
+        R.sb[c] = 1.0f;
+      }
+    }
+  };
+
+  // Multiply row n (its loads already issued into R) and store its sums.
+  // The scheduling fences keep one chunk's table lookups live at a time.
+  auto row_dot = [&](Row &R, int64_t n) {
+    float acc[MM];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) acc[m] = 0.0f;
+    const uint32_t b03 = (uint32_t)((n * bpr) & 3);
+#pragma unroll
+    for (int c = 0; c < KW; ++c) {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" : "+v"(R.sa[c]), "+v"(R.sb[c]));  // the scale is formed here, not earlier
+      const uint32_t w[4] = {R.cw[c].x, R.cw[c].y, R.cw[c].z, R.cw[c].w};
+      const uint32_t sh = 8 * ((b03 + (uint32_t)((kb + c * 2048 + lane * 32) >> 6)) & 3u);
+      const float A = DQ ? (float)((R.sa[c] >> sh) & 0xFFu) * R.sb[c] : as_f32(R.sa[c]);
       float p[MM];
 #pragma unroll
       for (int m = 0; m < MM; ++m) p[m] = 0.0f;
@@ -178,48 +261,113 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
 #pragma unroll
           for (int m = 0; m < MM; ++m)
             p[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr),
-                                                   __builtin_bit_cast(bf16x2, x[m][4 * q + b]), p[m], false);
+                                                   __builtin_bit_cast(bf16x2, x[c][m][4 * q + b]), p[m], false);
         }
 #pragma unroll
-      for (int m = 0; m < MM; ++m) acc[i][m] = __builtin_fmaf(A, p[m], acc[i][m]);
+      for (int m = 0; m < MM; ++m) {
+        acc[m] = __builtin_fmaf(A, p[m], acc[m]);
+        asm volatile("" : "+v"(acc[m]));
+      }
     }
-  }
-#pragma unroll
-  for (int i = 0; i < GEMV_RPW; ++i) {
-    const int64_t n = n_base + i;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
-      const float t = wave_sum(acc[i][m]);
-      if (lane == 0 && n < a.N && m < a.M) a.y_part[((int64_t)split * a.M + m) * a.N + n] = t;
+      const float t = wave_sum(acc[m]);
+      if (lane == 0 && m < a.M) a.y_part[((int64_t)split * a.M + m) * a.N + n] = t;
     }
+  };
+
+  // Rows in pairs with two register sets (no copies between them, so that
+  // a set's loads stay in flight while the other set is multiplied), then
+  // the odd row out.  (Two rows ahead costs occupancy and was slower.)
+  const int64_t rows = cdiv_d(a.N - n_first, a.row_waves);
+  Row r0, r1;
+  load_row(r0, n_first);
+  int64_t n = n_first;
+  for (int64_t t = 0; t + 2 <= rows; t += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_row(r1, n + a.row_waves);
+    row_dot(r0, n);
+    n += a.row_waves;
+    __builtin_amdgcn_sched_barrier(0);
+    load_row(r0, n + a.row_waves);
+    row_dot(r1, n);
+    n += a.row_waves;
   }
+  if (rows & 1) row_dot(r0, n);
 }
 
 // y[m][n] = sum_s y_part[s][m][n] + s_lora * sum_j H[m][j] * B[n][j], H summed
 // from its partials; rounded to bf16.  Optionally writes H (fp32, unscaled).
+// A workgroup covers EPI_ROWS rows n.  For the adapter term eight lanes share
+// a row of B, each reading 8 consecutive entries (one 16-byte load when r is a
+// multiple of 8), so that a wave reads 8 whole rows of B per instruction; the
+// eight partial sums are added with lane shuffles.
+constexpr int EPI_ROWS = kThreads / 8;
+
 __global__ __launch_bounds__(kThreads) void gemv_epilogue_kernel(const float *__restrict__ y_part, int splits,
                                                                  const float *__restrict__ h_part, int hsplits,
                                                                  int64_t M, int64_t N, int64_t r,
                                                                  const uint16_t *__restrict__ B, float s_lora,
                                                                  uint16_t *__restrict__ Y, float *H_out) {
-  __shared__ float Hs[8 * 64];
+  __shared__ float Hs[8 * 64];          // H[m][j], zero for j >= r
+  __shared__ float Ls[8 * EPI_ROWS];    // sum_j H[m][j] B[n][j] for the workgroup's rows
+  const int64_t n0 = (int64_t)blockIdx.x * EPI_ROWS;
+  // The split sums of this thread's outputs first, so that their loads
+  // overlap those of H and B.
+  float ysum[(8 * EPI_ROWS + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int u = 0; u < (8 * EPI_ROWS + kThreads - 1) / kThreads; ++u) {
+    const int idx = threadIdx.x + u * kThreads;
+    ysum[u] = 0.0f;
+    if (idx < M * EPI_ROWS) {
+      const int64_t m = idx / EPI_ROWS, i = idx % EPI_ROWS;
+      for (int s = 0; s < splits; ++s) ysum[u] += y_part[((int64_t)s * M + m) * N + n0 + i];
+    }
+  }
   for (int idx = threadIdx.x; idx < M * 64; idx += kThreads) {
     const int m = idx / 64, j = idx % 64;
     float v = 0.0f;
-    if (j < r)
+    if (j < r) {
+#pragma unroll 8
       for (int s = 0; s < hsplits; ++s) v += h_part[((int64_t)s * M + m) * 64 + j];
+    }
     Hs[idx] = v;
     if (H_out && blockIdx.x == 0 && j < r) H_out[m * r + j] = v;
   }
+  const int t = threadIdx.x, row = t >> 3, j0 = 8 * (t & 7);
+  const int64_t n = n0 + row;  // N % EPI_ROWS == 0
+  float b[8];
+  if (r % 8 == 0) {
+    const u32x4 v = j0 < r ? *reinterpret_cast<const u32x4 *>(B + n * r + j0) : u32x4{0, 0, 0, 0};
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { b[2 * q] = bf16_lo(w[q]); b[2 * q + 1] = bf16_hi(w[q]); }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) b[q] = j0 + q < r ? bf16_to_f32(B[n * r + j0 + q]) : 0.0f;
+  }
   __syncthreads();
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= M * N) return;
-  const int64_t m = idx / N, n = idx % N;
-  float y = 0.0f;
-  for (int s = 0; s < splits; ++s) y += y_part[((int64_t)s * M + m) * N + n];
-  float l = 0.0f;
-  for (int j = 0; j < r; ++j) l = __builtin_fmaf(Hs[m * 64 + j], bf16_to_f32(B[n * r + j]), l);
-  Y[m * N + n] = f32_to_bf16(__builtin_fmaf(s_lora, l, y));
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    if (m >= M) break;
+    float l = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) l = __builtin_fmaf(Hs[m * 64 + j0 + q], b[q], l);
+    l += __shfl_xor(l, 1, 64);
+    l += __shfl_xor(l, 2, 64);
+    l += __shfl_xor(l, 4, 64);
+    if (j0 == 0) Ls[m * EPI_ROWS + row] = l;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < (8 * EPI_ROWS + kThreads - 1) / kThreads; ++u) {
+    const int idx = t + u * kThreads;
+    if (idx < M * EPI_ROWS) {
+      const int64_t m = idx / EPI_ROWS, i = idx % EPI_ROWS;
+      Y[m * N + n0 + i] = f32_to_bf16(__builtin_fmaf(s_lora, Ls[idx], ysum[u]));
+    }
+  }
 }
 
 // ================================================================ host side
@@ -254,18 +402,67 @@ struct Carve {
 // Decode path sizing.
 constexpr int64_t GEMV_MAX_M = 8;
 
-void gemv_plan(int64_t M, int64_t N, int64_t K, int &splits, int64_t &kps, int &hsplits, int64_t &hkps) {
-  (void)M;
-  const int64_t row_blocks = cdiv(N, GEMV_ROWS);
+struct GemvPlan {
+  int splits;          // K-segments of gemv_kw(mm) chunks
+  int64_t kps;         // K per segment
+  int64_t row_waves;   // waves per segment
+  int row_wgs;         // workgroups for the rows
+  int hsplits;         // K-ranges of the H partials
+  int64_t hkps;
+};
+
+int gemv_mm(int64_t M) { return M == 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
+
+GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K) {
+  GemvPlan p;
   const int64_t chunks = cdiv(K, 2048);
-  const int64_t target = 4LL * num_cus();
-  int64_t sp = 1;
-  while (row_blocks * sp < target && sp * 2 <= chunks) sp *= 2;
-  splits = (int)sp;
-  kps = cdiv(chunks, sp) * 2048;
-  splits = (int)cdiv(K, kps);
-  hkps = 2048 * cdiv(chunks, std::min<int64_t>(chunks, 64));
-  hsplits = (int)cdiv(K, hkps);
+  const int64_t kw = gemv_kw(gemv_mm(M), chunks);
+  p.kps = kw * 2048;
+  p.splits = (int)cdiv(chunks, kw);
+  p.row_waves = 0;
+  p.row_wgs = 0;
+  p.hkps = 2048 * cdiv(chunks, std::min<int64_t>(chunks, 64));
+  p.hsplits = (int)cdiv(K, p.hkps);
+  return p;
+}
+
+// The decode kernel instance for M rows of activations and kw chunks per
+// segment.
+template <bool DQ>
+const void *gemv_fn(int64_t M, int64_t kw) {
+  switch (gemv_mm(M)) {
+    case 1:
+      return kw == 4 ? reinterpret_cast<const void *>(&gemv_kernel<1, DQ, 4>)
+           : kw == 2 ? reinterpret_cast<const void *>(&gemv_kernel<1, DQ, 2>)
+                     : reinterpret_cast<const void *>(&gemv_kernel<1, DQ, 1>);
+    case 2:
+      return kw == 2 ? reinterpret_cast<const void *>(&gemv_kernel<2, DQ, 2>)
+                     : reinterpret_cast<const void *>(&gemv_kernel<2, DQ, 1>);
+    case 4: return reinterpret_cast<const void *>(&gemv_kernel<4, DQ, 1>);
+    default: return reinterpret_cast<const void *>(&gemv_kernel<8, DQ, 1>);
+  }
+}
+
+// Workgroups of an instance that fit on one CU at once (cached per instance).
+int gemv_resident(const void *fn) {
+  static std::mutex mu;
+  static std::map<const void *, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(fn);
+  if (it != cache.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) != hipSuccess || nb < 1) nb = 1;
+  cache[fn] = nb;
+  return nb;
+}
+
+// Rows are dealt to as many waves as fit on the GPU at once (each wave then
+// walks its rows to the end with no second round of workgroups), but to no
+// more than half the rows, so that every wave has a next row to prefetch.
+void gemv_rows(GemvPlan &p, int64_t N, const void *fn) {
+  const int64_t waves = (int64_t)gemv_resident(fn) * num_cus() * (kThreads / 64);
+  p.row_waves = std::min<int64_t>(cdiv(N, 2), std::max<int64_t>(1, waves / p.splits));
+  p.row_wgs = (int)cdiv(p.row_waves * p.splits, kThreads / 64);
 }
 
 #define QN_TRY(x)                      \
@@ -280,11 +477,9 @@ void gemv_plan(int64_t M, int64_t N, int64_t K, int &splits, int64_t &kps, int &
 size_t fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
   Carve c(nullptr);
   if (M <= GEMV_MAX_M) {
-    int splits, hsplits;
-    int64_t kps, hkps;
-    gemv_plan(M, N, K, splits, kps, hsplits, hkps);
-    c.take<float>((int64_t)splits * M * N);
-    c.take<float>((int64_t)hsplits * M * 64);
+    const GemvPlan p = gemv_plan(M, N, K);
+    c.take<float>((int64_t)p.splits * M * N);
+    c.take<float>((int64_t)p.hsplits * M * 64);
   } else {
     c.take<uint16_t>(M * align_up(r, 8));
   }
@@ -294,25 +489,23 @@ size_t fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
 hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
   Carve c(a.ws);
   if (a.M <= GEMV_MAX_M) {
-    int splits, hsplits;
-    int64_t kps, hkps;
-    gemv_plan(a.M, a.N, a.K, splits, kps, hsplits, hkps);
-    float *y_part = c.take<float>((int64_t)splits * a.M * a.N);
-    float *h_part = c.take<float>((int64_t)hsplits * a.M * 64);
-    const int row_blocks = (int)cdiv(a.N, GEMV_ROWS);
-    const int h_blocks = hsplits * (int)cdiv(a.r, 4);
-    GemvArgs ga{a.X, a.M, a.N, a.K, a.codes, a.sc, a.A, a.r, y_part, h_part, kps, splits,
-                h_blocks, hsplits, hkps};
-    dim3 grid((unsigned)(h_blocks + row_blocks * splits));
+    GemvPlan p = gemv_plan(a.M, a.N, a.K);
+    const int64_t kw = p.kps / 2048;
+    const void *fn = a.sc.absmax_q ? gemv_fn<true>(a.M, kw) : gemv_fn<false>(a.M, kw);
+    gemv_rows(p, a.N, fn);
+    float *y_part = c.take<float>((int64_t)p.splits * a.M * a.N);
+    float *h_part = c.take<float>((int64_t)p.hsplits * a.M * 64);
+    const int h_blocks = p.hsplits * (int)cdiv(a.r, 4);
+    GemvArgs ga{a.X, a.M, a.N, a.K, a.codes, a.sc, a.A, a.r, y_part, h_part, p.kps, p.splits, p.row_waves,
+                h_blocks, p.hsplits, p.hkps};
+    dim3 grid((unsigned)(h_blocks + p.row_wgs));
     const Code16 cb = code16();
     TraceScope tr(QN_TRACE_GEMV, st);
-    if (a.M == 1) hipLaunchKernelGGL(gemv_kernel<1>, grid, dim3(kThreads), 0, st, ga, cb);
-    else if (a.M <= 2) hipLaunchKernelGGL(gemv_kernel<2>, grid, dim3(kThreads), 0, st, ga, cb);
-    else if (a.M <= 4) hipLaunchKernelGGL(gemv_kernel<4>, grid, dim3(kThreads), 0, st, ga, cb);
-    else hipLaunchKernelGGL(gemv_kernel<8>, grid, dim3(kThreads), 0, st, ga, cb);
+    void *args[] = {&ga, const_cast<Code16 *>(&cb)};
+    QN_TRY(hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, st));
     QN_TRY(hipGetLastError());
-    hipLaunchKernelGGL(gemv_epilogue_kernel, dim3((unsigned)cdiv(a.M * a.N, kThreads)), dim3(kThreads), 0, st,
-                       y_part, splits, h_part, hsplits, a.M, a.N, a.r, a.B, a.s, a.Y, a.H_out);
+    hipLaunchKernelGGL(gemv_epilogue_kernel, dim3((unsigned)(a.N / EPI_ROWS)), dim3(kThreads), 0, st,
+                       y_part, p.splits, h_part, p.hsplits, a.M, a.N, a.r, a.B, a.s, a.Y, a.H_out);
     return hipGetLastError();
   }
   // MFMA path: H = X A^T (low-rank kernel) -> sH bf16 -> tile GEMM with the

@@ -66,6 +66,7 @@ typedef enum { QN_F32 = 0, QN_BF16 = 1 } qn_dtype;
  *   scale2   fp32[ceil(nb/256)]: grid step of each group of 256 blocks; required
  *            when absmax_q is non-NULL.  The scale of block b is then
  *            fl32(absmax_q[b] * scale2[b/256]).
+ * codes 16-byte aligned; absmax, absmax_q and scale2 4-byte aligned.
  */
 typedef struct {
   const uint8_t *codes;

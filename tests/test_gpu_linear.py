@@ -86,12 +86,22 @@ def test_decode_path_small_M(M):
     run_fwd_bwd(Case(256, 512, M, 8, 16.0, seed=M), bwd=(M == 5))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 192, 3584), (2, 64, 2560), (3, 320, 6208), (1, 1024, 8192)])
+@pytest.mark.parametrize("M,N,K", [(1, 192, 3584), (2, 64, 2560), (3, 320, 6208), (1, 64, 6208), (1, 1024, 8192),
+                                   (1, 128, 20480)])
 def test_decode_path_ragged(M, N, K):
     """Contraction lengths that are not a multiple of the decode path's
-    2048-wide chunk (its out-of-range loads), and one that is."""
+    2048-wide chunk (its out-of-range loads) and that do not fill the last
+    K-segment, and ones that do (one and several segments)."""
     say(f"decode path ragged M={M} N={N} K={K}")
     run_fwd_bwd(Case(N, K, M, 16, 32.0, seed=N + K), bwd=False)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 192, 3584), (1, 256, 8192), (2, 128, 4096), (3, 320, 6208), (8, 128, 2048)])
+def test_decode_path_fp32_scales(M, N, K):
+    """The decode path reading fp32 block scales (no double quantisation),
+    with and without a ragged last chunk."""
+    say(f"decode path fp32 scales M={M} N={N} K={K}")
+    run_fwd_bwd(Case(N, K, M, 16, 32.0, seed=7 * N + K), bwd=False, dq=False)
 
 
 @pytest.mark.parametrize("M,r", [(1, 1), (2, 7), (1, 64), (8, 40)])

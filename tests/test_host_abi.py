@@ -83,6 +83,8 @@ def test_double_quant_and_dequant_reject_bad_arguments():
     assert L.nf4_dequant(ctypes.byref(w), vp(MISALIGNED), 0, vp(0)) == 4
     w = _w(codes=MISALIGNED)
     assert L.nf4_dequant(ctypes.byref(w), vp(FAKE), 0, vp(0)) == 4
+    w = _w(absmax=0, absmax_q=FAKE + 1, scale2=FAKE)   # 8-bit scales are read as aligned words
+    assert L.nf4_dequant(ctypes.byref(w), vp(FAKE), 0, vp(0)) == 4
 
 
 def test_workspace_size_rules():
