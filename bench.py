@@ -326,6 +326,40 @@ def main():
         stage_us[name] = e0.elapsed_time(e1) * 1e3 / (STAGE_REPLAYS * reps)
         del sg
     del wq_pool, nf_pool
+    # Decode on the 70B-shaped gate projection (28672 x 8192, r = 64), where the
+    # GEMV is bound by weight bandwidth rather than by launch latency: three
+    # distinct NF4 weights (3 x 121 MB, more than the Infinity Cache) in turn.
+    N70, K70, R70 = 28672, 8192, 64
+    g70 = torch.Generator(device=dev)
+    g70.manual_seed(70)
+    w70 = []
+    for _ in range(3):
+        src = (torch.randn((N70, K70), generator=g70, device=dev) * 0.015).to(torch.bfloat16)
+        w70.append(lib.quantize_weight(src))
+        del src
+    A70 = (torch.randn((R70, K70), generator=g70, device=dev) * 0.01).to(torch.bfloat16)
+    B70 = (torch.randn((N70, R70), generator=g70, device=dev) * 0.01).to(torch.bfloat16)
+    X70 = torch.randn((1, K70), generator=g70, device=dev).to(torch.bfloat16)
+    Y70 = torch.empty((1, N70), dtype=torch.bfloat16, device=dev)
+    ws70 = lib.workspace(lib.QN_OP_FWD, 1, N70, K70, R70, dev)
+    sg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(sg, stream=cap):
+        for i in range(6):
+            lib.qlora_linear_fwd(X70, w70[i % 3], A70, B70, 2.0 * R70, Y=Y70, ws=ws70)
+    for _ in range(2):
+        sg.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cap):
+        e0.record(cap)
+        for _ in range(STAGE_REPLAYS):
+            sg.replay()
+        e1.record(cap)
+    torch.cuda.synchronize()
+    dec70_us = e0.elapsed_time(e1) * 1e3 / (STAGE_REPLAYS * 6)
+    nb70 = N70 * K70 // 64
+    dec70_bytes = N70 * K70 // 2 + nb70 + 4 * ((nb70 + 255) // 256)
+    del sg, w70, A70, B70, X70, Y70, ws70
     # the quantise stages overwrote slot contents with the same values; restore order
     for i in range(SLOTS):
         quantize(i)
@@ -389,6 +423,8 @@ def main():
         "bwd_call_TFLOPs": round(s["bwd_flops"] / (stage_us["bwd"] * 1e-6) / 1e12, 1),
         "decode_call_weight_GBps": round(s["gemv_weight_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
         "decode_call_all_GBps": round(s["gemv_all_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
+        "decode_70b_gate_call_us": round(dec70_us, 2),
+        "decode_70b_gate_call_weight_GBps": round(dec70_bytes / (dec70_us * 1e-6) / 1e9, 1),
         "quantize_GBps": round(s["quantize_bytes"] / (stage_us["quantize"] * 1e-6) / 1e9, 1),
         "double_quant_GBps": round(s["dq_bytes"] / (stage_us["double_quant"] * 1e-6) / 1e9, 1),
         "dequant_GBps": round(s["dequant_bytes"] / (stage_us["dequant"] * 1e-6) / 1e9, 1),
@@ -416,6 +452,7 @@ def main():
         "metrics": {
             "prefill_dequant_gemm_TFLOPs": stages["prefill_fwd_gemm_kernel_TFLOPs"],
             "decode_gemv_weight_GBps": stages["decode_call_weight_GBps"],
+            "decode_gemv_weight_GBps_70b_gate": stages["decode_70b_gate_call_weight_GBps"],
             "quantize_GBps": stages["quantize_GBps"],
         },
         "roofline": roof(dominant),
