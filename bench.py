@@ -360,6 +360,48 @@ def main():
     nb70 = N70 * K70 // 64
     dec70_bytes = N70 * K70 // 2 + nb70 + 4 * ((nb70 + 255) // 256)
     del sg, w70, A70, B70, X70, Y70, ws70
+    # Bulk round trip: 7.62e9 weights streamed as 4096 x 4096 bf16 tiles
+    # (N(0, 0.02)) through NF4 quantisation, double quantisation and bf16
+    # dequantisation.  Sixteen distinct tiles (537 MB of source, more than the
+    # Infinity Cache) stand in for the stream; the sweep time is the per-tile
+    # time times the number of tiles.
+    SWEEP_WEIGHTS, TILE = 7.62e9, 4096 * 4096
+    g_sw = torch.Generator(device=dev)
+    g_sw.manual_seed(762)
+    tiles = [(torch.randn((4096, 4096), generator=g_sw, device=dev) * 0.02).to(torch.bfloat16) for _ in range(16)]
+    sw = [lib.quantize_weight(tiles[j]) for j in range(2)]
+    sw_out = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    sg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(sg, stream=cap):
+        for j in range(16):
+            w = sw[j % 2]
+            lib.nf4_quantize(tiles[j], codes=w.codes, absmax=w.absmax)
+            lib.nf4_double_quant(w.absmax, absmax_q=w.absmax_q, scale2=w.scale2)
+            lib.nf4_dequant(w, "bf16", out=sw_out)
+    for _ in range(2):
+        sg.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cap):
+        e0.record(cap)
+        for _ in range(STAGE_REPLAYS):
+            sg.replay()
+        e1.record(cap)
+    torch.cuda.synchronize()
+    tile_us = e0.elapsed_time(e1) * 1e3 / (STAGE_REPLAYS * 16)
+    nb_t = TILE // 64
+    # bytes per tile: quantise (bf16 in, codes + fp32 scales out), double quant
+    # (fp32 scales in, 8-bit scales + steps out), dequant (codes + 8-bit scales +
+    # steps in, bf16 out)
+    tile_bytes = (2 * TILE + TILE // 2 + 4 * nb_t) + (4 * nb_t + nb_t + 4 * (nb_t // 256)) + \
+                 (TILE // 2 + nb_t + 4 * (nb_t // 256) + 2 * TILE)
+    sweep = {
+        "tile_round_trip_us": round(tile_us, 2),
+        "round_trip_GBps": round(tile_bytes / (tile_us * 1e-6) / 1e9, 1),
+        "sweep_7.62e9_weights_ms": round(SWEEP_WEIGHTS / TILE * tile_us * 1e-3, 2),
+        "stored_bits_per_param": round((TILE // 2 + nb_t + 4 * (nb_t // 256)) * 8 / TILE, 6),
+    }
+    del sg, tiles, sw, sw_out
     # the quantise stages overwrote slot contents with the same values; restore order
     for i in range(SLOTS):
         quantize(i)
@@ -423,6 +465,7 @@ def main():
         "bwd_call_TFLOPs": round(s["bwd_flops"] / (stage_us["bwd"] * 1e-6) / 1e12, 1),
         "decode_call_weight_GBps": round(s["gemv_weight_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
         "decode_call_all_GBps": round(s["gemv_all_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
+        "bulk_round_trip_bf16_tiles": sweep,
         "decode_70b_gate_call_us": round(dec70_us, 2),
         "decode_70b_gate_call_weight_GBps": round(dec70_bytes / (dec70_us * 1e-6) / 1e9, 1),
         "quantize_GBps": round(s["quantize_bytes"] / (stage_us["quantize"] * 1e-6) / 1e9, 1),
