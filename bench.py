@@ -96,6 +96,71 @@ def traffic(kind):
     return t["bytes"]
 
 
+# Linear projections (N, K) of one transformer layer of each model shape.
+QWEN_LINEARS = {"q": (3584, 3584), "k": (512, 3584), "v": (512, 3584), "o": (3584, 3584),
+                "gate": (18944, 3584), "up": (18944, 3584), "down": (3584, 18944)}
+L70B_LINEARS = {"q": (8192, 8192), "k": (1024, 8192), "v": (1024, 8192), "o": (8192, 8192),
+                "gate": (28672, 8192), "up": (28672, 8192), "down": (8192, 28672)}
+
+
+def layer_times(lib, dev, stream, linears, r, M, bwd):
+    """Forward (and backward) time of all linears of one layer at M tokens:
+    seeded N(0, 0.02) weights in NF4 with double quantisation, one graph of the
+    layer's calls, replayed; TFLOP/s over the layer's algorithmic FLOPs."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(4096 + r)
+    rnd = lambda shape, std: (torch.randn(shape, generator=g, device=dev) * std).to(torch.bfloat16)
+    items = []
+    for name, (N, K) in linears.items():
+        w = lib.quantize_weight(rnd((N, K), 0.02))
+        X, A, B = rnd((M, K), 1.0), rnd((r, K), 0.01), rnd((N, r), 0.01)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        it = dict(N=N, K=K, w=w, X=X, A=A, B=B, Y=Y, wsf=lib.workspace(lib.QN_OP_FWD, M, N, K, r, dev))
+        if bwd:
+            it.update(dY=rnd((M, N), 1.0), dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                      dA=torch.empty((r, K), dtype=torch.bfloat16, device=dev),
+                      dB=torch.empty((N, r), dtype=torch.bfloat16, device=dev),
+                      wsb=lib.workspace(lib.QN_OP_BWD, M, N, K, r, dev))
+        items.append(it)
+    alpha = 2.0 * r
+
+    def run(kind):
+        for it in items:
+            if kind == "fwd":
+                lib.qlora_linear_fwd(it["X"], it["w"], it["A"], it["B"], alpha, Y=it["Y"], ws=it["wsf"])
+            else:
+                lib.qlora_linear_bwd(it["dY"], it["X"], it["w"], it["A"], it["B"], alpha,
+                                     out=(it["dX"], it["dA"], it["dB"]), ws=it["wsb"])
+
+    out = {}
+    for kind in (("fwd", "bwd") if bwd else ("fwd",)):
+        run(kind)
+        torch.cuda.synchronize()
+        sg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sg, stream=stream):
+            run(kind)
+        sg.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(3):
+                sg.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 3
+        if kind == "fwd":
+            flops = sum(2 * M * it["N"] * it["K"] + 2 * M * r * (it["K"] + it["N"]) for it in items)
+        else:
+            flops = sum(2 * M * it["N"] * it["K"] + 4 * M * r * (it["K"] + it["N"]) for it in items)
+        out[kind + "_us"] = round(us, 1)
+        out[kind + "_TFLOPs"] = round(flops / (us * 1e-6) / 1e12, 1)
+        del sg
+    del items
+    return out
+
+
 def sizes():
     n = N * K
     nb = n // 64
@@ -402,6 +467,8 @@ def main():
         "stored_bits_per_param": round((TILE // 2 + nb_t + 4 * (nb_t // 256)) * 8 / TILE, 6),
     }
     del sg, tiles, sw, sw_out
+    layers = {"qwen2.5_7b": layer_times(lib, dev, cap, QWEN_LINEARS, 16, 4096, bwd=True),
+              "70b": layer_times(lib, dev, cap, L70B_LINEARS, 64, 4096, bwd=False)}
     # the quantise stages overwrote slot contents with the same values; restore order
     for i in range(SLOTS):
         quantize(i)
@@ -466,6 +533,7 @@ def main():
         "decode_call_weight_GBps": round(s["gemv_weight_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
         "decode_call_all_GBps": round(s["gemv_all_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
         "bulk_round_trip_bf16_tiles": sweep,
+        "layers_M4096": layers,
         "decode_70b_gate_call_us": round(dec70_us, 2),
         "decode_70b_gate_call_weight_GBps": round(dec70_bytes / (dec70_us * 1e-6) / 1e9, 1),
         "quantize_GBps": round(s["quantize_bytes"] / (stage_us["quantize"] * 1e-6) / 1e9, 1),
