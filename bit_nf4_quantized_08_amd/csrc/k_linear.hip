@@ -126,6 +126,28 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave sums of MM values at once (MM a power of two <= 8): each exchange step
+// halves the values a lane carries, so MM sums cost MM - 1 + 6 - log2(MM)
+// shuffles instead of 6 MM.  Returns, in every lane, the full sum of value
+// m = lane >> (6 - log2(MM)).
+template <int MM>
+__device__ __forceinline__ float wave_sum_multi(float (&v)[MM], int lane) {
+  int off = 32;
+#pragma unroll
+  for (int cnt = MM; cnt > 1; cnt >>= 1, off >>= 1) {
+    const bool upper = (lane & off) != 0;
+#pragma unroll
+    for (int i = 0; i < cnt / 2; ++i) {
+      const float keep = upper ? v[i + cnt / 2] : v[i];
+      const float send = upper ? v[i] : v[i + cnt / 2];
+      v[i] = keep + __shfl_xor(send, off, 64);
+    }
+  }
+  float t = v[0];
+  for (; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+  return t;
+}
+
 template <int MM, bool DQ, int KW>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
   __shared__ uint32_t pairs[256];  // byte -> bf16(row lo) | bf16(row hi) << 16
@@ -270,11 +292,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < MM; ++m) {
-      const float t = wave_sum(acc[m]);
-      if (lane == 0 && m < a.M) a.y_part[((int64_t)split * a.M + m) * a.N + n] = t;
-    }
+    constexpr int kLog2MM = MM == 1 ? 0 : (MM == 2 ? 1 : (MM == 4 ? 2 : 3));
+    const float t = wave_sum_multi<MM>(acc, lane);
+    const int m = lane >> (6 - kLog2MM);
+    if ((lane & ((64 >> kLog2MM) - 1)) == 0 && m < a.M) a.y_part[((int64_t)split * a.M + m) * a.N + n] = t;
   };
 
   // Rows in pairs with two register sets (no copies between them, so that
