@@ -1,51 +1,51 @@
 """Throughput of the NF4 / QLoRA-linear hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of the single
-4096x4096 projection workload (W ~ N(0, 0.02) in fp32, LoRA r = 16,
-alpha = 32):
+Headline workload: the 70B-shaped transformer layer (hidden 8192; q, o 8192x8192,
+k, v 1024x8192, gate, up 28672x8192, down 8192x28672), each weight
+N(0, 0.015^2) fp32 with 0.1 % of its entries (seeded Bernoulli positions) x10,
+quantised once to NF4 (blocks of 64) with double quantisation (groups of 256)
+before the timed region -- the method quantises while loading; LoRA r = 64,
+alpha = 128 on every linear.
 
-  quantise W (fp32 -> NF4 codes + fp32 absmax)      nf4_quantize
-  double-quantise the absmax                         nf4_double_quant
-  dequantise a weight to bf16                        nf4_dequant
-  decode forward, X: 1 x 4096                        qlora_linear_fwd (M = 1)
-  prefill forward, X: 2048 x 4096                    qlora_linear_fwd (M = 2048)
-  backward at M = 2048 (dX, dA, dB)                  qlora_linear_bwd
+One step = that configuration's pass over all seven linears:
 
-Inputs are synthetic, generated on the device before the timed region.  Four
-weight slots rotate: step i quantises slot i % 4 while the forward/backward
-read slot (i + 2) % 4, quantised two steps earlier, so weight reads come from
-HBM rather than from a cache that still holds what the quantiser just wrote.
+  decode forward, X: 1 x K per linear                qlora_linear_fwd (M = 1)
+  prefill forward, X: 4096 x K per linear            qlora_linear_fwd (M = 4096)
 
-The step is captured once per slot phase into a HIP graph (the library only
-enqueues kernels on the current stream, so capture records them), and the
-timed region replays the graphs: the ~15 launches of a step then run without
-host launch gaps.  `value` is the step's algorithmic contraction work
-(prefill forward + backward + decode GEMV, FLOPs counted as 2 per
-multiply-add, dequant work not counted) divided by the step time.
+The step is captured once into a HIP graph and the timed region replays it.
+`value` = the step's algorithmic contraction work (2 per multiply-add over
+X W^T, X A^T and H B^T; the expansion of the codes is not counted) divided by
+the step time: the dequant-GEMM TFLOP/s of the layer, whole-step.
 
-Each stage is then timed alone (`stages.stage_us_graph`): a graph of
-back-to-back calls of that stage, replayed between two HIP events; the
-bandwidth-bound stages cycle through more distinct buffers than the
-Infinity Cache holds.  The quantise and decode figures of `metrics` come from
-these loops (per call, so the decode figure includes its epilogue kernel).
+`metrics` (each timed alone, graph-replayed):
+  prefill_dequant_gemm_TFLOPs   the layer's M = 4096 forward alone
+  decode_gemv_weight_GBps       the layer's M = 1 forward alone (441 MB of NF4
+                                weights, more than the 256 MB Infinity Cache)
+  quantize_GBps                 nf4_quantize on 4096 x 4096 bf16 tiles of the
+                                bulk sweep (7.62e9 weights)
+`stages` holds the rest of the path, each on its own configuration: the
+single 4096x4096 projection (quantise from fp32, double quant, dequant, decode,
+prefill forward and backward), the Qwen2.5-7B-shaped layer at M = 4096 forward
+and backward per linear, the bulk quantise / double-quant / dequant round trip
+with its error and stored bits per weight, the tiny configuration's call times,
+and the 70B layer's dequantisation error with and without double quantisation.
 
-A second, eager pass over the same steps enables the library's kernel trace:
+A second, eager pass over the same step enables the library's kernel trace:
 HIP events recorded around each call's dominant kernel on its own launch
-stream.  Its per-kernel average durations give the per-stage figures in
-`stages` and the `roofline` object (for the kernel with the largest share of
-the step).  `cpu_baseline` times the CPU oracle on a bounded sample.
-
-`roofline.traffic` is the HBM bytes per launch of that kernel read from
-rocprofv3 FETCH_SIZE and WRITE_SIZE counters (table `TRAFFIC` below, each
-counter scaled by what it reads for a plain copy of known size, taken with
-`--copy-calibration`); it is null when no such measurement exists for the
-kernel source as it is now.
+stream.  The `roofline` object is the dominant kernel of the step (the forward
+dequant-GEMM): algorithmic FLOPs of its launches over their summed durations.
+`roofline.traffic` is the HBM bytes per launch from rocprofv3 FETCH_SIZE and
+WRITE_SIZE counters (table `TRAFFIC`, each counter scaled by what it reads for
+a plain copy of known size, taken with `--copy-calibration`); null when no such
+measurement exists for the kernel source as it is now.  `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload.
 """
 
 import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -55,9 +55,6 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-N, K, R, ALPHA = 4096, 4096, 16, 32.0
-M_DEC, M_PRE = 1, 2048
-SLOTS = 4
 STAGE_REPS, STAGE_REPLAYS = 8, 5
 CSRC = os.path.join(ROOT, "bit_nf4_quantized_08_amd", "csrc")
 KERNEL_SOURCE = {
@@ -67,18 +64,18 @@ KERNEL_SOURCE = {
 }
 # Measured HBM bytes per launch: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per
 # dispatch), each scaled by the ratio of known bytes to counted bytes for a 256 MiB
-# copy in the same run.  Keyed by kernel; `sha256` is that of the kernel's source
-# file and qn_device.h when the counters were taken.
-TRAFFIC = {  # profiles/qlora_step_4096_hbm_traffic.md
-    "dequant": {"bytes": 42277971, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
-    "double_quant": {"bytes": 1372125, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
-    "gemv": {"bytes": 9061826, "sha256": "3dd0a326c81211bd432891d82b61327f1b245ee240598c45690d9ef94acefed1"},
-    "gemm_fwd": {"bytes": 85964666, "sha256": "a2a3370f8763a396d8a12159f88d6692a8a160dde4b3237fa6fc8f8e4ef0410b"},
-    "gemm_dx": {"bytes": 87147262, "sha256": "a2a3370f8763a396d8a12159f88d6692a8a160dde4b3237fa6fc8f8e4ef0410b"},
-    "quantize": {"bytes": 76629421, "sha256": "64942f24ec708f7693c38b703cf180ff08c4ebac7e360d443a7c99e630a68bd8"},
-    "lowrank": {"bytes": 27061116, "sha256": "0587280805dc337581ae803574baa2f2398fc9fae7da96d91f1c6910fbda4453"},
-    "gemm_db": {"bytes": 43088798, "sha256": "0587280805dc337581ae803574baa2f2398fc9fae7da96d91f1c6910fbda4453"},
-}
+# copy in the same run.  Keyed by kernel and workload; `sha256` is that of the
+# kernel's source file and qn_device.h when the counters were taken.
+TRAFFIC = {}
+
+# The configurations (N, K) of the linear layers.
+L70B = {"q": (8192, 8192), "k": (1024, 8192), "v": (1024, 8192), "o": (8192, 8192),
+        "gate": (28672, 8192), "up": (28672, 8192), "down": (8192, 28672)}
+R70, ALPHA70, M70_PRE, M70_DEC, W70_STD = 64, 128.0, 4096, 1, 0.015
+QWEN = {"q": (3584, 3584), "k": (512, 3584), "v": (512, 3584), "o": (3584, 3584),
+        "gate": (18944, 3584), "up": (18944, 3584), "down": (3584, 18944)}
+RQ, ALPHAQ, MQ = 16, 32.0, 4096
+N2, K2, R2, ALPHA2, M2_DEC, M2_PRE = 4096, 4096, 16, 32.0, 1, 2048
 
 
 def source_sha(kind):
@@ -89,113 +86,136 @@ def source_sha(kind):
     return h.hexdigest()
 
 
-def traffic(kind):
-    t = TRAFFIC.get(kind)
+def traffic(key, kind):
+    t = TRAFFIC.get(key)
     if t is None or t["sha256"] != source_sha(kind):
         return None
     return t["bytes"]
 
 
-# Linear projections (N, K) of one transformer layer of each model shape.
-QWEN_LINEARS = {"q": (3584, 3584), "k": (512, 3584), "v": (512, 3584), "o": (3584, 3584),
-                "gate": (18944, 3584), "up": (18944, 3584), "down": (3584, 18944)}
-L70B_LINEARS = {"q": (8192, 8192), "k": (1024, 8192), "v": (1024, 8192), "o": (8192, 8192),
-                "gate": (28672, 8192), "up": (28672, 8192), "down": (8192, 28672)}
+def nf4_bytes(N, K):
+    """Stored bytes of one NF4 weight with double quantisation."""
+    nb = N * K // 64
+    return N * K // 2 + nb + 4 * ((nb + 255) // 256)
 
 
-def layer_times(lib, dev, stream, linears, r, M, bwd):
-    """Forward (and backward) time of all linears of one layer at M tokens:
-    seeded N(0, 0.02) weights in NF4 with double quantisation, one graph of the
-    layer's calls, replayed; TFLOP/s over the layer's algorithmic FLOPs."""
-    import torch
-    g = torch.Generator(device=dev)
-    g.manual_seed(4096 + r)
-    rnd = lambda shape, std: (torch.randn(shape, generator=g, device=dev) * std).to(torch.bfloat16)
-    items = []
-    for name, (N, K) in linears.items():
-        w = lib.quantize_weight(rnd((N, K), 0.02))
-        X, A, B = rnd((M, K), 1.0), rnd((r, K), 0.01), rnd((N, r), 0.01)
-        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        it = dict(N=N, K=K, w=w, X=X, A=A, B=B, Y=Y, wsf=lib.workspace(lib.QN_OP_FWD, M, N, K, r, dev))
-        if bwd:
-            it.update(dY=rnd((M, N), 1.0), dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
-                      dA=torch.empty((r, K), dtype=torch.bfloat16, device=dev),
-                      dB=torch.empty((N, r), dtype=torch.bfloat16, device=dev),
-                      wsb=lib.workspace(lib.QN_OP_BWD, M, N, K, r, dev))
-        items.append(it)
-    alpha = 2.0 * r
+def fwd_flops(M, N, K, r):
+    return 2 * M * N * K + 2 * M * K * r + 2 * M * r * N
 
-    def run(kind):
-        for it in items:
-            if kind == "fwd":
-                lib.qlora_linear_fwd(it["X"], it["w"], it["A"], it["B"], alpha, Y=it["Y"], ws=it["wsf"])
-            else:
-                lib.qlora_linear_bwd(it["dY"], it["X"], it["w"], it["A"], it["B"], alpha,
-                                     out=(it["dX"], it["dA"], it["dB"]), ws=it["wsb"])
 
-    out = {}
-    for kind in (("fwd", "bwd") if bwd else ("fwd",)):
-        run(kind)
+def bwd_flops(M, N, K, r):
+    return 2 * M * N * K + 4 * M * N * r + 4 * M * r * K
+
+
+def lscpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def graph_time_us(torch, stream, fn, replays=STAGE_REPLAYS, calls=1):
+    """Capture fn() into a graph on `stream`, replay twice untimed, then time
+    `replays` replays with HIP events on the same stream; microseconds per call."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (replays * calls)
+    del g
+    return us
+
+
+# ------------------------------------------------------------------ workloads
+class Layer:
+    """All linears of one layer on the device: NF4 weights with double
+    quantisation, activations, adapters, outputs and workspaces."""
+
+    def __init__(self, torch, lib, dev, linears, r, w_std, M_list, seed, outliers=False, bwd_M=None,
+                 quality=False):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        rnd = lambda shape, std: (torch.randn(shape, generator=g, device=dev) * std).to(torch.bfloat16)
+        self.r, self.alpha, self.items = r, 2.0 * r, []
+        sq_err = {"dq": 0.0, "fp32_scales": 0.0}
+        sq_ref = 0.0
+        for name, (N, K) in linears.items():
+            W = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * w_std
+            if outliers:
+                mask = torch.rand((N, K), generator=g, device=dev) < 0.001
+                W = torch.where(mask, W * 10.0, W)
+                del mask
+            w = lib.quantize_weight(W)
+            if quality:
+                for key, dq in (("dq", True), ("fp32_scales", False)):
+                    d = lib.nf4_dequant(w, "f32", use_double_quant=dq)
+                    sq_err[key] += float(((d.double() - W.double()) ** 2).sum())
+                    del d
+                sq_ref += float((W.double() ** 2).sum())
+            del W
+            it = dict(name=name, N=N, K=K, w=w, A=rnd((r, K), 0.01), B=rnd((N, r), 0.01), X={}, Y={}, ws={})
+            for M in M_list:
+                it["X"][M] = rnd((M, K), 1.0)
+                it["Y"][M] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                it["ws"][M] = lib.workspace(lib.QN_OP_FWD, M, N, K, r, dev)
+            if bwd_M is not None:
+                M = bwd_M
+                it.update(dY=rnd((M, N), 1.0), dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                          dA=torch.empty((r, K), dtype=torch.bfloat16, device=dev),
+                          dB=torch.empty((N, r), dtype=torch.bfloat16, device=dev),
+                          H=torch.empty((M, r), dtype=torch.float32, device=dev),
+                          wsb=lib.workspace(lib.QN_OP_BWD, M, N, K, r, dev))
+            self.items.append(it)
         torch.cuda.synchronize()
-        sg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(sg, stream=stream):
-            run(kind)
-        sg.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for _ in range(3):
-                sg.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / 3
-        if kind == "fwd":
-            flops = sum(2 * M * it["N"] * it["K"] + 2 * M * r * (it["K"] + it["N"]) for it in items)
-        else:
-            flops = sum(2 * M * it["N"] * it["K"] + 4 * M * r * (it["K"] + it["N"]) for it in items)
-        out[kind + "_us"] = round(us, 1)
-        out[kind + "_TFLOPs"] = round(flops / (us * 1e-6) / 1e12, 1)
-        del sg
-    del items
-    return out
+        self.quality = None
+        if quality:
+            self.quality = {k: (v / sq_ref) ** 0.5 for k, v in sq_err.items()}
+
+    def fwd(self, lib, M, items=None, want_H=False):
+        for it in (items or self.items):
+            lib.qlora_linear_fwd(it["X"][M], it["w"], it["A"], it["B"], self.alpha, Y=it["Y"][M], ws=it["ws"][M],
+                                 H=it["H"] if want_H else None)
+
+    def bwd(self, lib, M, items=None):
+        for it in (items or self.items):
+            lib.qlora_linear_bwd(it["dY"], it["X"][M], it["w"], it["A"], it["B"], self.alpha,
+                                 out=(it["dX"], it["dA"], it["dB"]), ws=it["wsb"], H=it["H"])
+
+    def flops(self, M, kind="fwd", items=None):
+        f = fwd_flops if kind == "fwd" else bwd_flops
+        return sum(f(M, it["N"], it["K"], self.r) for it in (items or self.items))
+
+    def weight_bytes(self):
+        return sum(nf4_bytes(it["N"], it["K"]) for it in self.items)
 
 
-def sizes():
-    n = N * K
-    nb = n // 64
-    ng = (nb + 255) // 256
-    w_bytes = n // 2 + nb + 4 * ng
-    return dict(
-        n=n, nb=nb, ng=ng,
-        quantize_bytes=4 * n + n // 2 + 4 * nb,
-        dq_bytes=4 * nb + nb + 4 * ng,
-        dequant_bytes=w_bytes + 2 * n,
-        gemv_weight_bytes=w_bytes,
-        gemv_all_bytes=w_bytes + 2 * K * M_DEC + 2 * N * M_DEC + 2 * R * K + 2 * N * R,
-        gemv_flops=2 * M_DEC * N * K + 2 * M_DEC * K * R + 2 * M_DEC * R * N,
-        fwd_flops=2 * M_PRE * N * K + 2 * M_PRE * K * R + 2 * M_PRE * R * N,
-        fwd_gemm_kernel_flops=2 * M_PRE * N * K + 2 * M_PRE * R * N,
-        bwd_flops=2 * M_PRE * N * K + 4 * M_PRE * N * R + 4 * M_PRE * R * K,
-        dx_gemm_kernel_flops=2 * M_PRE * N * K + 2 * M_PRE * R * K,
-        # low-rank products: one launch in the forward (H = X A^T -> s H bf16), one
-        # in the backward (dH = s dY B -> dH and dH^T; H -> (s H)^T); operands read
-        # once, outputs written once.  The trace averages the two launches.
-        lowrank_fwd_bytes=2 * M_PRE * K + 2 * R * K + 2 * M_PRE * R,
-        lowrank_bwd_bytes=(2 * M_PRE * N + 2 * R * N + 4 * M_PRE * R) + (2 * M_PRE * K + 2 * R * K + 2 * M_PRE * R),
-        # column reductions dA = dH^T X and dB = (s H)^T dY in one launch: X, dY
-        # and the two transposed factors read once (its per-split partial sums are
-        # an implementation choice, not counted)
-        colred_bytes=2 * M_PRE * (K + N) + 4 * R * M_PRE,
-    )
+# ------------------------------------------------------------------ CPU oracle
+def cpu_baseline():
+    """The CPU oracle, as it stands, on bounded samples of the same workloads.
 
-
-def cpu_baseline(min_seconds=12.0, max_steps=24):
-    """Time the CPU oracle on a bounded sample of the same workload: whole oracle
-    steps (quantise, double quant and bf16 dequant of one 4096x4096 fp32 weight,
-    then the step's fp64 contractions: decode M=1, prefill M=2048 forward and
-    backward) repeated until `min_seconds` have passed.  The value is the step's
-    contraction FLOPs over the oracle's step time, as for the GPU figure."""
+    `value` (the headline unit, TFLOP/s): one linear of the 70B-shaped layer
+    (q, 8192 x 8192) on 256 token rows -- the oracle's dequantisation of the NF4
+    weight to bf16 values (one core, numpy) plus its fp64 forward (all BLAS
+    threads); quantisation happens before the timer, as on the GPU.  Also reported
+    (not the headline): codec GB/s on the tiny configuration, the 4096 x 4096
+    weight and 8 bulk tiles; fp64 contraction GFLOP/s on the tiny configuration,
+    the 4096 x 4096 projection (forward M = 2048 and backward) and 256-row subsets
+    of the Qwen2.5-7B- and 70B-shaped layers' linears (contraction only: its cost
+    does not depend on the weight's values, so a Gaussian bf16 matrix stands in
+    for W_hat there)."""
     import numpy as np
     import oracle
     from bit_nf4_quantized_08_amd import synth
@@ -204,57 +224,101 @@ def cpu_baseline(min_seconds=12.0, max_steps=24):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
-    s = sizes()
-    X = synth.bf16_values(synth.to_bf16(synth.gaussian((M_PRE, K), 1.0, synth.SEED_X)))
-    A = synth.bf16_values(synth.to_bf16(synth.gaussian((R, K), 0.01, synth.SEED_A)))
-    B = synth.bf16_values(synth.to_bf16(synth.gaussian((N, R), 0.01, synth.SEED_B)))
-    dY = synth.bf16_values(synth.to_bf16(synth.gaussian((M_PRE, N), 1.0, synth.SEED_DY)))
-    t_codec = t_q = t_mm = 0.0
-    steps = 0
-    while steps < max_steps and (steps < 2 or t_codec + t_mm < min_seconds):
-        W = synth.gaussian((N, K), 0.02, synth.SEED_BULK0 + steps)
+    t_all = time.perf_counter()
+    bf = lambda shape, std, seed: synth.bf16_values(synth.to_bf16(synth.gaussian(shape, std, seed)))
+    out = {"kind": "oracle", "unit": "TFLOP/s", "cores": int(blas_threads), "host_cpus": os.cpu_count(),
+           "cpu_model": lscpu_model()}
+
+    def codec_rate(W):
+        n = W.size
         t0 = time.perf_counter()
-        packed, absmax, _ = oracle.quantize(W)
-        t1 = time.perf_counter()
-        k, step = oracle.double_quant(absmax)
-        Wh = oracle.dequant_bf16_weight(packed, N, K, oracle.dq_absmax(k, step))
-        t2 = time.perf_counter()
-        oracle.forward(X[:M_DEC], Wh, A, B, ALPHA)
-        oracle.forward(X, Wh, A, B, ALPHA)
-        oracle.backward(dY, X, Wh, A, B, ALPHA)
-        t3 = time.perf_counter()
-        t_q += t1 - t0
-        t_codec += t2 - t0
-        t_mm += t3 - t2
-        steps += 1
-    flops = s["gemv_flops"] + s["fwd_flops"] + s["bwd_flops"]
-    return {
-        "value": flops * steps / (t_codec + t_mm) / 1e12,
-        "unit": "TFLOP/s",
-        "cores": int(blas_threads),
-        "kind": "oracle",
-        "sample": (f"{steps} whole oracle steps of the same workload in {t_codec + t_mm:.1f} s: codec "
-                   f"(quantise, double quant, bf16 dequant of a fresh 4096x4096 fp32 weight) "
-                   f"{t_codec / steps:.2f} s/step on 1 core, fp64 contractions {t_mm / steps:.2f} s/step "
-                   f"on {blas_threads} BLAS threads"),
-        "ms_per_step": (t_codec + t_mm) * 1e3 / steps,
-        "quantize_GBps": steps * s["quantize_bytes"] / t_q / 1e9,
-        "host_cpus": os.cpu_count(),
-    }
+        p, a, _ = oracle.quantize(W)
+        k, st = oracle.double_quant(a)
+        oracle.dequant_bf16_weight(p, W.shape[0], W.shape[1], oracle.dq_absmax(k, st))
+        dt = time.perf_counter() - t0
+        in_b = 4 if W.dtype == np.float32 else 2
+        nb = (n + 63) // 64
+        byts = (in_b * n + n // 2 + 4 * nb) + (5 * nb + 4 * ((nb + 255) // 256)) + (n // 2 + nb + 2 * n)
+        return byts, dt
+
+    # headline sample: 70B q projection, 256 rows
+    N, K = L70B["q"]
+    Wq = synth.with_outliers(synth.gaussian((N, K), W70_STD, synth.SEED_W), 0.001, 10.0)
+    p, a, _ = oracle.quantize(Wq)
+    k, st = oracle.double_quant(a)
+    X = bf((256, K), 1.0, synth.SEED_X)
+    A, B = bf((R70, K), 0.01, synth.SEED_A), bf((N, R70), 0.01, synth.SEED_B)
+    t0 = time.perf_counter()
+    Wh = oracle.dequant_bf16_weight(p, N, K, oracle.dq_absmax(k, st))
+    t1 = time.perf_counter()
+    oracle.forward(X, Wh, A, B, ALPHA70)
+    t2 = time.perf_counter()
+    fl = fwd_flops(256, N, K, R70)
+    out["value"] = fl / (t2 - t0) / 1e12
+    out["sample"] = (f"70B-shaped q projection (8192x8192, NF4 + double quant, r=64) forward of 256 token rows: "
+                     f"oracle bf16 dequantisation {t1 - t0:.2f} s on 1 core + fp64 forward {t2 - t1:.2f} s on "
+                     f"{blas_threads} BLAS threads; value = that sample's contraction FLOPs / its time")
+    del Wq, p, a, k, st, Wh
+    # codec GB/s
+    codec = {}
+    tiny = synth.tiny_inputs()
+    b, dt = codec_rate(tiny["W"])
+    codec["tiny_256x512_fp32"] = round(b / dt / 1e9, 4)
+    b, dt = codec_rate(synth.gaussian((N2, K2), 0.02, synth.SEED_W))
+    codec["proj4096_fp32"] = round(b / dt / 1e9, 4)
+    tb, tt = 0, 0.0
+    for t in range(8):
+        W = bf((4096, 4096), 0.02, synth.SEED_BULK0 + t)   # bf16 values, widened exactly
+        b, dt = codec_rate(W)
+        tb += b - 2 * W.size    # bf16 source: 2 bytes in, not 4
+        tt += dt
+    codec["bulk_8_tiles_bf16"] = round(tb / tt / 1e9, 4)
+    out["codec_GBps_1core"] = codec
+    # fp64 contractions
+    con = {}
+
+    def con_rate(M, N, K, r, bwd=True, reps=1):
+        X, A, B = bf((M, K), 1.0, 2), bf((r, K), 0.01, 3), bf((N, r), 0.01, 4)
+        Wh = bf((N, K), 0.02, 1)
+        G = bf((M, N), 1.0, 5) if bwd else None
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.forward(X, Wh, A, B, 2.0 * r)
+            if bwd:
+                oracle.backward(G, X, Wh, A, B, 2.0 * r)
+        dt = time.perf_counter() - t0
+        return reps * (fwd_flops(M, N, K, r) + (bwd_flops(M, N, K, r) if bwd else 0)), dt
+
+    f, dt = con_rate(4, 256, 512, 8, reps=50)
+    con["tiny_fwd_bwd"] = round(f / dt / 1e9, 3)
+    f, dt = con_rate(M2_PRE, N2, K2, R2)
+    con["proj4096_M2048_fwd_bwd"] = round(f / dt / 1e9, 3)
+    for tag, lin, r, bwd in (("qwen7b_layer_256rows_fwd_bwd", QWEN, RQ, True), ("70b_layer_256rows_fwd", L70B, R70, False)):
+        tf, tt = 0, 0.0
+        for (n_, k_) in lin.values():
+            f, dt = con_rate(256, n_, k_, r, bwd=bwd)
+            tf += f
+            tt += dt
+        con[tag] = round(tf / tt / 1e9, 3)
+    out["contraction_GFLOPs_fp64"] = con
+    out["seconds"] = round(time.perf_counter() - t_all, 1)
+    return out
 
 
+# ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true", help="headline step only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the run, copy 256 MiB three times (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the path is single-GPU; the sharding design is described in the docs).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build runs the path on "
+              "a single GPU (how it would shard is described in the design notes).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -263,287 +327,98 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib.load()
-    g = torch.Generator(device=dev)
-    g.manual_seed(1234)
-
-    def randn(shape, std):
-        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
-
-    Ws = [torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02 for _ in range(SLOTS)]
-    Xd = randn((M_DEC, K), 1.0)
-    Xp = randn((M_PRE, K), 1.0)
-    A = randn((R, K), 0.01)
-    B = randn((N, R), 0.01)
-    dY = randn((M_PRE, N), 1.0)
-    n = N * K
-    slots = []
-    for i in range(SLOTS):
-        codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
-        absmax = torch.empty(n // 64, dtype=torch.float32, device=dev)
-        aq = torch.empty(n // 64, dtype=torch.uint8, device=dev)
-        s2 = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device=dev)
-        slots.append(lib.NF4Weight(codes, absmax, aq, s2, N, K))
-    deq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-    Yd = torch.empty((M_DEC, N), dtype=torch.bfloat16, device=dev)
-    Yp = torch.empty((M_PRE, N), dtype=torch.bfloat16, device=dev)
-    dX = torch.empty((M_PRE, K), dtype=torch.bfloat16, device=dev)
-    dA = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
-    dB = torch.empty((N, R), dtype=torch.bfloat16, device=dev)
-    ws_dec = lib.workspace(lib.QN_OP_FWD, M_DEC, N, K, R, dev)
-    ws_pre = lib.workspace(lib.QN_OP_FWD, M_PRE, N, K, R, dev)
-    ws_bwd = lib.workspace(lib.QN_OP_BWD, M_PRE, N, K, R, dev)
-
-    def quantize(i):
-        w = slots[i % SLOTS]
-        lib.nf4_quantize(Ws[i % SLOTS], codes=w.codes, absmax=w.absmax)
-        lib.nf4_double_quant(w.absmax, absmax_q=w.absmax_q, scale2=w.scale2)
-
-    def step(i, ev=None):
-        def mark(k):
-            if ev is not None:
-                ev[k].record()
-        mark(0)
-        quantize(i)
-        mark(1)
-        w = slots[(i + 2) % SLOTS]
-        lib.nf4_dequant(w, "bf16", out=deq)
-        mark(2)
-        lib.qlora_linear_fwd(Xd, w, A, B, ALPHA, Y=Yd, ws=ws_dec)
-        mark(3)
-        lib.qlora_linear_fwd(Xp, w, A, B, ALPHA, Y=Yp, ws=ws_pre)
-        mark(4)
-        lib.qlora_linear_bwd(dY, Xp, w, A, B, ALPHA, out=(dX, dA, dB), ws=ws_bwd)
-        mark(5)
-
-    for i in range(SLOTS):
-        quantize(i)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # One graph per slot phase (the step reads/writes slot-dependent buffers).
-    graphs = []
     cap = torch.cuda.Stream()
-    for ph in range(SLOTS):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            step(ph)
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % SLOTS].replay()
-    torch.cuda.synchronize()
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
 
-    # ---- timed region: graph replays
+    # ---------------- headline: the 70B-shaped layer
+    log("70B layer: quantising 7 weights")
+    L = Layer(torch, lib, dev, L70B, R70, W70_STD, [M70_DEC, M70_PRE], seed=70, outliers=True, quality=True)
+
+    def step():
+        L.fwd(lib, M70_DEC)
+        L.fwd(lib, M70_PRE)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % SLOTS].replay()
+    for _ in range(args.steps):
+        g.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    del g
     ms_step = (t1 - t0) * 1e3 / args.steps
+    step_flops = L.flops(M70_DEC) + L.flops(M70_PRE)
+    value = step_flops / (ms_step * 1e-3) / 1e12
 
-    # ---- each stage alone: a graph of STAGE_REPS back-to-back calls (rotating
-    # weight slots), replayed; HIP events around the replays on the capture stream
-    def stage_fns(i):
-        w = slots[(i + 2) % SLOTS]
-        return {
-            "quantize": lambda: lib.nf4_quantize(Ws[i % SLOTS], codes=slots[i % SLOTS].codes,
-                                                 absmax=slots[i % SLOTS].absmax),
-            "double_quant": lambda: lib.nf4_double_quant(slots[i % SLOTS].absmax, absmax_q=slots[i % SLOTS].absmax_q,
-                                                         scale2=slots[i % SLOTS].scale2),
-            "dequant": lambda: lib.nf4_dequant(w, "bf16", out=deq),
-            "fwd_decode": lambda: lib.qlora_linear_fwd(Xd, w, A, B, ALPHA, Y=Yd, ws=ws_dec),
-            "fwd_prefill": lambda: lib.qlora_linear_fwd(Xp, w, A, B, ALPHA, Y=Yp, ws=ws_pre),
-            "bwd": lambda: lib.qlora_linear_bwd(dY, Xp, w, A, B, ALPHA, out=(dX, dA, dB), ws=ws_bwd),
-        }
-    # Bandwidth-bound stages cycle through more distinct buffers than the 256 MB
-    # Infinity Cache holds: 8 fp32 weights (512 MiB) to quantise, 64 NF4 weights
-    # (553 MB) to dequantise or multiply at M = 1.
-    wq_pool = [Ws[j % SLOTS].clone() for j in range(8)]
-    nf_pool = [lib.NF4Weight(slots[j % SLOTS].codes.clone(), slots[j % SLOTS].absmax.clone(),
-                             slots[j % SLOTS].absmax_q.clone(), slots[j % SLOTS].scale2.clone(), N, K)
-               for j in range(64)]
-    pool_fns = {
-        "quantize": (8, lambda i: lib.nf4_quantize(wq_pool[i], codes=slots[i % SLOTS].codes,
-                                                   absmax=slots[i % SLOTS].absmax)),
-        "dequant": (64, lambda i: lib.nf4_dequant(nf_pool[i], "bf16", out=deq)),
-        "fwd_decode": (64, lambda i: lib.qlora_linear_fwd(Xd, nf_pool[i], A, B, ALPHA, Y=Yd, ws=ws_dec)),
-    }
-    stage_us = {}
-    for name in stage_fns(0):
-        reps, fn = pool_fns.get(name, (STAGE_REPS, None))
-        sg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(sg, stream=cap):
-            for i in range(reps):
-                if fn is None:
-                    stage_fns(i)[name]()
-                else:
-                    fn(i)
-        for _ in range(2):
-            sg.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(cap):
-            e0.record(cap)
-            for _ in range(STAGE_REPLAYS):
-                sg.replay()
-            e1.record(cap)
-        torch.cuda.synchronize()
-        stage_us[name] = e0.elapsed_time(e1) * 1e3 / (STAGE_REPLAYS * reps)
-        del sg
-    del wq_pool, nf_pool
-    # Decode on the 70B-shaped gate projection (28672 x 8192, r = 64), where the
-    # GEMV is bound by weight bandwidth rather than by launch latency: three
-    # distinct NF4 weights (3 x 121 MB, more than the Infinity Cache) in turn.
-    N70, K70, R70 = 28672, 8192, 64
-    g70 = torch.Generator(device=dev)
-    g70.manual_seed(70)
-    w70 = []
-    for _ in range(3):
-        src = (torch.randn((N70, K70), generator=g70, device=dev) * 0.015).to(torch.bfloat16)
-        w70.append(lib.quantize_weight(src))
-        del src
-    A70 = (torch.randn((R70, K70), generator=g70, device=dev) * 0.01).to(torch.bfloat16)
-    B70 = (torch.randn((N70, R70), generator=g70, device=dev) * 0.01).to(torch.bfloat16)
-    X70 = torch.randn((1, K70), generator=g70, device=dev).to(torch.bfloat16)
-    Y70 = torch.empty((1, N70), dtype=torch.bfloat16, device=dev)
-    ws70 = lib.workspace(lib.QN_OP_FWD, 1, N70, K70, R70, dev)
-    sg = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(sg, stream=cap):
-        for i in range(6):
-            lib.qlora_linear_fwd(X70, w70[i % 3], A70, B70, 2.0 * R70, Y=Y70, ws=ws70)
-    for _ in range(2):
-        sg.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(cap):
-        e0.record(cap)
-        for _ in range(STAGE_REPLAYS):
-            sg.replay()
-        e1.record(cap)
-    torch.cuda.synchronize()
-    dec70_us = e0.elapsed_time(e1) * 1e3 / (STAGE_REPLAYS * 6)
-    nb70 = N70 * K70 // 64
-    dec70_bytes = N70 * K70 // 2 + nb70 + 4 * ((nb70 + 255) // 256)
-    del sg, w70, A70, B70, X70, Y70, ws70
-    # Bulk round trip: 7.62e9 weights streamed as 4096 x 4096 bf16 tiles
-    # (N(0, 0.02)) through NF4 quantisation, double quantisation and bf16
-    # dequantisation.  Sixteen distinct tiles (537 MB of source, more than the
-    # Infinity Cache) stand in for the stream; the sweep time is the per-tile
-    # time times the number of tiles.
-    SWEEP_WEIGHTS, TILE = 7.62e9, 4096 * 4096
-    g_sw = torch.Generator(device=dev)
-    g_sw.manual_seed(762)
-    tiles = [(torch.randn((4096, 4096), generator=g_sw, device=dev) * 0.02).to(torch.bfloat16) for _ in range(16)]
-    sw = [lib.quantize_weight(tiles[j]) for j in range(2)]
-    sw_out = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
-    sg = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(sg, stream=cap):
-        for j in range(16):
-            w = sw[j % 2]
-            lib.nf4_quantize(tiles[j], codes=w.codes, absmax=w.absmax)
-            lib.nf4_double_quant(w.absmax, absmax_q=w.absmax_q, scale2=w.scale2)
-            lib.nf4_dequant(w, "bf16", out=sw_out)
-    for _ in range(2):
-        sg.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(cap):
-        e0.record(cap)
-        for _ in range(STAGE_REPLAYS):
-            sg.replay()
-        e1.record(cap)
-    torch.cuda.synchronize()
-    tile_us = e0.elapsed_time(e1) * 1e3 / (STAGE_REPLAYS * 16)
-    nb_t = TILE // 64
-    # bytes per tile: quantise (bf16 in, codes + fp32 scales out), double quant
-    # (fp32 scales in, 8-bit scales + steps out), dequant (codes + 8-bit scales +
-    # steps in, bf16 out)
-    tile_bytes = (2 * TILE + TILE // 2 + 4 * nb_t) + (4 * nb_t + nb_t + 4 * (nb_t // 256)) + \
-                 (TILE // 2 + nb_t + 4 * (nb_t // 256) + 2 * TILE)
-    sweep = {
-        "tile_round_trip_us": round(tile_us, 2),
-        "round_trip_GBps": round(tile_bytes / (tile_us * 1e-6) / 1e9, 1),
-        "sweep_7.62e9_weights_ms": round(SWEEP_WEIGHTS / TILE * tile_us * 1e-3, 2),
-        "stored_bits_per_param": round((TILE // 2 + nb_t + 4 * (nb_t // 256)) * 8 / TILE, 6),
-    }
-    del sg, tiles, sw, sw_out
-    layers = {"qwen2.5_7b": layer_times(lib, dev, cap, QWEN_LINEARS, 16, 4096, bwd=True),
-              "70b": layer_times(lib, dev, cap, L70B_LINEARS, 64, 4096, bwd=False)}
-    # the quantise stages overwrote slot contents with the same values; restore order
-    for i in range(SLOTS):
-        quantize(i)
-    torch.cuda.synchronize()
+    # the two halves of the step alone
+    pre_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE))
+    dec_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_DEC))
+    per_linear = {}
+    for it in L.items:
+        us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE, [it]))
+        dus = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_DEC, [it]), replays=20)
+        per_linear[it["name"]] = {"prefill_us": round(us, 1),
+                                  "prefill_TFLOPs": round(fwd_flops(M70_PRE, it["N"], it["K"], R70) / us / 1e6, 1),
+                                  "decode_us": round(dus, 2),
+                                  "decode_weight_GBps": round(nf4_bytes(it["N"], it["K"]) / dus / 1e3, 1)}
 
-    # ---- traced eager pass over the same steps: per-kernel durations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # kernel trace over one eager step
     lib.trace_enable(True)
     torch.cuda.synchronize()
-    te0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    step()
     torch.cuda.synchronize()
-    te1 = time.perf_counter()
     trace = lib.trace_read()
     lib.trace_enable(False)
-    stage_ms = {k: 0.0 for k in ("quantize+dq", "dequant", "fwd_decode", "fwd_prefill", "bwd")}
-    names = list(stage_ms)
-    for e in evs:
-        for j in range(5):
-            stage_ms[names[j]] += e[j].elapsed_time(e[j + 1]) / args.steps
     kern = {}
     for kind, ms in trace:
         kern.setdefault(kind, []).append(ms)
-    kern_avg = {k: sum(v) / len(v) for k, v in kern.items()}
-    kern_per_step = {k: sum(v) / args.steps for k, v in kern.items()}
+    gemm = kern["gemm_fwd"]
+    gemm_flops = sum(2 * M70_PRE * it["N"] * it["K"] + 2 * M70_PRE * R70 * it["N"] for it in L.items)
+    ach = gemm_flops / (sum(gemm) * 1e-3) / 1e12
+    roofline = {"kernel": "gemm_fwd", "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic("gemm_fwd_70b", "gemm_fwd"),
+                "launches": len(gemm), "avg_ms": round(sum(gemm) / len(gemm), 5),
+                "launch_ms": [round(x, 5) for x in gemm],
+                "work_per_launch": gemm_flops // len(gemm),
+                "note": "one launch per linear (q, k, v, o, gate, up, down) at M = 4096; work = 2MNK + 2MrN "
+                        "per launch (the X A^T product runs in the low-rank kernel)"}
+    gemv = kern.get("gemv", [])
+    gemv_bytes = sum(nf4_bytes(it["N"], it["K"]) + 2 * it["K"] + 2 * it["N"] + 2 * R70 * it["K"] for it in L.items)
+    gemv_roof = None
+    if gemv:
+        a = gemv_bytes / (sum(gemv) * 1e-3) / 1e9
+        gemv_roof = {"kernel": "gemv", "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4), "traffic": traffic("gemv_70b", "gemv"),
+                     "launches": len(gemv), "avg_ms": round(sum(gemv) / len(gemv), 5),
+                     "note": "the streaming kernel alone (its epilogue launch excluded); bytes = NF4 weights + "
+                             "x + y + A read by the H blocks"}
+    quality = L.quality
+    weight_bytes = L.weight_bytes()
+    del L
+    torch.cuda.empty_cache()
 
-    s = sizes()
-    flops_step = s["fwd_flops"] + s["bwd_flops"] + s["gemv_flops"]
-    value = flops_step / (ms_step * 1e-3) / 1e12
+    flops_pre = sum(fwd_flops(M70_PRE, n_, k_, R70) for n_, k_ in L70B.values())
+    stages = {"70b_layer": {"prefill_M4096_us": round(pre_us, 1),
+                            "prefill_M4096_TFLOPs": round(flops_pre / pre_us / 1e6, 1),
+                            "decode_M1_us": round(dec_us, 2),
+                            "decode_M1_weight_GBps": round(weight_bytes / dec_us / 1e3, 1),
+                            "per_linear": per_linear,
+                            "dequant_rel_rmse": {k: round(v, 6) for k, v in quality.items()},
+                            "gemv_roofline": gemv_roof}}
+    metrics = {"prefill_dequant_gemm_TFLOPs": round(flops_pre / pre_us / 1e6, 1),
+               "decode_gemv_weight_GBps": round(weight_bytes / dec_us / 1e3, 1)}
 
-    work = {  # algorithmic work per launch, and its roofline
-        "quantize": (s["quantize_bytes"], "hbm"),
-        "double_quant": (s["dq_bytes"], "hbm"),
-        "dequant": (s["dequant_bytes"], "hbm"),
-        "gemv": (s["gemv_all_bytes"], "hbm"),
-        "gemm_fwd": (s["fwd_gemm_kernel_flops"], "mfma"),
-        "gemm_dx": (s["dx_gemm_kernel_flops"], "mfma"),
-        "lowrank": ((s["lowrank_fwd_bytes"] + s["lowrank_bwd_bytes"]) // 2, "hbm"),
-        "gemm_db": (s["colred_bytes"], "hbm"),
-    }
-
-    def roof(kind):
-        amount, bound = work[kind]
-        avg = kern_avg[kind]
-        if bound == "hbm":
-            ach = amount / (avg * 1e-3) / 1e9
-            return {"kernel": kind, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
-                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic(kind),
-                    "avg_ms": round(avg, 5), "work_per_launch": amount}
-        ach = amount / (avg * 1e-3) / 1e12
-        return {"kernel": kind, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic(kind),
-                "avg_ms": round(avg, 5), "work_per_launch": amount}
-
-    dominant = max((k for k in kern_per_step if k in work), key=lambda k: kern_per_step[k])
-    stages = {
-        "stage_us_graph": {k: round(v, 2) for k, v in stage_us.items()},
-        "prefill_fwd_call_TFLOPs": round(s["fwd_flops"] / (stage_us["fwd_prefill"] * 1e-6) / 1e12, 1),
-        "prefill_fwd_gemm_kernel_TFLOPs": round(s["fwd_gemm_kernel_flops"] / (kern_avg["gemm_fwd"] * 1e-3) / 1e12, 1),
-        "bwd_call_TFLOPs": round(s["bwd_flops"] / (stage_us["bwd"] * 1e-6) / 1e12, 1),
-        "decode_call_weight_GBps": round(s["gemv_weight_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
-        "decode_call_all_GBps": round(s["gemv_all_bytes"] / (stage_us["fwd_decode"] * 1e-6) / 1e9, 1),
-        "bulk_round_trip_bf16_tiles": sweep,
-        "layers_M4096": layers,
-        "decode_70b_gate_call_us": round(dec70_us, 2),
-        "decode_70b_gate_call_weight_GBps": round(dec70_bytes / (dec70_us * 1e-6) / 1e9, 1),
-        "quantize_GBps": round(s["quantize_bytes"] / (stage_us["quantize"] * 1e-6) / 1e9, 1),
-        "double_quant_GBps": round(s["dq_bytes"] / (stage_us["double_quant"] * 1e-6) / 1e9, 1),
-        "dequant_GBps": round(s["dequant_bytes"] / (stage_us["dequant"] * 1e-6) / 1e9, 1),
-        "stage_ms_eager_traced": {k: round(v, 4) for k, v in stage_ms.items()},
-        "eager_traced_ms_per_step": round((te1 - te0) * 1e3 / args.steps, 4),
-        "kernel_avg_ms": {k: round(v, 5) for k, v in kern_avg.items()},
-        "kernel_rooflines": {k: roof(k) for k in work if k in kern_avg},
-    }
+    if not args.no_stages:
+        stages.update(other_stages(torch, lib, dev, cap, log))
     out = {
         "metric": "NF4 dequant-GEMM TFLOP/s (prefill), weight GB/s (decode GEMV), quantize GB/s",
         "value": round(value, 2),
@@ -557,19 +432,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "single 4096x4096 projection: NF4 bs64 + double quant bs256, LoRA r=16 alpha=32, "
-                               "decode M=1 and prefill M=2048 forward, backward at M=2048, fp32 weight source",
-                   "N": N, "K": K, "r": R, "alpha": ALPHA, "M_decode": M_DEC, "M_prefill": M_PRE},
-        "metrics": {
-            "prefill_dequant_gemm_TFLOPs": stages["prefill_fwd_gemm_kernel_TFLOPs"],
-            "decode_gemv_weight_GBps": stages["decode_call_weight_GBps"],
-            "decode_gemv_weight_GBps_70b_gate": stages["decode_70b_gate_call_weight_GBps"],
-            "quantize_GBps": stages["quantize_GBps"],
-        },
-        "roofline": roof(dominant),
-        "stages": stages,
+        "config": {"workload": "70B-shaped layer: q/o 8192x8192, k/v 1024x8192, gate/up 28672x8192, down "
+                               "8192x28672; W ~ N(0, 0.015^2) with 0.1% outliers x10 in NF4 bs64 + double quant "
+                               "bs256; LoRA r=64 alpha=128; decode M=1 and prefill M=4096 forward over all 7 linears",
+                   "hidden": 8192, "r": R70, "alpha": ALPHA70, "M_decode": M70_DEC, "M_prefill": M70_PRE},
     }
+    if "bulk_round_trip_bf16_tiles" in stages:
+        metrics["quantize_GBps"] = stages["bulk_round_trip_bf16_tiles"]["quantize_GBps"]
+    out["metrics"] = metrics
+    out["roofline"] = roofline
+    out["stages"] = stages
     if not args.no_cpu_baseline:
+        log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
     if args.copy_calibration:
@@ -579,6 +453,201 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print("copy calibration: 3 x 268435456 B read + written", file=sys.stderr, flush=True)
+
+
+
+def other_stages(torch, lib, dev, cap, log):
+    """The rest of the path, each on its own configuration (graph-replayed)."""
+    st = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    randn = lambda shape, std: (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(
+        torch.bfloat16)
+
+    # ---- single 4096 x 4096 projection (fp32 source weights)
+    log("4096x4096 projection stages")
+    N, K, R, AL = N2, K2, R2, ALPHA2
+    n = N * K
+    nb = n // 64
+    Wf = [torch.randn((N, K), generator=g, device=dev) * 0.02 for _ in range(8)]   # 512 MiB of fp32 sources
+    w0 = lib.quantize_weight(Wf[0])
+    pool = [lib.NF4Weight(w0.codes.clone(), w0.absmax.clone(), w0.absmax_q.clone(), w0.scale2.clone(), N, K)
+            for _ in range(64)]                                                      # 553 MB of NF4 weights
+    Xd, Xp = randn((M2_DEC, K), 1.0), randn((M2_PRE, K), 1.0)
+    A, B, dY = randn((R, K), 0.01), randn((N, R), 0.01), randn((M2_PRE, N), 1.0)
+    deq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    Yd = torch.empty((M2_DEC, N), dtype=torch.bfloat16, device=dev)
+    Yp = torch.empty((M2_PRE, N), dtype=torch.bfloat16, device=dev)
+    Hp = torch.empty((M2_PRE, R), dtype=torch.float32, device=dev)
+    dX = torch.empty((M2_PRE, K), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
+    dB = torch.empty((N, R), dtype=torch.bfloat16, device=dev)
+    ws_d = lib.workspace(lib.QN_OP_FWD, M2_DEC, N, K, R, dev)
+    ws_p = lib.workspace(lib.QN_OP_FWD, M2_PRE, N, K, R, dev)
+    ws_b = lib.workspace(lib.QN_OP_BWD, M2_PRE, N, K, R, dev)
+    wq = pool[0]
+    us = {}
+    us["quantize_fp32"] = graph_time_us(torch, cap, lambda: [lib.nf4_quantize(Wf[i], codes=pool[i].codes,
+                                                                              absmax=pool[i].absmax)
+                                                             for i in range(8)], calls=8)
+    us["double_quant"] = graph_time_us(torch, cap, lambda: [lib.nf4_double_quant(pool[i].absmax,
+                                                                                 absmax_q=pool[i].absmax_q,
+                                                                                 scale2=pool[i].scale2)
+                                                            for i in range(64)], calls=64)
+    us["dequant_bf16"] = graph_time_us(torch, cap, lambda: [lib.nf4_dequant(pool[i], "bf16", out=deq)
+                                                            for i in range(64)], calls=64)
+    us["fwd_decode_M1"] = graph_time_us(torch, cap, lambda: [lib.qlora_linear_fwd(Xd, pool[i], A, B, AL, Y=Yd,
+                                                                                  ws=ws_d)
+                                                             for i in range(64)], calls=64)
+    us["fwd_prefill_M2048"] = graph_time_us(torch, cap, lambda: [lib.qlora_linear_fwd(Xp, pool[i], A, B, AL, Y=Yp,
+                                                                                      ws=ws_p, H=Hp)
+                                                                 for i in range(8)], calls=8)
+    us["bwd_M2048"] = graph_time_us(torch, cap, lambda: [lib.qlora_linear_bwd(dY, Xp, pool[i], A, B, AL,
+                                                                              out=(dX, dA, dB), ws=ws_b, H=Hp)
+                                                         for i in range(8)], calls=8)
+    wb = nf4_bytes(N, K)
+    p4 = {"us_per_call": {k: round(v, 2) for k, v in us.items()},
+          "quantize_fp32_GBps": round((4 * n + n // 2 + 4 * nb) / us["quantize_fp32"] / 1e3, 1),
+          "double_quant_GBps": round((5 * nb + 4 * (nb // 256)) / us["double_quant"] / 1e3, 1),
+          "dequant_bf16_GBps": round((wb + 2 * n) / us["dequant_bf16"] / 1e3, 1),
+          "decode_call_weight_GBps": round(wb / us["fwd_decode_M1"] / 1e3, 1),
+          "prefill_call_TFLOPs": round(fwd_flops(M2_PRE, N, K, R) / us["fwd_prefill_M2048"] / 1e6, 1),
+          "bwd_call_TFLOPs": round(bwd_flops(M2_PRE, N, K, R) / us["bwd_M2048"] / 1e6, 1)}
+    # kernel trace of one eager pass of these calls
+    lib.trace_enable(True)
+    torch.cuda.synchronize()
+    for i in range(4):
+        lib.nf4_quantize(Wf[i], codes=pool[i].codes, absmax=pool[i].absmax)
+        lib.nf4_double_quant(pool[i].absmax, absmax_q=pool[i].absmax_q, scale2=pool[i].scale2)
+        lib.nf4_dequant(pool[i + 4], "bf16", out=deq)
+        lib.qlora_linear_fwd(Xd, pool[i + 8], A, B, AL, Y=Yd, ws=ws_d)
+        lib.qlora_linear_fwd(Xp, pool[i + 12], A, B, AL, Y=Yp, ws=ws_p, H=Hp)
+        lib.qlora_linear_bwd(dY, Xp, pool[i + 12], A, B, AL, out=(dX, dA, dB), ws=ws_b, H=Hp)
+    torch.cuda.synchronize()
+    tr = lib.trace_read()
+    lib.trace_enable(False)
+    kern = {}
+    for kind, ms in tr:
+        kern.setdefault(kind, []).append(ms)
+    avg = {k: sum(v) / len(v) for k, v in kern.items()}
+    work = {
+        "quantize": ((4 * n + n // 2 + 4 * nb), "hbm"),
+        "double_quant": ((5 * nb + 4 * (nb // 256)), "hbm"),
+        "dequant": ((wb + 2 * n), "hbm"),
+        "gemv": ((wb + 2 * K + 2 * N + 2 * R * K), "hbm"),
+        "gemm_fwd": ((2 * M2_PRE * N * K + 2 * M2_PRE * R * N), "mfma"),
+        "gemm_dx": ((2 * M2_PRE * N * K + 2 * M2_PRE * R * K), "mfma"),
+        # forward launch: X and A read, sH written; backward launch (H given): dY and B^T read, dH and dH^T written
+        "lowrank": (((2 * M2_PRE * K + 2 * R * K + 2 * M2_PRE * R) + (2 * M2_PRE * N + 2 * R * N + 4 * M2_PRE * R)) // 2,
+                    "hbm"),
+        # dA = dH^T X and dB = (sH)^T dY in one launch: X, dY and the two factors read once
+        "gemm_db": ((2 * M2_PRE * (K + N) + 4 * R * M2_PRE), "hbm"),
+    }
+    roofs = {}
+    for k, (amount, bound) in work.items():
+        if k not in avg:
+            continue
+        t = avg[k] * 1e-3
+        if bound == "hbm":
+            a = amount / t / 1e9
+            roofs[k] = {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(a / PEAK_HBM_GBPS, 4), "avg_ms": round(avg[k], 5), "work_per_launch": amount,
+                        "traffic": traffic(k + "_4096", k)}
+        else:
+            a = amount / t / 1e12
+            roofs[k] = {"bound": "mfma", "achieved": round(a, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(a / PEAK_BF16_TFLOPS, 4), "avg_ms": round(avg[k], 5), "work_per_launch": amount,
+                        "traffic": traffic(k + "_4096", k)}
+    p4["kernel_rooflines"] = roofs
+    st["proj4096"] = p4
+    del Wf, pool, w0
+    torch.cuda.empty_cache()
+
+    # ---- Qwen2.5-7B-shaped layer, forward and backward at M = 4096
+    log("Qwen2.5-7B-shaped layer")
+    Q = Layer(torch, lib, dev, QWEN, RQ, 0.02, [MQ], seed=7, bwd_M=MQ)
+    q = {"per_linear": {}}
+    for it in Q.items:
+        fu = graph_time_us(torch, cap, lambda: Q.fwd(lib, MQ, [it], want_H=True))
+        bu = graph_time_us(torch, cap, lambda: Q.bwd(lib, MQ, [it]))
+        q["per_linear"][it["name"]] = {"fwd_us": round(fu, 1), "bwd_us": round(bu, 1),
+                                       "fwd_TFLOPs": round(fwd_flops(MQ, it["N"], it["K"], RQ) / fu / 1e6, 1),
+                                       "bwd_TFLOPs": round(bwd_flops(MQ, it["N"], it["K"], RQ) / bu / 1e6, 1)}
+    fu = graph_time_us(torch, cap, lambda: Q.fwd(lib, MQ, want_H=True))
+    bu = graph_time_us(torch, cap, lambda: Q.bwd(lib, MQ))
+    q.update(fwd_us=round(fu, 1), bwd_us=round(bu, 1), fwd_TFLOPs=round(Q.flops(MQ) / fu / 1e6, 1),
+             bwd_TFLOPs=round(Q.flops(MQ, "bwd") / bu / 1e6, 1))
+    st["qwen2.5_7b_layer_M4096"] = q
+    del Q
+    torch.cuda.empty_cache()
+
+    # ---- bulk sweep: 7.62e9 weights as 4096 x 4096 bf16 tiles, round trip
+    log("bulk round trip")
+    SWEEP_WEIGHTS, TILE = 7.62e9, 4096 * 4096
+    g_sw = torch.Generator(device=dev)
+    g_sw.manual_seed(762)
+    tiles = [(torch.randn((4096, 4096), generator=g_sw, device=dev) * 0.02).to(torch.bfloat16) for _ in range(16)]
+    sw = [lib.quantize_weight(tiles[j]) for j in range(16)]
+    sw_out = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+
+    def round_trip():
+        for j in range(16):
+            w = sw[j]
+            lib.nf4_quantize(tiles[j], codes=w.codes, absmax=w.absmax)
+            lib.nf4_double_quant(w.absmax, absmax_q=w.absmax_q, scale2=w.scale2)
+            lib.nf4_dequant(w, "bf16", out=sw_out)
+
+    tile_us = graph_time_us(torch, cap, round_trip, calls=16)
+    q_us = graph_time_us(torch, cap, lambda: [lib.nf4_quantize(tiles[j], codes=sw[j].codes, absmax=sw[j].absmax)
+                                              for j in range(16)], calls=16)
+    nb_t = TILE // 64
+    q_bytes = 2 * TILE + TILE // 2 + 4 * nb_t
+    tile_bytes = q_bytes + (4 * nb_t + nb_t + 4 * (nb_t // 256)) + (TILE // 2 + nb_t + 4 * (nb_t // 256) + 2 * TILE)
+    # round-trip error over the 16 tiles (bf16 source vs bf16 dequantised)
+    se = sr = 0.0
+    for j in range(16):
+        d = lib.nf4_dequant(sw[j], "bf16")
+        se += float(((d.float() - tiles[j].float()).double() ** 2).sum())
+        sr += float((tiles[j].double() ** 2).sum())
+    st["bulk_round_trip_bf16_tiles"] = {
+        "tile_round_trip_us": round(tile_us, 2),
+        "round_trip_GBps": round(tile_bytes / tile_us / 1e3, 1),
+        "quantize_us": round(q_us, 2),
+        "quantize_GBps": round(q_bytes / q_us / 1e3, 1),
+        "sweep_7.62e9_weights_ms": round(SWEEP_WEIGHTS / TILE * tile_us * 1e-3, 2),
+        "stored_bits_per_param": round((TILE // 2 + nb_t + 4 * (nb_t // 256)) * 8 / TILE, 6),
+        "round_trip_rel_rmse": round((se / sr) ** 0.5, 5),
+        "note": "16 distinct tiles (537 MB of bf16 source) stand in for the 454-tile stream; sweep time = per-tile "
+                "time x 7.62e9 / 4096^2",
+    }
+    del tiles, sw, sw_out
+    torch.cuda.empty_cache()
+
+    # ---- the tiny configuration (launch-bound)
+    from bit_nf4_quantized_08_amd import synth
+    t = synth.tiny_inputs()
+    Wt = torch.from_numpy(t["W"]).to(dev)
+    wt = lib.quantize_weight(Wt)
+    X, A, B, dY = (t[k].to(dev) for k in ("X", "A", "B", "dY"))
+    Yt, Ht = lib.qlora_linear_fwd(X, wt, A, B, t["alpha"], want_H=True)
+    M, r = X.shape[0], A.shape[0]
+    gt = (torch.empty_like(X), torch.empty_like(A), torch.empty_like(B))
+    wsf = lib.workspace(lib.QN_OP_FWD, M, wt.N, wt.K, r, dev)
+    wsb = lib.workspace(lib.QN_OP_BWD, M, wt.N, wt.K, r, dev)
+
+    def qdq():
+        lib.nf4_quantize(Wt, codes=wt.codes, absmax=wt.absmax)
+        lib.nf4_double_quant(wt.absmax, absmax_q=wt.absmax_q, scale2=wt.scale2)
+
+    st["tiny"] = {
+        "quantize_dq_us": round(graph_time_us(torch, cap, qdq, replays=50), 2),
+        "fwd_us": round(graph_time_us(torch, cap, lambda: lib.qlora_linear_fwd(X, wt, A, B, t["alpha"], Y=Yt, H=Ht,
+                                                                               ws=wsf), replays=50), 2),
+        "bwd_us": round(graph_time_us(torch, cap, lambda: lib.qlora_linear_bwd(dY, X, wt, A, B, t["alpha"], H=Ht,
+                                                                               out=gt, ws=wsb), replays=50), 2),
+        "note": "launch-bound: a few microseconds of fixed cost per kernel",
+    }
+    return st
 
 
 if __name__ == "__main__":

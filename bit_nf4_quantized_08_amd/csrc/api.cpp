@@ -30,6 +30,9 @@ int check_weight(const qn_nf4_weight *W) {
 int check_linear_shapes(int64_t M, const qn_nf4_weight *W, int64_t r, float alpha) {
   if (M <= 0 || r < 1 || r > QN_MAX_RANK) return QN_ERR_SHAPE;
   if (W->K % QN_BLOCK != 0 || W->N % QN_BLOCK != 0) return QN_ERR_SHAPE;
+  // The GEMM kernels address the code array with 32-bit byte offsets (the
+  // transposed reader of the backward spans all of it): N*K/2 bytes must fit.
+  if (W->N * W->K / 2 > (int64_t)INT32_MAX) return QN_ERR_SHAPE;
   if (M > kMaxElems / W->K || M > kMaxElems / W->N) return QN_ERR_SHAPE;
   if (M > INT32_MAX / 64 || W->N > INT32_MAX / 64) return QN_ERR_SHAPE;
   if (!std::isfinite(alpha)) return QN_ERR_VALUE;
@@ -114,16 +117,16 @@ int qlora_linear_fwd(const void *X, int64_t M, const qn_nf4_weight *W, const voi
   return hip_status(qn::run_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
-int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qn_nf4_weight *W, const void *A,
-                     const void *B, int64_t r, float alpha, void *dX, void *dA, void *dB, void *workspace,
-                     size_t ws_bytes, void *stream) {
+int qlora_linear_bwd(const void *dY, const void *X, const float *H, int64_t M, const qn_nf4_weight *W,
+                     const void *A, const void *B, int64_t r, float alpha, void *dX, void *dA, void *dB,
+                     void *workspace, size_t ws_bytes, void *stream) {
   int st = check_weight(W);
   if (st != QN_OK) return st;
   if (!dY || !X || !A || !B || !dA || !dB) return QN_ERR_NULL;
   st = check_linear_shapes(M, W, r, alpha);
   if (st != QN_OK) return st;
   if (!aligned(dY, 16) || !aligned(X, 16) || !aligned(A, 16) || !aligned(B, 16) || !aligned(dA, 16) ||
-      !aligned(dB, 16) || (dX && !aligned(dX, 16)))
+      !aligned(dB, 16) || (dX && !aligned(dX, 16)) || (H && !aligned(H, 4)))
     return QN_ERR_ALIGN;
   const size_t need = qn::bwd_workspace(M, W->N, W->K, r);
   if (!workspace || ws_bytes < need) return QN_ERR_WORKSPACE;
@@ -132,6 +135,7 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qn_nf4_weig
   qn::BwdArgs a{};
   a.dY = static_cast<const uint16_t *>(dY);
   a.X = static_cast<const uint16_t *>(X);
+  a.H = H;
   a.M = M; a.N = W->N; a.K = W->K; a.r = r;
   a.codes = W->codes;
   a.sc = qn::ScaleSrc{W->absmax, W->absmax_q, W->scale2};

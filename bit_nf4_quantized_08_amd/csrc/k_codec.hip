@@ -279,16 +279,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
 
 int grid_for(int64_t work_items, int per_cu_waves = 8) {
   // At most a few workgroups per CU for a grid-stride loop; at least one item each.
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  static int cus = 0;
-  if (cus == 0) {
-    hipDeviceProp_t p;
-    if (hipGetDeviceProperties(&p, dev) == hipSuccess) cus = p.multiProcessorCount;
-    if (cus <= 0) cus = 256;
-  }
   int64_t wgs = (work_items + kThreads - 1) / kThreads;
-  int64_t cap = (int64_t)cus * per_cu_waves;
+  const int64_t cap = (int64_t)device_cus() * per_cu_waves;
   if (wgs > cap) wgs = cap;
   if (wgs < 1) wgs = 1;
   return (int)wgs;

@@ -17,7 +17,8 @@
 //                         applied to partial sums.  Its first blocks compute
 //                         the adapter's H partials.
 //   gemv_epilogue_kernel  adds the split partials and the adapter term.
-//   transpose_bf16_kernel B^T for the backward's dH = dY B.
+//   bwd_prep_kernel       B^T for the backward's dH = dY B, and (s H)^T from a
+//                         given H.
 
 #include <map>
 #include <mutex>
@@ -51,15 +52,25 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
 
 __device__ __forceinline__ int64_t cdiv_d(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Transpose a small bf16 matrix: out[c][r] = in[r][c] for c < C, rows of out
-// beyond C (up to out_rows) zero.  in is [R, C] with leading dim ldi.
-__global__ __launch_bounds__(kThreads) void transpose_bf16_kernel(const uint16_t *__restrict__ in, int64_t R,
-                                                                  int64_t C, int64_t ldi,
-                                                                  uint16_t *__restrict__ out, int64_t out_rows) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // over out_rows * R
-  if (idx >= out_rows * R) return;
-  const int64_t c = idx / R, r = idx % R;
-  out[c * R + r] = (c < C) ? in[r * ldi + c] : (uint16_t)0;
+// Backward preparation in one launch: Bt[j][n] = B[n][j] for j < r and zero for
+// r <= j < rp (B is [N, r]); when H is given, also sHt[j][m] = bf16(s H[m][j])
+// for j < r, m < M, zero elsewhere in [rp, Mp] (H is [M, r] fp32).  Thread idx
+// writes element idx of Bt, then of sHt: the writes are coalesced, the reads of
+// the two small factors strided.
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t *__restrict__ B, int64_t N, int64_t r,
+                                                            int64_t rp, uint16_t *__restrict__ Bt,
+                                                            const float *__restrict__ H, int64_t M, int64_t Mp,
+                                                            float s, uint16_t *__restrict__ sHt) {
+  int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx < rp * N) {
+    const int64_t j = idx / N, n = idx % N;
+    Bt[idx] = j < r ? B[n * r + j] : (uint16_t)0;
+    return;
+  }
+  idx -= rp * N;
+  if (!H || idx >= rp * Mp) return;
+  const int64_t j = idx / Mp, m = idx % Mp;
+  sHt[idx] = (j < r && m < M) ? f32_to_bf16(H[m * r + j] * s) : (uint16_t)0;
 }
 
 // ================================================================ GEMV (decode)
@@ -392,17 +403,7 @@ __global__ __launch_bounds__(kThreads) void gemv_epilogue_kernel(const float *__
 }
 
 // ================================================================ host side
-int num_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    hipDeviceProp_t p;
-    if (hipGetDeviceProperties(&p, dev) == hipSuccess) cus = p.multiProcessorCount;
-    if (cus <= 0) cus = 256;
-  }
-  return cus;
-}
+int num_cus() { return device_cus(); }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -521,9 +522,12 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
                 h_blocks, p.hsplits, p.hkps};
     dim3 grid((unsigned)(h_blocks + p.row_wgs));
     const Code16 cb = code16();
-    TraceScope tr(QN_TRACE_GEMV, st);
-    void *args[] = {&ga, const_cast<Code16 *>(&cb)};
-    QN_TRY(hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, st));
+    {
+      // The trace brackets the streaming kernel alone, not the epilogue.
+      TraceScope tr(QN_TRACE_GEMV, st);
+      void *args[] = {&ga, const_cast<Code16 *>(&cb)};
+      QN_TRY(hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, st));
+    }
     QN_TRY(hipGetLastError());
     hipLaunchKernelGGL(gemv_epilogue_kernel, dim3((unsigned)(a.N / EPI_ROWS)), dim3(kThreads), 0, st,
                        y_part, p.splits, h_part, p.hsplits, a.M, a.N, a.r, a.B, a.s, a.Y, a.H_out);
@@ -574,11 +578,16 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
   float *bpart = c.take<float>((int64_t)colred_splits(a.M) * a.r * a.N);
   float *apart = c.take<float>((int64_t)colred_splits(a.M) * a.r * a.K);
 
-  // B^T [rp, N] (rows >= r zero) so that dH = dY (B^T)^T runs on the low-rank kernel.
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(rp * a.N, kThreads)), dim3(kThreads), 0, st,
-                     a.B, a.N, a.r, a.r, Bt, rp);
-  QN_TRY(hipGetLastError());
-  // One launch: dH = s dY B -> dHb [M, rp], dHt [rp, Mp]; H = X A^T -> (sH)^T [rp, Mp].
+  // B^T [rp, N] (rows >= r zero) so that dH = dY (B^T)^T runs on the low-rank
+  // kernel; with the forward's H given, (sH)^T from it in the same launch.
+  {
+    const int64_t elems = rp * a.N + (a.H ? rp * Mp : 0);
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)cdiv(elems, kThreads)), dim3(kThreads), 0, st, a.B, a.N,
+                       a.r, rp, Bt, a.H, a.M, Mp, a.s, sHt);
+    QN_TRY(hipGetLastError());
+  }
+  // One launch: dH = s dY B -> dHb [M, rp], dHt [rp, Mp]; without a given H also
+  // H = X A^T -> (sH)^T [rp, Mp].
   {
     LowRankArgs ld{}, lh{};
     ld.L = a.dY; ld.ldl = a.N; ld.M = a.M; ld.Kc = a.N;
@@ -587,7 +596,7 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
     lh.L = a.X; lh.ldl = a.K; lh.M = a.M; lh.Kc = a.K;
     lh.P = a.A; lh.ldp = a.K; lh.R = a.r; lh.scale = a.s;
     lh.out_t = sHt; lh.ldt_rows = rp; lh.Mp = Mp;
-    QN_TRY(launch_lowrank2(ld, &lh, st));
+    QN_TRY(launch_lowrank2(ld, a.H ? nullptr : &lh, st));
   }
 
   // One launch: dB [N, r] = ((sH)^T dY)^T and dA [r, K] = dH^T X, contractions over M.

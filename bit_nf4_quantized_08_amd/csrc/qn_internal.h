@@ -30,6 +30,9 @@ bool codec_tables_ok();
 // Host: fp64 NF4 rows before rounding (exposed for the library's own checks).
 void nf4_rows_f64(double out[16]);
 
+// Compute units of the current device (device.cpp); cached per device, thread-safe.
+int device_cus();
+
 // Kernel-level timing (trace.cpp).  While tracing is enabled, an object of this
 // type records a start event on construction and a stop event on destruction,
 // on the given stream, and logs the pair under `kind` (QN_TRACE_* codes).
@@ -152,6 +155,7 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t s);
 struct BwdArgs {
   const uint16_t *dY;    // bf16 [M,N]
   const uint16_t *X;     // bf16 [M,K]
+  const float *H;        // fp32 [M,r] = X A^T from the forward, or null (recomputed)
   int64_t M, N, K, r;
   const uint8_t *codes;
   ScaleSrc sc;

@@ -63,8 +63,8 @@ def load():
         "qlora_workspace_size": (ctypes.c_size_t, [i32, i64, i64, i64, i64]),
         "qlora_linear_fwd": (i32, [vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp,
                                    ctypes.c_size_t, vp]),
-        "qlora_linear_bwd": (i32, [vp, vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp,
-                                   vp, ctypes.c_size_t, vp]),
+        "qlora_linear_bwd": (i32, [vp, vp, vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp,
+                                   vp, vp, ctypes.c_size_t, vp]),
         "qn_status_string": (ctypes.c_char_p, [i32]),
         "qn_trace_enable": (i32, [i32]),
         "qn_trace_read": (i32, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float), i32]),
@@ -209,8 +209,10 @@ def workspace(op, M, N, K, r, device="cuda"):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def qlora_linear_fwd(X, w: NF4Weight, A, B, alpha, want_H=False, use_double_quant=True, Y=None, ws=None):
-    """Y = X bf16(dequant(W))^T + (alpha/r) (X A^T) B^T; returns Y (and H)."""
+def qlora_linear_fwd(X, w: NF4Weight, A, B, alpha, want_H=False, use_double_quant=True, Y=None, ws=None, H=None):
+    """Y = X bf16(dequant(W))^T + (alpha/r) (X A^T) B^T; returns Y (and H).
+
+    ``H`` (optional, fp32 [M, r]) receives X A^T; passing it implies want_H."""
     torch = _torch()
     _need(X, "X", torch.bfloat16, 2)
     _need(A, "A", torch.bfloat16, 2)
@@ -221,7 +223,16 @@ def qlora_linear_fwd(X, w: NF4Weight, A, B, alpha, want_H=False, use_double_quan
         raise ValueError("shape mismatch between X, W, A, B")
     if Y is None:
         Y = torch.empty((M, w.N), dtype=torch.bfloat16, device=X.device)
-    H = torch.empty((M, r), dtype=torch.float32, device=X.device) if want_H else None
+    _need(Y, "Y", torch.bfloat16, 2)
+    if Y.shape != (M, w.N):
+        raise ValueError("Y must be [M, N]")
+    if H is not None:
+        _need(H, "H", torch.float32, 2)
+        if H.shape != (M, r):
+            raise ValueError("H must be [M, r]")
+        want_H = True
+    elif want_H:
+        H = torch.empty((M, r), dtype=torch.float32, device=X.device)
     if ws is None:
         ws = workspace(QN_OP_FWD, M, w.N, w.K, r, X.device)
     st = w.struct(use_double_quant)
@@ -231,8 +242,12 @@ def qlora_linear_fwd(X, w: NF4Weight, A, B, alpha, want_H=False, use_double_quan
     return (Y, H) if want_H else Y
 
 
-def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_quant=True, out=None, ws=None):
-    """Returns (dX or None, dA, dB) for the upstream gradient dY."""
+def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_quant=True, out=None, ws=None,
+                     H=None):
+    """Returns (dX or None, dA, dB) for the upstream gradient dY.
+
+    ``H`` (optional, fp32 [M, r]) is X A^T as the forward returned it with
+    ``want_H=True``; given, the call does not recompute it from X."""
     torch = _torch()
     _need(dY, "dY", torch.bfloat16, 2)
     _need(X, "X", torch.bfloat16, 2)
@@ -242,6 +257,10 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_
     r = A.shape[0]
     if dY.shape != (M, w.N) or K != w.K or A.shape[1] != w.K or B.shape != (w.N, r):
         raise ValueError("shape mismatch between dY, X, W, A, B")
+    if H is not None:
+        _need(H, "H", torch.float32, 2)
+        if H.shape != (M, r):
+            raise ValueError("H must be [M, r]")
     if out is None:
         dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device) if want_dX else None
         dA = torch.empty((r, K), dtype=torch.bfloat16, device=X.device)
@@ -252,7 +271,7 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_
         ws = workspace(QN_OP_BWD, M, w.N, w.K, r, X.device)
     st = w.struct(use_double_quant)
     _check("qlora_linear_bwd", load().qlora_linear_bwd(
-        _ptr(dY), _ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(dX), _ptr(dA),
+        _ptr(dY), _ptr(X), _ptr(H), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(dX), _ptr(dA),
         _ptr(dB), _ptr(ws), ws.numel(), _stream()))
     return dX, dA, dB
 

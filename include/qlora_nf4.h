@@ -133,11 +133,14 @@ size_t qlora_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t r);
  *     Y = X * bf16(dequant(W))^T + (alpha/r) * (X * A^T) * B^T
  *   X   device bf16 [M, K]      A  device bf16 [r, K]      B  device bf16 [N, r]
  *   Y   device bf16 [M, N] out (fp32 accumulation, rounded to nearest even once)
- *   H_out  device fp32 [M, r] out, X*A^T (unscaled), or NULL.
+ *   H_out  device fp32 [M, r] out, X*A^T (unscaled), or NULL.  Keeping it for
+ *       the backward saves that call a second pass over X.
  *   workspace  device, >= qlora_workspace_size(QN_OP_FWD, M, N, K, r) bytes.
- * Requires M >= 1, N % 64 == 0, K % 64 == 0 (whole blocks per row, whole
- * contraction steps in both directions), 1 <= r <= QN_MAX_RANK, finite alpha;
- * workspace 256-byte aligned.
+ * Requires M >= 1, N % 64 == 0, K % 64 == 0 (whole blocks per row; whole
+ * contraction steps of 64 over K in the forward and over N in dX),
+ * N*K/2 <= INT32_MAX (the kernels address the codes with 32-bit byte offsets),
+ * 1 <= r <= QN_MAX_RANK, finite alpha; workspace 256-byte aligned, H_out 4-byte
+ * aligned.  Any other shape returns QN_ERR_SHAPE before anything is launched.
  * M <= 8 runs the streaming decode path (weights read once at HBM rate); larger
  * M runs the MFMA path (tiles dequantised into LDS, bf16 MFMA). */
 int qlora_linear_fwd(const void *X, int64_t M, const qn_nf4_weight *W,
@@ -151,11 +154,14 @@ int qlora_linear_fwd(const void *X, int64_t M, const qn_nf4_weight *W,
  * With G = dY, s = alpha/r, H = X A^T:
  *     dH = s G B,  dB = s G^T H,  dA = dH^T X,  dX = G bf16(dequant(W)) + dH A
  *   dY  device bf16 [M, N]; X, A, B as in the forward.
+ *   H   device fp32 [M, r]: X A^T as the forward wrote it to H_out, or NULL,
+ *       in which case it is recomputed from X and A (one more read of X).
+ *       With H given, dB uses bf16(s H) of these values; 4-byte aligned.
  *   dX  device bf16 [M, K] out, or NULL to skip it.
  *   dA  device bf16 [r, K] out;  dB device bf16 [N, r] out.
  *   workspace  device, >= qlora_workspace_size(QN_OP_BWD, M, N, K, r) bytes.
  * Same shape rules as the forward. */
-int qlora_linear_bwd(const void *dY, const void *X, int64_t M,
+int qlora_linear_bwd(const void *dY, const void *X, const float *H, int64_t M,
                      const qn_nf4_weight *W, const void *A, const void *B,
                      int64_t r, float alpha, void *dX, void *dA, void *dB,
                      void *workspace, size_t ws_bytes, void *stream);

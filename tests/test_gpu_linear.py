@@ -1,12 +1,25 @@
 """GPU parity of the fused QLoRA linear (forward and backward) against the fp64 oracle.
 
-Tolerance: relative Frobenius error <= 5e-3 per output tensor (Y, H, dX, dA,
-dB), with the adapter term also checked alone (W = 0).  The decode path
-(M <= 8) and the MFMA path (M > 8) are both covered, with ragged M, N not a
-multiple of the 128-wide tile, several ranks, with and without double
-quantisation, and at the full 4096x4096 / 7B-layer / 70B-layer shapes on
-sampled output rows.
+Every output (Y, H, dX, dA, dB) is written into a buffer with guard bands on both
+sides, and checked two ways against the oracle:
+
+* relative Frobenius error <= 5e-3 per tensor, and
+* element by element, |got - ref| <= 2 * 2^-8 * bound, where bound is the same
+  contraction taken over absolute values (for Y: |X| |W_hat|^T + s |H| |B|^T).
+  The kernels round each output to bf16 once (2^-9 relative), feed bf16-rounded
+  adapter intermediates (s H, dH) to the matrix unit (2^-9 of their share), the
+  decode path rounds the table rows rather than their products to bf16 (2^-8),
+  and accumulate in fp32; 2 * 2^-8 covers the sum.  A wrong tile, row or
+  column shows here even when a norm over the whole tensor would dilute it.
+
+The decode path (M <= 8) and the MFMA path (M > 8) are both covered, with ragged
+M, N not a multiple of the 128-wide tile, several ranks, with and without double
+quantisation, the backward with the forward's H given and recomputed, and every
+linear of the 7B- and 70B-shaped layers at full size (sampled output rows where
+the fp64 reference of a whole output would take too long).
 """
+
+import functools
 
 import numpy as np
 import pytest
@@ -18,17 +31,32 @@ from tests.gpu_util import REL_FRO_TOL, dev, guarded, guards_intact, host, rel_f
 
 pytestmark = pytest.mark.gpu
 
+ELEM_C = 2.0 * 2.0 ** -8
+
+
+@functools.lru_cache(maxsize=4)
+def _weight(N, K, seed, w_std, outliers, w_zero):
+    if w_zero:
+        return np.zeros((N, K), np.float32)
+    W = synth.gaussian((N, K), w_std, synth.SEED_W + seed)
+    if outliers:
+        W = synth.with_outliers(W, 0.001, 10.0)
+    return W
+
+
+@functools.lru_cache(maxsize=4)
+def _oracle_codes(N, K, seed, w_std, outliers, w_zero):
+    p, a, _ = oracle.quantize(_weight(N, K, seed, w_std, outliers, w_zero))
+    k, step = oracle.double_quant(a)
+    return p, a, k, step
+
 
 class Case:
     def __init__(self, N, K, M, r, alpha, seed=0, w_std=0.02, w_zero=False, outliers=False, x_std=1.0,
                  ab_std=0.01):
         self.N, self.K, self.M, self.r, self.alpha = N, K, M, r, alpha
-        W = synth.gaussian((N, K), w_std, synth.SEED_W + seed)
-        if outliers:
-            W = synth.with_outliers(W, 0.001, 10.0)
-        if w_zero:
-            W = np.zeros((N, K), np.float32)
-        self.W = W
+        self.key = (N, K, seed, w_std, outliers, w_zero)
+        self.W = _weight(*self.key)
         self.Xb = synth.to_bf16(synth.gaussian((M, K), x_std, synth.SEED_X + seed))
         self.Ab = synth.to_bf16(synth.gaussian((r, K), ab_std, synth.SEED_A + seed))
         self.Bb = synth.to_bf16(synth.gaussian((N, r), ab_std, synth.SEED_B + seed))
@@ -37,47 +65,126 @@ class Case:
         self.A = synth.bf16_values(self.Ab)
         self.B = synth.bf16_values(self.Bb)
         self.dY = synth.bf16_values(self.dYb)
+        self.s = alpha / r
 
     def oracle_weight(self, dq=True):
-        p, a, _ = oracle.quantize(self.W)
-        scale = oracle.dq_absmax(*oracle.double_quant(a)) if dq else a
+        p, a, k, step = _oracle_codes(*self.key)
+        scale = oracle.dq_absmax(k, step) if dq else a
         return oracle.dequant_bf16_weight(p, self.N, self.K, scale)
 
-    def device(self, dq=True):
+    def device(self):
         w = lib.quantize_weight(to_dev(self.W), double_quant=True)
         return w, self.Xb.to(dev()), self.Ab.to(dev()), self.Bb.to(dev()), self.dYb.to(dev())
 
+    def check_codes(self, w):
+        """The device codec at this shape is bit-exact with the oracle."""
+        p, _, k, step = _oracle_codes(*self.key)
+        assert np.array_equal(host(w.codes), p), "codes differ from the oracle"
+        assert np.array_equal(host(w.absmax_q), k), "8-bit scales differ from the oracle"
+        assert np.array_equal(host(w.scale2).view(np.uint32), step.view(np.uint32)), "group steps differ"
 
-def _check(name, got, ref, tol=REL_FRO_TOL):
+
+class Out:
+    """An output tensor with guard bands on both sides."""
+
+    def __init__(self, shape, dtype):
+        self.shape, self.dtype = shape, dtype
+        self.nbytes = int(np.prod(shape)) * (2 if dtype == torch.bfloat16 else 4)
+        self.full, view = guarded(self.nbytes, dtype)
+        self.t = view.view(*shape)
+
+    def check_guards(self, name):
+        assert guards_intact(self.full, self.nbytes), f"{name}: guard band overwritten"
+
+
+def _check(name, got, ref, bound, tol=REL_FRO_TOL):
+    """Relative Frobenius error and the elementwise bound (see the module docstring)."""
+    got = np.asarray(got, np.float64)
     e = rel_fro(got, ref)
     assert e <= tol, f"{name}: relative Frobenius error {e:.3e} > {tol:.1e}"
+    err = np.abs(got - ref)
+    lim = ELEM_C * np.asarray(bound, np.float64) + 1e-30
+    bad = err > lim
+    if np.any(bad):
+        i = np.unravel_index(int(np.argmax(err / lim)), err.shape)
+        raise AssertionError(f"{name}: {int(bad.sum())} elements beyond the elementwise bound; worst at {i}: "
+                             f"got {got[i]!r}, ref {ref[i]!r}, bound {lim[i]!r}")
     return e
 
 
-def run_fwd_bwd(c: Case, dq=True, bwd=True):
+def _abs64(a):
+    return np.abs(np.asarray(a, np.float64))
+
+
+def fwd_bounds(c, Wh, X, H):
+    return _abs64(X) @ _abs64(Wh).T + c.s * (_abs64(H) @ _abs64(c.B).T)
+
+
+def check_forward(c, Y, H, Wh, sel=None):
+    X = c.X if sel is None else c.X[sel]
+    Yref, Href = oracle.forward(X, Wh, c.A, c.B, c.alpha)
+    Yg, Hg = host(Y), host(H)
+    if sel is not None:
+        Yg, Hg = Yg[sel], Hg[sel]
+    _check("Y", Yg, Yref, fwd_bounds(c, Wh, X, Href))
+    _check("H", Hg, Href, _abs64(X) @ _abs64(c.A).T)
+
+
+def check_backward(c, dX, dA, dB, Wh, sel=None):
+    _, dAr, dBr = oracle.backward(c.dY, c.X, None, c.A, c.B, c.alpha, want_dX=False)
+    G, X = _abs64(c.dY), _abs64(c.X)
+    Href = np.asarray(c.X, np.float64) @ np.asarray(c.A, np.float64).T
+    dHref = c.s * (np.asarray(c.dY, np.float64) @ np.asarray(c.B, np.float64))
+    _check("dA", host(dA), dAr, np.abs(dHref).T @ X)
+    _check("dB", host(dB), dBr, c.s * (G.T @ np.abs(Href)))
+    if dX is None:
+        return
+    if sel is None:
+        dXr, _, _ = oracle.backward(c.dY, c.X, Wh, c.A, c.B, c.alpha)
+        got, Gs, dHs = host(dX), G, dHref
+    else:
+        dXr, _, _ = oracle.backward(c.dY[sel], c.X[sel], Wh, c.A, c.B, c.alpha)
+        got, Gs, dHs = host(dX)[sel], G[sel], dHref[sel]
+    _check("dX", got, dXr, Gs @ _abs64(Wh) + np.abs(dHs) @ _abs64(c.A))
+
+
+def run_fwd_bwd(c: Case, dq=True, bwd=True, rows=None, seed=0, check_codes=False):
+    """Forward (and backward) on the device, every output guard-banded.  With
+    ``rows`` only that many sampled rows of Y, H and dX are compared (dA and dB
+    always in full).  The backward runs twice: recomputing H, and with the
+    forward's H given; both are checked, and on the MFMA path (where the forward
+    and the recompute form H by the same kernel) they must agree bit for bit."""
     w, X, A, B, dY = c.device()
+    if check_codes:
+        c.check_codes(w)
     Wh = c.oracle_weight(dq)
-    Yref, Href = oracle.forward(c.X, Wh, c.A, c.B, c.alpha)
-    nY = c.M * c.N * 2
-    yf, Y = guarded(nY, torch.bfloat16)
-    Y = Y.view(c.M, c.N)
-    Y, H = lib.qlora_linear_fwd(X, w, A, B, c.alpha, want_H=True, use_double_quant=dq, Y=Y)
-    assert guards_intact(yf, nY), "Y guard band overwritten"
-    _check("Y", host(Y), Yref)
-    _check("H", host(H), Href)
+    sel = None if rows is None else np.sort(np.random.default_rng(seed + 1).choice(c.M, size=min(rows, c.M),
+                                                                                   replace=False))
+    Y, H = Out((c.M, c.N), torch.bfloat16), Out((c.M, c.r), torch.float32)
+    lib.qlora_linear_fwd(X, w, A, B, c.alpha, use_double_quant=dq, Y=Y.t, H=H.t)
+    Y.check_guards("Y")
+    H.check_guards("H")
+    check_forward(c, Y.t, H.t, Wh, sel)
     if not bwd:
         return
-    dXr, dAr, dBr = oracle.backward(c.dY, c.X, Wh, c.A, c.B, c.alpha)
-    dX, dA, dB = lib.qlora_linear_bwd(dY, X, w, A, B, c.alpha, use_double_quant=dq)
-    _check("dX", host(dX), dXr)
-    _check("dA", host(dA), dAr)
-    _check("dB", host(dB), dBr)
+    results = []
+    for given in (False, True):
+        dX, dA, dB = Out((c.M, c.K), torch.bfloat16), Out((c.r, c.K), torch.bfloat16), Out((c.N, c.r), torch.bfloat16)
+        lib.qlora_linear_bwd(dY, X, w, A, B, c.alpha, use_double_quant=dq, out=(dX.t, dA.t, dB.t),
+                             H=H.t if given else None)
+        for name, o in (("dX", dX), ("dA", dA), ("dB", dB)):
+            o.check_guards(name + (" (H given)" if given else ""))
+        check_backward(c, dX.t, dA.t, dB.t, Wh, sel)
+        results.append((dX.t, dA.t, dB.t))
+    if c.M > 8:
+        for name, a, b in zip(("dX", "dA", "dB"), results[0], results[1]):
+            assert torch.equal(a, b), f"{name} differs between a given and a recomputed H"
 
 
 def test_tiny_config_forward_backward():
     say("tiny config fwd+bwd (decode path, M=4)")
     t = synth.TINY
-    run_fwd_bwd(Case(t["N"], t["K"], t["M"], t["r"], t["alpha"]))
+    run_fwd_bwd(Case(t["N"], t["K"], t["M"], t["r"], t["alpha"]), check_codes=True)
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
@@ -87,7 +194,7 @@ def test_decode_path_small_M(M):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 192, 3584), (2, 64, 2560), (3, 320, 6208), (1, 64, 6208), (1, 1024, 8192),
-                                   (1, 128, 20480)])
+                                   (1, 128, 20480), (8, 192, 6208), (5, 128, 10240)])
 def test_decode_path_ragged(M, N, K):
     """Contraction lengths that are not a multiple of the decode path's
     2048-wide chunk (its out-of-range loads) and that do not fill the last
@@ -96,7 +203,8 @@ def test_decode_path_ragged(M, N, K):
     run_fwd_bwd(Case(N, K, M, 16, 32.0, seed=N + K), bwd=False)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 192, 3584), (1, 256, 8192), (2, 128, 4096), (3, 320, 6208), (8, 128, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 192, 3584), (1, 256, 8192), (2, 128, 4096), (3, 320, 6208), (8, 128, 2048),
+                                   (8, 128, 8192)])
 def test_decode_path_fp32_scales(M, N, K):
     """The decode path reading fp32 block scales (no double quantisation),
     with and without a ragged last chunk."""
@@ -155,45 +263,24 @@ def test_deterministic():
         assert torch.equal(a, b)
 
 
-def _sampled_rows(M, k, seed):
-    return np.sort(np.random.default_rng(seed).choice(M, size=min(k, M), replace=False))
-
-
-def run_full_size_sampled(N, K, M, r, alpha, w_std=0.02, outliers=False, bwd=True, seed=0, rows=64, dq=True):
-    """Full-size GPU run; the oracle checks a seeded subset of output rows of Y and
-    dX, and dA / dB in full (their reductions over M are cheap in fp64)."""
-    c = Case(N, K, M, r, alpha, seed=seed, w_std=w_std, outliers=outliers)
-    w, X, A, B, dY = c.device()
-    Wh = c.oracle_weight(dq)
-    sel = _sampled_rows(M, rows, seed + 1)
-    Y, H = lib.qlora_linear_fwd(X, w, A, B, alpha, want_H=True, use_double_quant=dq)
-    Yref, Href = oracle.forward(c.X[sel], Wh, c.A, c.B, alpha)
-    _check("Y rows", host(Y)[sel], Yref)
-    _check("H rows", host(H)[sel], Href)
-    if not bwd:
-        return
-    dX, dA, dB = lib.qlora_linear_bwd(dY, X, w, A, B, alpha, use_double_quant=dq)
-    _, dAr, dBr = oracle.backward(c.dY, c.X, None, c.A, c.B, alpha, want_dX=False)
-    _check("dA", host(dA), dAr)
-    _check("dB", host(dB), dBr)
-    dXr, _, _ = oracle.backward(c.dY[sel], c.X[sel], Wh, c.A, c.B, alpha)
-    _check("dX rows", host(dX)[sel], dXr)
-
-
 def test_proj4096_decode_full():
-    say("4096x4096 M=1 decode")
+    say("4096x4096 M=1 decode, every output")
     p = synth.PROJ4096
-    c = Case(4096, 4096, 1, p["r"], p["alpha"], seed=0)
-    w, X, A, B, _ = c.device()
-    Y = lib.qlora_linear_fwd(X, w, A, B, c.alpha)
-    Yref, _ = oracle.forward(c.X, c.oracle_weight(), c.A, c.B, c.alpha)
-    _check("Y", host(Y), Yref)
+    run_fwd_bwd(Case(4096, 4096, 1, p["r"], p["alpha"], seed=0), bwd=False, check_codes=True)
+
+
+def test_proj4096_decode_m8_full():
+    """M = 8 (the instance with the most activation registers) over two
+    K-segments at 4096x4096, every output."""
+    say("4096x4096 M=8 decode, every output")
+    p = synth.PROJ4096
+    run_fwd_bwd(Case(4096, 4096, 8, p["r"], p["alpha"], seed=0), bwd=False)
 
 
 def test_proj4096_prefill_sampled():
     say("4096x4096 M=2048 prefill fwd+bwd")
     p = synth.PROJ4096
-    run_full_size_sampled(4096, 4096, 2048, p["r"], p["alpha"])
+    run_fwd_bwd(Case(4096, 4096, 2048, p["r"], p["alpha"], seed=0), rows=64, seed=0)
 
 
 def test_proj4096_prefill_fp32_scales_sampled():
@@ -201,54 +288,40 @@ def test_proj4096_prefill_fp32_scales_sampled():
     the kernels whose per-step reload is one load shorter."""
     say("4096x4096 M=2048 prefill fwd+bwd, fp32 block scales")
     p = synth.PROJ4096
-    run_full_size_sampled(4096, 4096, 2048, p["r"], p["alpha"], seed=11, dq=False)
+    run_fwd_bwd(Case(4096, 4096, 2048, p["r"], p["alpha"], seed=11), dq=False, rows=64, seed=11)
 
 
-def test_qwen_layer_shapes_sampled():
+@pytest.mark.parametrize("name", list(synth.QWEN7B["linears"]))
+def test_qwen_layer_linear(name):
+    """Every linear of the Qwen2.5-7B-shaped layer at M = 4096 tokens, forward
+    and backward (sampled rows of Y, H, dX; dA, dB in full; codes bit-exact)."""
     q = synth.QWEN7B
-    for name in ("k", "down"):
-        N, K = q["linears"][name]
-        say(f"qwen {name} {N}x{K} M=4096 fwd+bwd")
-        run_full_size_sampled(N, K, q["M"], q["r"], q["alpha"], seed=3, rows=32)
+    N, K = q["linears"][name]
+    say(f"qwen {name} {N}x{K} M=4096 fwd+bwd")
+    seed = 20 + list(q["linears"]).index(name)
+    run_fwd_bwd(Case(N, K, q["M"], q["r"], q["alpha"], seed=seed), rows=16, seed=seed, check_codes=True)
 
 
-def test_70b_layer_shapes_sampled():
-    L = synth.L70B
-    N, K = L["linears"]["k"]
-    say(f"70b k {N}x{K} M=1 and M=4096 fwd")
-    c = Case(N, K, 1, L["r"], L["alpha"], seed=4, w_std=L["w_std"], outliers=True)
-    w, X, A, B, _ = c.device()
-    Y = lib.qlora_linear_fwd(X, w, A, B, c.alpha)
-    Yref, _ = oracle.forward(c.X, c.oracle_weight(), c.A, c.B, c.alpha)
-    _check("Y decode", host(Y), Yref)
-    run_full_size_sampled(N, K, L["M_prefill"], L["r"], L["alpha"], w_std=L["w_std"], outliers=True,
-                          bwd=False, seed=4, rows=32)
-
-
-def test_qwen_gate_sampled():
-    q = synth.QWEN7B
-    N, K = q["linears"]["gate"]
-    say(f"qwen gate {N}x{K} M=4096 fwd+bwd")
-    run_full_size_sampled(N, K, q["M"], q["r"], q["alpha"], seed=5, rows=16)
-
-
-@pytest.mark.parametrize("name", ["gate", "down"])
-def test_70b_large_linears(name):
-    """The two largest 70B-layer linears: decode (every output checked) and the
-    M=4096 forward on sampled rows; the down projection has the longest
-    contraction (28672)."""
+@pytest.mark.parametrize("name", list(synth.L70B["linears"]))
+def test_70b_layer_linear(name):
+    """Every linear of the 70B-shaped layer (N(0, 0.015) weights, 0.1 % outliers
+    x10, r = 64): decode at M = 1 with every output checked, and the M = 4096
+    forward on sampled rows; codes bit-exact."""
     L = synth.L70B
     N, K = L["linears"][name]
-    say(f"70b {name} {N}x{K} M=1 and M=4096 fwd")
-    c = Case(N, K, 1, L["r"], L["alpha"], seed=6, w_std=L["w_std"], outliers=True)
-    w, X, A, B, _ = c.device()
-    Wh = c.oracle_weight()
-    Y = lib.qlora_linear_fwd(X, w, A, B, c.alpha)
-    Yref, _ = oracle.forward(c.X, Wh, c.A, c.B, c.alpha)
-    _check("Y decode", host(Y), Yref)
-    M = L["M_prefill"]
-    Xp = synth.to_bf16(synth.gaussian((M, K), 1.0, synth.SEED_X + 60))
-    sel = _sampled_rows(M, 16, 61)
-    Yp = lib.qlora_linear_fwd(Xp.to(dev()), w, A, B, c.alpha)
-    Yref, _ = oracle.forward(synth.bf16_values(Xp)[sel], Wh, c.A, c.B, c.alpha)
-    _check("Y prefill rows", host(Yp)[sel], Yref)
+    seed = 40 + list(L["linears"]).index(name)
+    say(f"70b {name} {N}x{K} M=1 fwd, every output")
+    c = Case(N, K, 1, L["r"], L["alpha"], seed=seed, w_std=L["w_std"], outliers=True)
+    run_fwd_bwd(c, bwd=False, check_codes=True)
+    say(f"70b {name} {N}x{K} M=4096 fwd, sampled rows")
+    cp = Case(N, K, L["M_prefill"], L["r"], L["alpha"], seed=seed, w_std=L["w_std"], outliers=True)
+    run_fwd_bwd(cp, bwd=False, rows=12, seed=seed)
+
+
+def test_70b_gate_decode_m8_full():
+    """M = 8 decode over four K-segments of the 70B-shaped gate projection,
+    every output."""
+    L = synth.L70B
+    N, K = L["linears"]["gate"]
+    say(f"70b gate {N}x{K} M=8 decode, every output")
+    run_fwd_bwd(Case(N, K, 8, L["r"], L["alpha"], seed=44, w_std=L["w_std"], outliers=True), bwd=False)

@@ -116,7 +116,30 @@ def test_linear_rejects_bad_arguments():
     w2 = _w(N=256, K=500)
     assert L.qlora_linear_fwd(vp(FAKE), 4, ctypes.byref(w2), vp(FAKE), vp(FAKE), 8, 16.0, vp(FAKE), vp(0),
                               vp(FAKE), big, vp(0)) == 2
-    bargs = lambda dA=FAKE, M=4: (vp(FAKE), vp(FAKE), M, ctypes.byref(w), vp(FAKE), vp(FAKE), 8, 16.0,
-                                  vp(FAKE), vp(dA), vp(FAKE), vp(FAKE), big, vp(0))
+    bargs = lambda dA=FAKE, M=4, H=0, wt=w: (vp(FAKE), vp(FAKE), vp(H), M, ctypes.byref(wt), vp(FAKE), vp(FAKE), 8,
+                                           16.0, vp(FAKE), vp(dA), vp(FAKE), vp(FAKE), big, vp(0))
     assert L.qlora_linear_bwd(*bargs(dA=0)) == 1
     assert L.qlora_linear_bwd(*bargs(M=-3)) == 2
+    assert L.qlora_linear_bwd(*bargs(H=FAKE + 2)) == 4          # H is read as fp32 words
+    assert L.qlora_linear_bwd(*bargs(wt=w2)) == 2
+
+
+def test_linear_rejects_codes_beyond_32bit_offsets():
+    """N*K/2 bytes of codes must be addressable with 32-bit offsets: the largest
+    accepted weight has N*K/2 = INT32_MAX rounded down to whole 64-blocks, one more
+    row of 64 is rejected, in the forward and the backward alike."""
+    L = lib.load()
+    vp = ctypes.c_void_p
+    big = 1 << 40
+    K = 1 << 16
+    ok_rows = (2 ** 31 - 1) * 2 // K // 64 * 64          # N*K/2 <= INT32_MAX
+    for N, want in ((ok_rows + 64, 2),):
+        w = _w(N=N, K=K)
+        assert L.qlora_linear_fwd(vp(FAKE), 4, ctypes.byref(w), vp(FAKE), vp(FAKE), 8, 16.0, vp(FAKE), vp(0),
+                                  vp(FAKE), big, vp(0)) == want
+        assert L.qlora_linear_bwd(vp(FAKE), vp(FAKE), vp(0), 4, ctypes.byref(w), vp(FAKE), vp(FAKE), 8, 16.0,
+                                  vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), big, vp(0)) == want
+    # the largest accepted size passes validation up to the workspace check
+    w = _w(N=ok_rows, K=K)
+    assert L.qlora_linear_fwd(vp(FAKE), 4, ctypes.byref(w), vp(FAKE), vp(FAKE), 8, 16.0, vp(FAKE), vp(0),
+                              vp(FAKE), 16, vp(0)) == 5
