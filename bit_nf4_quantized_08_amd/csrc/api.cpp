@@ -117,6 +117,34 @@ int qlora_linear_fwd(const void *X, int64_t M, const qn_nf4_weight *W, const voi
   return hip_status(qn::run_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
+int qlora_linear_fwd_noalloc(const void *X, int64_t M, const qn_nf4_weight *W, const void *A, const void *B,
+                             int64_t r, float alpha, void *Y, float *H_out, void *stream) {
+  int st = check_weight(W);
+  if (st != QN_OK) return st;
+  if (!X || !A || !B || !Y) return QN_ERR_NULL;
+  st = check_linear_shapes(M, W, r, alpha);
+  if (st != QN_OK) return st;
+  if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 16) || !aligned(Y, 16)) return QN_ERR_ALIGN;
+  if (H_out && !aligned(H_out, 4)) return QN_ERR_ALIGN;
+  const size_t need = qn::fwd_workspace(M, W->N, W->K, r);
+  if (need > (size_t)QN_NOALLOC_SCRATCH_BYTES) return QN_ERR_SCRATCH;
+  if (!qn::codec_tables_ok()) return QN_ERR_VALUE;
+  void *scratch = nullptr;
+  if (qn::noalloc_scratch(&scratch) != hipSuccess) return QN_ERR_HIP;
+  qn::FwdArgs a{};
+  a.X = static_cast<const uint16_t *>(X);
+  a.M = M; a.N = W->N; a.K = W->K; a.r = r;
+  a.codes = W->codes;
+  a.sc = qn::ScaleSrc{W->absmax, W->absmax_q, W->scale2};
+  a.A = static_cast<const uint16_t *>(A);
+  a.B = static_cast<const uint16_t *>(B);
+  a.s = alpha / (float)r;
+  a.Y = static_cast<uint16_t *>(Y);
+  a.H_out = H_out;
+  a.ws = scratch; a.ws_bytes = QN_NOALLOC_SCRATCH_BYTES;
+  return hip_status(qn::run_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
 int qlora_linear_bwd(const void *dY, const void *X, const float *H, int64_t M, const qn_nf4_weight *W,
                      const void *A, const void *B, int64_t r, float alpha, void *dX, void *dA, void *dB,
                      void *workspace, size_t ws_bytes, void *stream) {
@@ -159,6 +187,7 @@ const char *qn_status_string(int status) {
     case QN_ERR_WORKSPACE: return "workspace missing or too small";
     case QN_ERR_HIP: return "HIP launch error";
     case QN_ERR_VALUE: return "invalid scalar value";
+    case QN_ERR_SCRATCH: return "problem needs more scratch than the static buffer holds";
     default: return "unknown status";
   }
 }

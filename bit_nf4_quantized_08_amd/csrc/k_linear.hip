@@ -620,4 +620,41 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------- no-allocation forward
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops): the forward's workspace is this file-scope array,
+// one copy per device, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, once per device
+// with that device current, and is cached.  Nothing in the forward's workspace
+// needs to start at zero (every piece is written before it is read), so the
+// array is never cleared.  Calls on one device share it: two such calls that
+// overlap in time on one device (different streams or host threads without
+// ordering) race on it.
+static __device__ __align__(256) uint8_t scratch[QN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_ptr;
+}  // namespace
+
+hipError_t noalloc_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *ptr = it->second;
+    return hipSuccess;
+  }
+  void *p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  g_scratch_ptr[dev] = p;
+  *ptr = p;
+  return hipSuccess;
+}
+
 }  // namespace qn

@@ -151,6 +151,9 @@ struct FwdArgs {
 };
 size_t fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
 hipError_t run_fwd(const FwdArgs &a, hipStream_t s);
+// Device address of the current device's static scratch array (k_linear.hip),
+// looked up once per device.
+hipError_t noalloc_scratch(void **ptr);
 
 struct BwdArgs {
   const uint16_t *dY;    // bf16 [M,N]

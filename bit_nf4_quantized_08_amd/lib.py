@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libqlora_nf4.so")
 QN_OK = 0
 QN_F32, QN_BF16 = 0, 1
 QN_OP_FWD, QN_OP_BWD = 0, 1
+QN_ERR_SCRATCH = 8
+QN_NOALLOC_SCRATCH_BYTES = 16 << 20
 QN_BLOCK, QN_GROUP, QN_MAX_RANK = 64, 256, 64
 
 _lib = None
@@ -63,6 +65,7 @@ def load():
         "qlora_workspace_size": (ctypes.c_size_t, [i32, i64, i64, i64, i64]),
         "qlora_linear_fwd": (i32, [vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp,
                                    ctypes.c_size_t, vp]),
+        "qlora_linear_fwd_noalloc": (i32, [vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp]),
         "qlora_linear_bwd": (i32, [vp, vp, vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp,
                                    vp, vp, ctypes.c_size_t, vp]),
         "qn_status_string": (ctypes.c_char_p, [i32]),
@@ -80,7 +83,7 @@ def load():
 
 def exported_symbols():
     return ["qn_codebook", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_workspace_size",
-            "qlora_linear_fwd", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_trace_enable",
+            "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_trace_enable",
             "qn_trace_read"]
 
 
@@ -240,6 +243,28 @@ def qlora_linear_fwd(X, w: NF4Weight, A, B, alpha, want_H=False, use_double_quan
         _ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(H),
         _ptr(ws), ws.numel(), _stream()))
     return (Y, H) if want_H else Y
+
+
+def qlora_linear_fwd_noalloc(X, w: NF4Weight, A, B, alpha, Y, H=None, use_double_quant=True):
+    """qlora_linear_fwd without a workspace: the library's static scratch array
+    is the workspace.  Y (and H) are caller-provided; nothing is allocated."""
+    torch = _torch()
+    _need(X, "X", torch.bfloat16, 2)
+    _need(A, "A", torch.bfloat16, 2)
+    _need(B, "B", torch.bfloat16, 2)
+    _need(Y, "Y", torch.bfloat16, 2)
+    M, K = X.shape
+    r = A.shape[0]
+    if K != w.K or A.shape[1] != w.K or B.shape != (w.N, r) or Y.shape != (M, w.N):
+        raise ValueError("shape mismatch between X, W, A, B, Y")
+    if H is not None:
+        _need(H, "H", torch.float32, 2)
+        if H.shape != (M, r):
+            raise ValueError("H must be [M, r]")
+    st = w.struct(use_double_quant)
+    _check("qlora_linear_fwd_noalloc", load().qlora_linear_fwd_noalloc(
+        _ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(H), _stream()))
+    return Y
 
 
 def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_quant=True, out=None, ws=None,

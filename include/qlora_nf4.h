@@ -50,7 +50,9 @@ typedef enum {
   QN_ERR_ALIGN = 4,      /* a device pointer is not 16-byte aligned               */
   QN_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than qlora_workspace_size() */
   QN_ERR_HIP = 6,        /* the HIP runtime reported an error on launch           */
-  QN_ERR_VALUE = 7       /* a scalar argument is not finite                       */
+  QN_ERR_VALUE = 7,      /* a scalar argument is not finite                       */
+  QN_ERR_SCRATCH = 8     /* the no-allocation entry point's static scratch is too */
+                         /* small for this problem                                */
 } qn_status;
 
 typedef enum { QN_F32 = 0, QN_BF16 = 1 } qn_dtype;
@@ -147,6 +149,25 @@ int qlora_linear_fwd(const void *X, int64_t M, const qn_nf4_weight *W,
                      const void *A, const void *B, int64_t r, float alpha,
                      void *Y, float *H_out, void *workspace, size_t ws_bytes,
                      void *stream);
+
+/* No-allocation variant of qlora_linear_fwd, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results
+ * and shape rules as qlora_linear_fwd (identical kernels, bit-identical
+ * output), without the workspace arguments: the workspace is a static device
+ * array of QN_NOALLOC_SCRATCH_BYTES in the library, one per device, kept until
+ * the process ends.  The call uses the current device's copy (the device that
+ * is current must be the stream's).  Returns QN_ERR_SCRATCH, before anything is
+ * launched, when qlora_workspace_size(QN_OP_FWD, M, N, K, r) exceeds it (16 MiB
+ * covers decode, M <= 8, at every configured shape and the MFMA path up to
+ * M * r = 8 Mi).  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress); no call allocates or frees memory.  Calls that overlap
+ * in time on one device (different streams, or host threads without ordering)
+ * share the array and race: the caller serialises them. */
+#define QN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int qlora_linear_fwd_noalloc(const void *X, int64_t M, const qn_nf4_weight *W,
+                             const void *A, const void *B, int64_t r, float alpha,
+                             void *Y, float *H_out, void *stream);
 
 /* QLoRA linear backward: gradients reach the adapter only; the frozen base gets
  * none ([QE] "Name the one memory cost LoRA could not remove"; "Turn a LoRA
