@@ -184,6 +184,12 @@ class Layer:
         if quality:
             self.quality = {k: (v / sq_ref) ** 0.5 for k, v in sq_err.items()}
 
+    def groups(self, lib, M, partition):
+        """FwdGroup objects (one grouped call each) over the named linears."""
+        by = {it["name"]: it for it in self.items}
+        return [lib.FwdGroup([(by[n]["X"][M], by[n]["w"], by[n]["A"], by[n]["B"], self.alpha, by[n]["Y"][M], None)
+                              for n in part]) for part in partition]
+
     def fwd(self, lib, M, items=None, want_H=False):
         for it in (items or self.items):
             lib.qlora_linear_fwd(it["X"][M], it["w"], it["A"], it["B"], self.alpha, Y=it["Y"][M], ws=it["ws"][M],
@@ -334,9 +340,19 @@ def main():
     log("70B layer: quantising 7 weights")
     L = Layer(torch, lib, dev, L70B, R70, W70_STD, [M70_DEC, M70_PRE], seed=70, outliers=True, quality=True)
 
+    # Grouped calls in the order a layer's data allows: q, k, v read the same
+    # normalised hidden state; o reads the attention output; gate and up read
+    # the same normalised hidden state; down reads act(gate) * up.
+    dep = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    dec_groups = L.groups(lib, M70_DEC, dep)
+    pre_groups = L.groups(lib, M70_PRE, dep)
+    all7 = L.groups(lib, M70_PRE, [tuple(L70B)])
+
     def step():
-        L.fwd(lib, M70_DEC)
-        L.fwd(lib, M70_PRE)
+        for grp in dec_groups:
+            grp.run()
+        for grp in pre_groups:
+            grp.run()
 
     for _ in range(args.warmup):
         step()
@@ -358,9 +374,12 @@ def main():
     step_flops = L.flops(M70_DEC) + L.flops(M70_PRE)
     value = step_flops / (ms_step * 1e-3) / 1e12
 
-    # the two halves of the step alone
-    pre_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE))
-    dec_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_DEC))
+    # the two halves of the step alone, and the forward as 7 single calls and as
+    # one call over all 7 linears
+    pre_us = graph_time_us(torch, cap, lambda: [grp.run() for grp in pre_groups])
+    dec_us = graph_time_us(torch, cap, lambda: [grp.run() for grp in dec_groups])
+    pre_single_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE))
+    pre_all7_us = graph_time_us(torch, cap, lambda: all7[0].run())
     per_linear = {}
     for it in L.items:
         us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE, [it]))
@@ -393,8 +412,10 @@ def main():
                 "launches": len(gemm), "avg_ms": round(sum(gemm) / len(gemm), 5),
                 "launch_ms": [round(x, 5) for x in gemm],
                 "work_per_launch": gemm_flops // len(gemm),
-                "note": "one launch per linear (q, k, v, o, gate, up, down) at M = 4096; work = 2MNK + 2MrN "
-                        "per launch (the X A^T product runs in the low-rank kernel)"}
+                "launch_flops": [sum(2 * M70_PRE * L70B[n][0] * L70B[n][1] + 2 * M70_PRE * R70 * L70B[n][0] for n in part)
+                                 for part in dep],
+                "note": "grouped launches q,k,v | o | gate,up | down at M = 4096; work = 2MNK + 2MrN over "
+                        "the linears of each launch (the X A^T product runs in the low-rank kernel)"}
     gemv = kern.get("gemv", [])
     gemv_bytes = sum(nf4_bytes(it["N"], it["K"]) + 2 * it["K"] + 2 * it["N"] + 2 * R70 * it["K"] for it in L.items)
     gemv_roof = None
@@ -413,6 +434,8 @@ def main():
     flops_pre = sum(fwd_flops(M70_PRE, n_, k_, R70) for n_, k_ in L70B.values())
     stages = {"70b_layer": {"prefill_M4096_us": round(pre_us, 1),
                             "prefill_M4096_TFLOPs": round(flops_pre / pre_us / 1e6, 1),
+                            "prefill_M4096_single_calls_TFLOPs": round(flops_pre / pre_single_us / 1e6, 1),
+                            "prefill_M4096_one_call_all7_TFLOPs": round(flops_pre / pre_all7_us / 1e6, 1),
                             "decode_M1_us": round(dec_us, 2),
                             "decode_M1_weight_GBps": round(weight_bytes / dec_us / 1e3, 1),
                             "per_linear": per_linear,
@@ -583,8 +606,16 @@ def other_stages(torch, lib, dev, cap, log):
                                        "bwd_TFLOPs": round(bwd_flops(MQ, it["N"], it["K"], RQ) / bu / 1e6, 1)}
     fu = graph_time_us(torch, cap, lambda: Q.fwd(lib, MQ, want_H=True))
     bu = graph_time_us(torch, cap, lambda: Q.bwd(lib, MQ))
-    q.update(fwd_us=round(fu, 1), bwd_us=round(bu, 1), fwd_TFLOPs=round(Q.flops(MQ) / fu / 1e6, 1),
-             bwd_TFLOPs=round(Q.flops(MQ, "bwd") / bu / 1e6, 1))
+    qdep = Q.groups(lib, MQ, [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)])
+    qall = Q.groups(lib, MQ, [tuple(QWEN)])
+    gu = graph_time_us(torch, cap, lambda: [grp.run() for grp in qdep])
+    au = graph_time_us(torch, cap, lambda: qall[0].run())
+    q.update(fwd_single_calls_us=round(fu, 1), bwd_us=round(bu, 1),
+             fwd_single_calls_TFLOPs=round(Q.flops(MQ) / fu / 1e6, 1),
+             fwd_grouped_us=round(gu, 1), fwd_grouped_TFLOPs=round(Q.flops(MQ) / gu / 1e6, 1),
+             fwd_one_call_all7_TFLOPs=round(Q.flops(MQ) / au / 1e6, 1),
+             bwd_TFLOPs=round(Q.flops(MQ, "bwd") / bu / 1e6, 1),
+             note="grouped = q,k,v | o | gate,up | down, the calls a layer's data dependencies allow")
     st["qwen2.5_7b_layer_M4096"] = q
     del Q
     torch.cuda.empty_cache()

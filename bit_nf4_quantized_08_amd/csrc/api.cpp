@@ -117,6 +117,54 @@ int qlora_linear_fwd(const void *X, int64_t M, const qn_nf4_weight *W, const voi
   return hip_status(qn::run_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t qlora_workspace_size_grouped(int n, const qlora_fwd_problem *problems) {
+  if (n < 1 || n > QN_MAX_GROUP || !problems) return 0;
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    const size_t w = qlora_workspace_size(QN_OP_FWD, problems[i].M, problems[i].W.N, problems[i].W.K, problems[i].r);
+    if (w == 0) return 0;
+    total += w;   // each piece is a multiple of 256 bytes
+  }
+  return total;
+}
+
+int qlora_linear_fwd_grouped(int n, const qlora_fwd_problem *problems, void *workspace, size_t ws_bytes,
+                             void *stream) {
+  if (!problems) return QN_ERR_NULL;
+  if (n < 1 || n > QN_MAX_GROUP) return QN_ERR_SHAPE;
+  qn::FwdArgs args[QN_MAX_GROUP];
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const qlora_fwd_problem &p = problems[i];
+    int st = check_weight(&p.W);
+    if (st != QN_OK) return st;
+    if (!p.X || !p.A || !p.B || !p.Y) return QN_ERR_NULL;
+    st = check_linear_shapes(p.M, &p.W, p.r, p.alpha);
+    if (st != QN_OK) return st;
+    if (!aligned(p.X, 16) || !aligned(p.A, 16) || !aligned(p.B, 16) || !aligned(p.Y, 16)) return QN_ERR_ALIGN;
+    if (p.H_out && !aligned(p.H_out, 4)) return QN_ERR_ALIGN;
+    qn::FwdArgs &a = args[i];
+    a = qn::FwdArgs{};
+    a.X = static_cast<const uint16_t *>(p.X);
+    a.M = p.M; a.N = p.W.N; a.K = p.W.K; a.r = p.r;
+    a.codes = p.W.codes;
+    a.sc = qn::ScaleSrc{p.W.absmax, p.W.absmax_q, p.W.scale2};
+    a.A = static_cast<const uint16_t *>(p.A);
+    a.B = static_cast<const uint16_t *>(p.B);
+    a.s = p.alpha / (float)p.r;
+    a.Y = static_cast<uint16_t *>(p.Y);
+    a.H_out = p.H_out;
+    const size_t need = qn::fwd_workspace(p.M, p.W.N, p.W.K, p.r);
+    a.ws = workspace ? static_cast<char *>(workspace) + off : nullptr;
+    a.ws_bytes = need;
+    off += need;
+  }
+  if (!workspace || ws_bytes < off) return QN_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return QN_ERR_ALIGN;
+  if (!qn::codec_tables_ok()) return QN_ERR_VALUE;
+  return hip_status(qn::run_fwd_group(args, n, static_cast<hipStream_t>(stream)));
+}
+
 int qlora_linear_fwd_noalloc(const void *X, int64_t M, const qn_nf4_weight *W, const void *A, const void *B,
                              int64_t r, float alpha, void *Y, float *H_out, void *stream) {
   int st = check_weight(W);

@@ -508,6 +508,24 @@ size_t fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
   return c.off;
 }
 
+// Arguments of the forward's MFMA path: the low-rank product H = X A^T
+// (written unscaled to H_out, and as bf16(s H) to the workspace) and the tile
+// GEMM that takes bf16(s H) B^T as its extra contraction step.
+static void fwd_mfma_args(const FwdArgs &a, LowRankArgs &la, QGemmArgs &g) {
+  Carve c(a.ws);
+  const int64_t rp = align_up(a.r, 8);
+  uint16_t *sH = c.take<uint16_t>(a.M * rp);
+  la = LowRankArgs{};
+  la.L = a.X; la.ldl = a.K; la.M = a.M; la.Kc = a.K;
+  la.P = a.A; la.ldp = a.K; la.R = a.r; la.scale = a.s;
+  la.out_f32 = a.H_out; la.out_b = sH; la.ldb = rp; la.out_t = nullptr; la.Mp = a.M;
+  g = QGemmArgs{};
+  g.L = a.X; g.ldl = a.K; g.M = a.M; g.Nout = a.N; g.Kc = a.K;
+  g.codes = a.codes; g.absmax = a.sc.absmax; g.absmax_q = a.sc.absmax_q; g.scale2 = a.sc.scale2;
+  g.L2 = sH; g.ldl2 = rp; g.R2 = a.B; g.ldr2 = a.r; g.r = a.r;
+  g.out = a.Y; g.ldo = a.N;
+}
+
 hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
   Carve c(a.ws);
   if (a.M <= GEMV_MAX_M) {
@@ -535,21 +553,31 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
   }
   // MFMA path: H = X A^T (low-rank kernel) -> sH bf16 -> tile GEMM with the
   // adapter term as extra contraction steps.
-  const int64_t rp = align_up(a.r, 8);
-  uint16_t *sH = c.take<uint16_t>(a.M * rp);
-  {
-    LowRankArgs la{};
-    la.L = a.X; la.ldl = a.K; la.M = a.M; la.Kc = a.K;
-    la.P = a.A; la.ldp = a.K; la.R = a.r; la.scale = a.s;
-    la.out_f32 = a.H_out; la.out_b = sH; la.ldb = rp; la.out_t = nullptr; la.Mp = a.M;
-    QN_TRY(launch_lowrank(la, st));
-  }
-  QGemmArgs g{};
-  g.L = a.X; g.ldl = a.K; g.M = a.M; g.Nout = a.N; g.Kc = a.K;
-  g.codes = a.codes; g.absmax = a.sc.absmax; g.absmax_q = a.sc.absmax_q; g.scale2 = a.sc.scale2;
-  g.L2 = sH; g.ldl2 = rp; g.R2 = a.B; g.ldr2 = a.r; g.r = a.r;
-  g.out = a.Y; g.ldo = a.N;
+  LowRankArgs la;
+  QGemmArgs g;
+  fwd_mfma_args(a, la, g);
+  QN_TRY(launch_lowrank(la, st));
   return launch_qgemm_fwd(g, st);
+}
+
+hipError_t run_fwd_group(const FwdArgs *a, int n, hipStream_t st) {
+  LowRankArgs la[QN_MAX_GROUP];
+  QGemmArgs g[2][QN_MAX_GROUP];   // [double-quantised scales?][problem]
+  int nl = 0, ng[2] = {0, 0};
+  for (int i = 0; i < n; ++i) {
+    if (a[i].M <= GEMV_MAX_M) {
+      QN_TRY(run_fwd(a[i], st));
+      continue;
+    }
+    const int dq = a[i].sc.absmax_q != nullptr;
+    fwd_mfma_args(a[i], la[nl], g[dq][ng[dq]]);
+    ++nl;
+    ++ng[dq];
+  }
+  if (nl) QN_TRY(launch_lowrank_n(la, nl, st));
+  for (int dq = 0; dq < 2; ++dq)
+    if (ng[dq]) QN_TRY(launch_qgemm_fwd_group(g[dq], ng[dq], st));
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- backward

@@ -45,10 +45,14 @@ __host__ __device__ inline int64_t lowrank_rows(const LowRankArgs &a) {
   return a.out_t && a.Mp > a.M ? a.Mp : a.M;
 }
 
+struct LowRankGroup {
+  LowRankArgs p[QN_MAX_GROUP];
+};
+
 template <int RT>  // 16-column tiles of the output: R <= 16 * RT
-__global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankArgs a0, LowRankArgs a1) {
+__global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankGroup grp) {
   __shared__ float red[kWaves][ROWS][RT * 16];
-  const LowRankArgs &a = blockIdx.y ? a1 : a0;
+  const LowRankArgs a = grp.p[__builtin_amdgcn_readfirstlane((int)blockIdx.y)];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * ROWS;
@@ -129,16 +133,26 @@ __global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankArgs a0, LowRa
 
 }  // namespace
 
-hipError_t launch_lowrank2(const LowRankArgs &a, const LowRankArgs *b, hipStream_t st) {
-  const int64_t rows = std::max(lowrank_rows(a), b ? lowrank_rows(*b) : 0);
-  const int64_t R = std::max(a.R, b ? b->R : 0);
-  const dim3 grid((unsigned)((rows + ROWS - 1) / ROWS), b ? 2u : 1u);
-  const LowRankArgs &a1 = b ? *b : a;
+hipError_t launch_lowrank_n(const LowRankArgs *a, int n, hipStream_t st) {
+  if (n < 1 || n > QN_MAX_GROUP) return hipErrorInvalidValue;
+  LowRankGroup grp{};
+  int64_t rows = 0, R = 0;
+  for (int i = 0; i < n; ++i) {
+    grp.p[i] = a[i];
+    rows = std::max(rows, lowrank_rows(a[i]));
+    R = std::max(R, a[i].R);
+  }
+  const dim3 grid((unsigned)((rows + ROWS - 1) / ROWS), (unsigned)n);
   TraceScope tr(QN_TRACE_LOWRANK, st);
-  if (R <= 16) hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(kThreads), 0, st, a, a1);
-  else if (R <= 32) hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(kThreads), 0, st, a, a1);
-  else hipLaunchKernelGGL(lowrank_kernel<4>, grid, dim3(kThreads), 0, st, a, a1);
+  if (R <= 16) hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(kThreads), 0, st, grp);
+  else if (R <= 32) hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(kThreads), 0, st, grp);
+  else hipLaunchKernelGGL(lowrank_kernel<4>, grid, dim3(kThreads), 0, st, grp);
   return hipGetLastError();
+}
+
+hipError_t launch_lowrank2(const LowRankArgs &a, const LowRankArgs *b, hipStream_t st) {
+  const LowRankArgs two[2] = {a, b ? *b : a};
+  return launch_lowrank_n(two, b ? 2 : 1, st);
 }
 
 hipError_t launch_lowrank(const LowRankArgs &a, hipStream_t st) { return launch_lowrank2(a, nullptr, st); }

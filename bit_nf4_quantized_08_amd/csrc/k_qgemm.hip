@@ -369,7 +369,16 @@ __device__ __forceinline__ void lds_barrier() {
 // operands in registers instead of re-reading them one by one.
 template <bool KN, bool DQ, bool EPI_NK>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void qgemm_kernel(QGemmArgs a, Code16 cb) {
+void qgemm_kernel(QGemmGroup grp, Code16 cb) {
+  // The problem this workgroup belongs to (a grouped launch runs several
+  // independent products; see QGemmGroup) and its tile index within it.
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < QN_MAX_GROUP; ++i) gi += (i < grp.n && (int)blockIdx.x >= grp.start[i]) ? 1 : 0;
+  gi = __builtin_amdgcn_readfirstlane(gi);
+  const QGemmArgs a = grp.p[gi];
+  const int tile = (int)blockIdx.x - grp.start[gi];
+  if (tile >= a.tiles_m * a.tiles_n) return;   // padding of the problem's range to a multiple of 8
   // Separate arrays per stage: the compiler then tracks the direct-to-LDS
   // loads into each activation stage on their own and waits only for the
   // stage a fragment read touches.
@@ -386,7 +395,7 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
   }
 
   int tm, tn;
-  tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
+  tile_coords(tile, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool producer = wave >= 4;
@@ -662,45 +671,72 @@ void qgemm_kernel(QGemmArgs a, Code16 cb) {
 
 int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-template <bool KN, bool EPI_NK>
-hipError_t launch(const QGemmArgs &a0, hipStream_t st, int trace_kind) {
-  QGemmArgs a = a0;
+// Tiles, and the row-tile group size of the XCD-aware order: each XCD runs T/8
+// tiles; the group is chosen so that an XCD's share covers about as many
+// activation bytes (rows x Kc x 2) as weight bytes (columns x Kc / 2).
+bool plan(QGemmArgs &a) {
   // The adapter term is exactly one extra contraction step, and the producer
   // and MMA waves count their barriers on that: reject any other rank here.
-  if (a.r < 1 || a.r > BK || a.Kc < BK || a.Kc % BK != 0) return hipErrorInvalidValue;
+  if (a.r < 1 || a.r > BK || a.Kc < BK || a.Kc % BK != 0) return false;
   a.tiles_m = (int)cdiv(a.M, BM);
   a.tiles_n = (int)cdiv(a.Nout, BN);
-  // Row-tile group size: each XCD runs T/8 tiles; choose the group so that an
-  // XCD's share covers about as many activation bytes (rows x Kc x 2) as weight
-  // bytes (columns x Kc / 2).
-  {
-    const int T8 = std::max(1, a.tiles_m * a.tiles_n / 8);
-    int best = 1;
-    double best_cost = 1e300;
-    for (int g = 1; g <= a.tiles_m; ++g) {
-      const int cols = std::max(1, std::min(a.tiles_n, T8 / g));
-      const double cost = (double)g * BM * 2 + (double)cols * BN / 2;
-      if (cost < best_cost) { best_cost = cost; best = g; }
-    }
-    a.group_m = best;
+  const int T8 = std::max(1, a.tiles_m * a.tiles_n / 8);
+  int best = 1;
+  double best_cost = 1e300;
+  for (int g = 1; g <= a.tiles_m; ++g) {
+    const int cols = std::max(1, std::min(a.tiles_n, T8 / g));
+    const double cost = (double)g * BM * 2 + (double)cols * BN / 2;
+    if (cost < best_cost) { best_cost = cost; best = g; }
   }
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+  a.group_m = best;
+  return true;
+}
+
+// One launch over n problems.  Problems with the longest contraction (the
+// most work per tile) are dispatched first, so that short tiles fill in at
+// the end; each problem's workgroup range is rounded up to a multiple of 8 so
+// that the XCD-aware order within it holds (workgroups are dealt to the XCDs
+// round-robin by their global index).
+template <bool KN, bool EPI_NK>
+hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
+  if (n < 1 || n > QN_MAX_GROUP) return hipErrorInvalidValue;
+  QGemmGroup grp{};
+  int order[QN_MAX_GROUP];
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order, order + n, [&](int x, int y) { return in[x].Kc > in[y].Kc; });
+  const bool dq = in[0].absmax_q != nullptr;
+  int64_t total = 0;
+  for (int k = 0; k < n; ++k) {
+    QGemmArgs a = in[order[k]];
+    if ((a.absmax_q != nullptr) != dq || !plan(a)) return hipErrorInvalidValue;
+    grp.p[k] = a;
+    grp.start[k] = (int)total;
+    total += (int64_t)((a.tiles_m * a.tiles_n + 7) / 8) * 8;
+  }
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  for (int k = n; k <= QN_MAX_GROUP; ++k) grp.start[k] = (int)total;
+  grp.n = n;
+  const dim3 grid((unsigned)total);
   TraceScope tr(trace_kind, st);
-  if (a.absmax_q)
-    hipLaunchKernelGGL((qgemm_kernel<KN, true, EPI_NK>), grid, dim3(kThreads), 0, st, a, code16());
+  if (dq)
+    hipLaunchKernelGGL((qgemm_kernel<KN, true, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16());
   else
-    hipLaunchKernelGGL((qgemm_kernel<KN, false, EPI_NK>), grid, dim3(kThreads), 0, st, a, code16());
+    hipLaunchKernelGGL((qgemm_kernel<KN, false, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16());
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_qgemm_fwd(const QGemmArgs &a, hipStream_t st) {
-  return launch<false, true>(a, st, QN_TRACE_GEMM_FWD);
+  return launch<false, true>(&a, 1, st, QN_TRACE_GEMM_FWD);
+}
+
+hipError_t launch_qgemm_fwd_group(const QGemmArgs *a, int n, hipStream_t st) {
+  return launch<false, true>(a, n, st, QN_TRACE_GEMM_FWD);
 }
 
 hipError_t launch_qgemm_dx(const QGemmArgs &a, hipStream_t st) {
-  return launch<true, false>(a, st, QN_TRACE_GEMM_DX);
+  return launch<true, false>(&a, 1, st, QN_TRACE_GEMM_DX);
 }
 
 }  // namespace qn

@@ -95,6 +95,18 @@ struct QGemmArgs {
 };
 hipError_t launch_qgemm_fwd(const QGemmArgs &a, hipStream_t s);
 hipError_t launch_qgemm_dx(const QGemmArgs &a, hipStream_t s);
+// Several independent forward products in one launch (n <= QN_MAX_GROUP); the
+// problems must agree on the scale source (all double-quantised or none).
+hipError_t launch_qgemm_fwd_group(const QGemmArgs *a, int n, hipStream_t s);
+
+// Problems of one grouped launch, passed by value in the kernel arguments.
+// Workgroups [start[g], start[g+1]) run problem g; each range is a multiple of
+// 8 workgroups (the XCD count), the tail ones past the problem's tiles exit.
+struct QGemmGroup {
+  QGemmArgs p[QN_MAX_GROUP];
+  int start[QN_MAX_GROUP + 1];
+  int n;
+};
 
 // Low-rank product (k_lowrank.hip): C[M, R] = L[M, Kc] * P[R, Kc]^T, R <= 64,
 // Kc % 32 == 0.  Writes any of: out_f32 [M, R] (unscaled), out_b [M, ldb] =
@@ -115,6 +127,8 @@ struct LowRankArgs {
 hipError_t launch_lowrank(const LowRankArgs &a, hipStream_t s);
 // Two independent products with the same rank bucket in one launch (b may be null).
 hipError_t launch_lowrank2(const LowRankArgs &a, const LowRankArgs *b, hipStream_t s);
+// Up to QN_MAX_GROUP independent products in one launch (blockIdx.y picks one).
+hipError_t launch_lowrank_n(const LowRankArgs *a, int n, hipStream_t s);
 
 // Column-streaming reduction over rows (k_lowrank.hip): out = bf16(sum_m
 // Lt[j][m] * Q[m][c]) for j < R <= 64, as [R][Ncols] or transposed [Ncols][R].
@@ -151,6 +165,10 @@ struct FwdArgs {
 };
 size_t fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r);
 hipError_t run_fwd(const FwdArgs &a, hipStream_t s);
+// Several forwards: decode-path problems (M <= 8) as in run_fwd, the others
+// with one low-rank launch and one dequant-GEMM launch per scale source.  Each
+// problem's workspace is a[g].ws (carved by the caller).
+hipError_t run_fwd_group(const FwdArgs *a, int n, hipStream_t s);
 // Device address of the current device's static scratch array (k_linear.hip),
 // looked up once per device.
 hipError_t noalloc_scratch(void **ptr);

@@ -24,7 +24,7 @@ QN_F32, QN_BF16 = 0, 1
 QN_OP_FWD, QN_OP_BWD = 0, 1
 QN_ERR_SCRATCH = 8
 QN_NOALLOC_SCRATCH_BYTES = 16 << 20
-QN_BLOCK, QN_GROUP, QN_MAX_RANK = 64, 256, 64
+QN_BLOCK, QN_GROUP, QN_MAX_RANK, QN_MAX_GROUP = 64, 256, 64, 8
 
 _lib = None
 
@@ -43,6 +43,20 @@ class NF4WeightStruct(ctypes.Structure):
         ("scale2", ctypes.c_void_p),
         ("N", ctypes.c_int64),
         ("K", ctypes.c_int64),
+    ]
+
+
+class FwdProblemStruct(ctypes.Structure):
+    _fields_ = [
+        ("X", ctypes.c_void_p),
+        ("M", ctypes.c_int64),
+        ("W", NF4WeightStruct),
+        ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p),
+        ("r", ctypes.c_int64),
+        ("alpha", ctypes.c_float),
+        ("Y", ctypes.c_void_p),
+        ("H_out", ctypes.c_void_p),
     ]
 
 
@@ -65,6 +79,8 @@ def load():
         "qlora_workspace_size": (ctypes.c_size_t, [i32, i64, i64, i64, i64]),
         "qlora_linear_fwd": (i32, [vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp,
                                    ctypes.c_size_t, vp]),
+        "qlora_workspace_size_grouped": (ctypes.c_size_t, [i32, ctypes.POINTER(FwdProblemStruct)]),
+        "qlora_linear_fwd_grouped": (i32, [i32, ctypes.POINTER(FwdProblemStruct), vp, ctypes.c_size_t, vp]),
         "qlora_linear_fwd_noalloc": (i32, [vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp]),
         "qlora_linear_bwd": (i32, [vp, vp, vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp,
                                    vp, vp, ctypes.c_size_t, vp]),
@@ -83,7 +99,8 @@ def load():
 
 def exported_symbols():
     return ["qn_codebook", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_workspace_size",
-            "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_trace_enable",
+            "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_workspace_size_grouped",
+            "qlora_linear_fwd_grouped", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_trace_enable",
             "qn_trace_read"]
 
 
@@ -243,6 +260,51 @@ def qlora_linear_fwd(X, w: NF4Weight, A, B, alpha, want_H=False, use_double_quan
         _ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(H),
         _ptr(ws), ws.numel(), _stream()))
     return (Y, H) if want_H else Y
+
+
+class FwdGroup:
+    """A fixed set of independent forwards for qlora_linear_fwd_grouped.
+
+    ``problems`` is a list of (X, w, A, B, alpha, Y, H) with H optional (None);
+    the descriptor array and the workspace are built once, so that run() only
+    enqueues (and can be captured into a HIP graph)."""
+
+    def __init__(self, problems, use_double_quant=True, ws=None):
+        torch = _torch()
+        n = len(problems)
+        if not 1 <= n <= QN_MAX_GROUP:
+            raise ValueError(f"1 to {QN_MAX_GROUP} problems per group")
+        self._keep = problems
+        arr = (FwdProblemStruct * n)()
+        for i, (X, w, A, B, alpha, Y, H) in enumerate(problems):
+            _need(X, "X", torch.bfloat16, 2)
+            _need(A, "A", torch.bfloat16, 2)
+            _need(B, "B", torch.bfloat16, 2)
+            _need(Y, "Y", torch.bfloat16, 2)
+            M, K = X.shape
+            r = A.shape[0]
+            if K != w.K or A.shape[1] != w.K or B.shape != (w.N, r) or Y.shape != (M, w.N):
+                raise ValueError(f"problem {i}: shape mismatch between X, W, A, B, Y")
+            if H is not None:
+                _need(H, "H", torch.float32, 2)
+                if H.shape != (M, r):
+                    raise ValueError(f"problem {i}: H must be [M, r]")
+            arr[i] = FwdProblemStruct(X.data_ptr(), M, w.struct(use_double_quant), A.data_ptr(), B.data_ptr(), r,
+                                      float(alpha), Y.data_ptr(), H.data_ptr() if H is not None else 0)
+        self._arr, self._n = arr, n
+        nbytes = int(load().qlora_workspace_size_grouped(n, arr))
+        if nbytes == 0:
+            raise QNError("qlora_workspace_size_grouped", 2)
+        self.ws = ws if ws is not None else torch.empty(nbytes, dtype=torch.uint8, device=problems[0][0].device)
+
+    def run(self):
+        _check("qlora_linear_fwd_grouped", load().qlora_linear_fwd_grouped(
+            self._n, self._arr, _ptr(self.ws), self.ws.numel(), _stream()))
+
+
+def qlora_linear_fwd_grouped(problems, use_double_quant=True):
+    """Run independent forwards [(X, w, A, B, alpha, Y, H or None), ...] in one call."""
+    FwdGroup(problems, use_double_quant).run()
 
 
 def qlora_linear_fwd_noalloc(X, w: NF4Weight, A, B, alpha, Y, H=None, use_double_quant=True):

@@ -41,6 +41,7 @@ extern "C" {
 #define QN_BLOCK 64
 #define QN_GROUP 256
 #define QN_MAX_RANK 64   /* [LQ] "How LoRA Works": r is commonly 8 to 64 */
+#define QN_MAX_GROUP 8   /* linears per grouped launch (a layer has 7)   */
 
 typedef enum {
   QN_OK = 0,
@@ -149,6 +150,37 @@ int qlora_linear_fwd(const void *X, int64_t M, const qn_nf4_weight *W,
                      const void *A, const void *B, int64_t r, float alpha,
                      void *Y, float *H_out, void *workspace, size_t ws_bytes,
                      void *stream);
+
+/* Grouped forward: several independent QLoRA linear forwards in one call
+ * ([QE] "Turn a LoRA script into a QLoRA script with one config object":
+ * target_modules="all-linear" puts an adapter on every linear of a layer).
+ * Problem g computes exactly what qlora_linear_fwd computes with its fields
+ * (bit-identical results).  The problems with M > 8 share one low-rank launch
+ * and one dequant-GEMM launch per scale source (double-quantised or fp32
+ * scales) whose tiles cover all of them, the longest contractions first, so
+ * that linears too small to fill the GPU on their own (a layer's k and v
+ * projections) run beside the others; problems with M <= 8 run the decode
+ * path one after the other.  The problems must be independent: no output may
+ * overlap another problem's input or output.
+ *   n          1 <= n <= QN_MAX_GROUP.
+ *   problems   host array of n descriptors; each follows qlora_linear_fwd's
+ *              rules (QN_ERR_* of the first failing problem).
+ *   workspace  device, >= qlora_workspace_size_grouped(n, problems) bytes,
+ *              256-byte aligned. */
+typedef struct {
+  const void *X;        /* bf16 [M, K]                                 */
+  int64_t M;
+  qn_nf4_weight W;      /* [N, K]                                      */
+  const void *A;        /* bf16 [r, K]                                 */
+  const void *B;        /* bf16 [N, r]                                 */
+  int64_t r;
+  float alpha;
+  void *Y;              /* bf16 [M, N] out                             */
+  float *H_out;         /* fp32 [M, r] out, or NULL                    */
+} qlora_fwd_problem;
+size_t qlora_workspace_size_grouped(int n, const qlora_fwd_problem *problems);
+int qlora_linear_fwd_grouped(int n, const qlora_fwd_problem *problems, void *workspace,
+                             size_t ws_bytes, void *stream);
 
 /* No-allocation variant of qlora_linear_fwd, for callers that cannot allocate
  * device memory or pass a workspace (code under HIP graph capture, tight

@@ -1,0 +1,91 @@
+"""The grouped forward (qlora_linear_fwd_grouped) against single calls and the oracle.
+
+One call runs several independent linears: the MFMA-path problems share one
+low-rank launch and one dequant-GEMM launch per scale source, the decode-path
+ones run one after another.  Each problem's Y and H must be bit-identical to
+what qlora_linear_fwd gives for it alone (same kernels, same inputs), and, for
+a mixed group small enough for the fp64 oracle, within the parity bar of the
+oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_nf4_quantized_08_amd import lib, synth
+from tests.gpu_util import REL_FRO_TOL, dev, guarded, guards_intact, host, rel_fro, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _problem(N, K, M, r, seed, dq=True, w_std=0.02):
+    W = synth.gaussian((N, K), w_std, synth.SEED_W + seed)
+    w = lib.quantize_weight(to_dev(W))
+    X = synth.to_bf16(synth.gaussian((M, K), 1.0, synth.SEED_X + seed))
+    A = synth.to_bf16(synth.gaussian((r, K), 0.01, synth.SEED_A + seed))
+    B = synth.to_bf16(synth.gaussian((N, r), 0.01, synth.SEED_B + seed))
+    return dict(W=W, w=w, X=X, A=A, B=B, M=M, N=N, K=K, r=r, alpha=2.0 * r, dq=dq)
+
+
+def _run_grouped(probs):
+    outs = []
+    items = []
+    for p in probs:
+        nY = p["M"] * p["N"] * 2
+        fy, Y = guarded(nY, torch.bfloat16)
+        fh, H = guarded(p["M"] * p["r"] * 4, torch.float32)
+        Y, H = Y.view(p["M"], p["N"]), H.view(p["M"], p["r"])
+        outs.append((fy, nY, Y, fh, p["M"] * p["r"] * 4, H))
+        items.append((p["X"].to(dev()), p["w"], p["A"].to(dev()), p["B"].to(dev()), p["alpha"], Y, H))
+    dqs = {p["dq"] for p in probs}
+    assert len(dqs) == 1
+    lib.FwdGroup(items, use_double_quant=dqs.pop()).run()
+    torch.cuda.synchronize()
+    for fy, nY, Y, fh, nH, H in outs:
+        assert guards_intact(fy, nY), "Y guard band overwritten"
+        assert guards_intact(fh, nH), "H guard band overwritten"
+    return items, [(o[2], o[5]) for o in outs]
+
+
+def _check_against_single_calls(probs, items, outs):
+    for p, it, (Y, H) in zip(probs, items, outs):
+        Y1, H1 = lib.qlora_linear_fwd(it[0], it[1], it[2], it[3], it[4], want_H=True, use_double_quant=p["dq"])
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y1), f"Y of {p['N']}x{p['K']} M={p['M']} differs from the single call"
+        assert torch.equal(H, H1), f"H of {p['N']}x{p['K']} M={p['M']} differs from the single call"
+
+
+@pytest.mark.parametrize("dq", [True, False])
+def test_mixed_group_matches_single_calls_and_oracle(dq):
+    """Seven problems of different shapes, ranks and row counts (two on the
+    decode path), including ragged M and N not a multiple of the tile width."""
+    shapes = [(256, 512, 300, 16), (64, 512, 77, 8), (320, 1024, 130, 64), (192, 320, 9, 24), (512, 256, 1, 16),
+              (128, 2048, 8, 8), (448, 512, 513, 1)]
+    say(f"grouped mixed dq={dq}")
+    probs = [_problem(N, K, M, r, seed=200 + i, dq=dq) for i, (N, K, M, r) in enumerate(shapes)]
+    items, outs = _run_grouped(probs)
+    _check_against_single_calls(probs, items, outs)
+    for p, (Y, H) in zip(probs, outs):
+        pk, a, _ = oracle.quantize(p["W"])
+        scale = oracle.dq_absmax(*oracle.double_quant(a)) if dq else a
+        Wh = oracle.dequant_bf16_weight(pk, p["N"], p["K"], scale)
+        X, A, B = (synth.bf16_values(p[k]) for k in ("X", "A", "B"))
+        Yr, Hr = oracle.forward(X, Wh, A, B, p["alpha"])
+        assert rel_fro(host(Y), Yr) <= REL_FRO_TOL
+        assert rel_fro(host(H), Hr) <= REL_FRO_TOL
+
+
+@pytest.mark.parametrize("layer", ["qwen", "70b"])
+def test_layer_group_matches_single_calls(layer):
+    """All seven linears of the Qwen2.5-7B-shaped (M = 4096) and 70B-shaped
+    (M = 1024, to bound the test's memory and time) layers in one grouped
+    launch, bit-identical to seven single calls."""
+    if layer == "qwen":
+        cfg, M, r, std = synth.QWEN7B, 4096, 16, 0.02
+    else:
+        cfg, M, r, std = synth.L70B, 1024, 64, 0.015
+    say(f"grouped {layer} layer M={M}")
+    probs = [_problem(N, K, M, r, seed=300 + i, w_std=std) for i, (N, K) in enumerate(cfg["linears"].values())]
+    items, outs = _run_grouped(probs)
+    _check_against_single_calls(probs, items, outs)

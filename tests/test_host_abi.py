@@ -143,3 +143,22 @@ def test_linear_rejects_codes_beyond_32bit_offsets():
     w = _w(N=ok_rows, K=K)
     assert L.qlora_linear_fwd(vp(FAKE), 4, ctypes.byref(w), vp(FAKE), vp(FAKE), 8, 16.0, vp(FAKE), vp(0),
                               vp(FAKE), 16, vp(0)) == 5
+
+
+def test_grouped_forward_rejects_bad_arguments():
+    L = lib.load()
+    arr = (lib.FwdProblemStruct * 2)()
+    for i in range(2):
+        arr[i] = lib.FwdProblemStruct(FAKE, 64, _w(N=256, K=512), FAKE, FAKE, 16, 32.0, FAKE, 0)
+    vp = ctypes.c_void_p
+    assert L.qlora_linear_fwd_grouped(0, arr, vp(FAKE), 1 << 40, vp(0)) == 2
+    assert L.qlora_linear_fwd_grouped(9, arr, vp(FAKE), 1 << 40, vp(0)) == 2
+    assert L.qlora_linear_fwd_grouped(2, None, vp(FAKE), 1 << 40, vp(0)) == 1
+    assert L.qlora_linear_fwd_grouped(2, arr, vp(FAKE), 16, vp(0)) == 5
+    assert L.qlora_workspace_size_grouped(2, arr) == 2 * lib.workspace_size(lib.QN_OP_FWD, 64, 256, 512, 16)
+    arr[1].r = 65
+    assert L.qlora_linear_fwd_grouped(2, arr, vp(FAKE), 1 << 40, vp(0)) == 2
+    assert L.qlora_workspace_size_grouped(2, arr) == 0
+    arr[1].r = 16
+    arr[1].W.K = 500
+    assert L.qlora_linear_fwd_grouped(2, arr, vp(FAKE), 1 << 40, vp(0)) == 2
