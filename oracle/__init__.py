@@ -36,6 +36,10 @@ Parity status per function:
   dq.double_quant           pinned (closed forms, brute force).
   linear.forward / backward pinned (merged-weight identity, finite
                             differences, adjoint identity).
+  merge.merge               pinned (exact rational sum within its rounding
+                            bound, zero adapter reads back the dequantised
+                            weight, X W_m^T against the forward, re-quantising
+                            W_m loses the update as the pages say).
 """
 
 from .codebook import nf4_codebook, uniform_table, midpoints
@@ -43,6 +47,7 @@ from .bf16 import bf16_round, bf16_bits, bf16_from_bits
 from .nf4 import quantize, pack_codes, unpack_codes, dequant, block_absmax
 from .dq import double_quant, dq_absmax
 from .linear import forward, backward, dequant_bf16_weight
+from .merge import merge, adapter_delta
 from . import sizes
 
 __all__ = [
@@ -50,6 +55,6 @@ __all__ = [
     "bf16_round", "bf16_bits", "bf16_from_bits",
     "quantize", "pack_codes", "unpack_codes", "dequant", "block_absmax",
     "double_quant", "dq_absmax",
-    "forward", "backward", "dequant_bf16_weight",
+    "forward", "backward", "dequant_bf16_weight", "merge", "adapter_delta",
     "sizes",
 ]
