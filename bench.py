@@ -55,6 +55,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
 STAGE_REPS, STAGE_REPLAYS = 8, 5
 CSRC = os.path.join(ROOT, "bit_nf4_quantized_08_amd", "csrc")
 KERNEL_SOURCE = {
@@ -426,6 +427,19 @@ def main():
                      "launches": len(gemv), "avg_ms": round(sum(gemv) / len(gemv), 5),
                      "note": "the streaming kernel alone (its epilogue launch excluded); bytes = NF4 weights + "
                              "x + y + A read by the H blocks"}
+    # merge/export of the layer's adapters into bf16 weights (one call per linear)
+    mo = {it["name"]: torch.empty((it["N"], it["K"]), dtype=torch.bfloat16, device=dev) for it in L.items}
+    merge_us = graph_time_us(torch, cap, lambda: [lib.qlora_merge(it["w"], it["A"], it["B"], L.alpha, out=mo[it["name"]])
+                                                  for it in L.items], replays=3)
+    n_el = sum(it["N"] * it["K"] for it in L.items)
+    merge_bytes = sum(nf4_bytes(it["N"], it["K"]) + 2 * it["N"] * it["K"] + 2 * R70 * (it["N"] + it["K"])
+                      for it in L.items)
+    merge = {"us": round(merge_us, 1), "GBps": round(merge_bytes / merge_us / 1e3, 1),
+             "fma_TFLOPs": round(2 * R70 * n_el / merge_us / 1e6, 1),
+             "alu_frac": round(2 * R70 * n_el / merge_us / 1e6 / PEAK_FP32_TFLOPS, 4),
+             "note": "all 7 linears merged to bf16 (r = 64): r fused multiply-adds per weight, bound by the fp32 "
+                     "vector rate (157.3 TFLOP/s) rather than by its bytes"}
+    del mo
     quality = L.quality
     weight_bytes = L.weight_bytes()
     del L
@@ -440,6 +454,7 @@ def main():
                             "decode_M1_weight_GBps": round(weight_bytes / dec_us / 1e3, 1),
                             "per_linear": per_linear,
                             "dequant_rel_rmse": {k: round(v, 6) for k, v in quality.items()},
+                            "merge_export_bf16": merge,
                             "gemv_roofline": gemv_roof}}
     metrics = {"prefill_dequant_gemm_TFLOPs": round(flops_pre / pre_us / 1e6, 1),
                "decode_gemv_weight_GBps": round(weight_bytes / dec_us / 1e3, 1)}

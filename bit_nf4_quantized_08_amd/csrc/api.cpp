@@ -81,6 +81,20 @@ int nf4_dequant(const qn_nf4_weight *W, void *out, int out_dtype, void *stream) 
   return hip_status(qn::launch_dequant(*W, out, out_dtype == QN_BF16, static_cast<hipStream_t>(stream)));
 }
 
+int qlora_merge(const qn_nf4_weight *W, const void *A, const void *B, int64_t r, float alpha, void *out,
+                int out_dtype, void *stream) {
+  int st = check_weight(W);
+  if (st != QN_OK) return st;
+  if (!A || !B || !out) return QN_ERR_NULL;
+  if (out_dtype != QN_F32 && out_dtype != QN_BF16) return QN_ERR_DTYPE;
+  if (r < 1 || r > QN_MAX_RANK || W->K % QN_BLOCK != 0 || W->N > 2097120 || W->K > (1 << 25)) return QN_ERR_SHAPE;
+  if (!std::isfinite(alpha)) return QN_ERR_VALUE;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16)) return QN_ERR_ALIGN;
+  if (!qn::codec_tables_ok()) return QN_ERR_VALUE;
+  return hip_status(qn::launch_merge(*W, static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), r,
+                                     alpha, out, out_dtype == QN_BF16, static_cast<hipStream_t>(stream)));
+}
+
 size_t qlora_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t r) {
   if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QN_MAX_RANK) return 0;
   if (K % QN_BLOCK != 0 || N % QN_BLOCK != 0) return 0;

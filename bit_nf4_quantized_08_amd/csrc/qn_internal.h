@@ -55,6 +55,9 @@ hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, uint8_t *cod
 hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *absmax_q,
                                float *scale2, hipStream_t s);
 hipError_t launch_dequant(const qn_nf4_weight &W, void *out, int out_bf16, hipStream_t s);
+// Adapter merged into the dequantised base (k_merge.hip).  W.K % 64 == 0, 1 <= r <= 64.
+hipError_t launch_merge(const qn_nf4_weight &W, const uint16_t *A, const uint16_t *B, int64_t r, float alpha,
+                        void *out, int out_bf16, hipStream_t s);
 
 // Scale of block b: fl32(k_b * step_g) with double quantisation, else absmax[b].
 struct ScaleSrc {

@@ -76,6 +76,7 @@ def load():
         "nf4_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "nf4_double_quant": (i32, [vp, i64, vp, vp, vp]),
         "nf4_dequant": (i32, [ctypes.POINTER(NF4WeightStruct), vp, i32, vp]),
+        "qlora_merge": (i32, [ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, i32, vp]),
         "qlora_workspace_size": (ctypes.c_size_t, [i32, i64, i64, i64, i64]),
         "qlora_linear_fwd": (i32, [vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp,
                                    ctypes.c_size_t, vp]),
@@ -98,7 +99,7 @@ def load():
 
 
 def exported_symbols():
-    return ["qn_codebook", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_workspace_size",
+    return ["qn_codebook", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_merge", "qlora_workspace_size",
             "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_workspace_size_grouped",
             "qlora_linear_fwd_grouped", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_trace_enable",
             "qn_trace_read"]
@@ -214,6 +215,23 @@ def nf4_dequant(w: NF4Weight, out_dtype="bf16", use_double_quant=True, out=None)
         out = torch.empty((w.N, w.K), dtype=dt[1], device=w.codes.device)
     st = w.struct(use_double_quant)
     _check("nf4_dequant", load().nf4_dequant(ctypes.byref(st), _ptr(out), dt[0], _stream()))
+    return out
+
+
+def qlora_merge(w: NF4Weight, A, B, alpha, out_dtype="bf16", use_double_quant=True, out=None):
+    """The adapter merged into the dequantised base: [N, K] bf16 (or fp32)."""
+    torch = _torch()
+    _need(A, "A", torch.bfloat16, 2)
+    _need(B, "B", torch.bfloat16, 2)
+    r = A.shape[0]
+    if A.shape[1] != w.K or B.shape != (w.N, r):
+        raise ValueError("A must be [r, K] and B [N, r]")
+    dt = {"bf16": (QN_BF16, torch.bfloat16), "f32": (QN_F32, torch.float32)}[out_dtype]
+    if out is None:
+        out = torch.empty((w.N, w.K), dtype=dt[1], device=w.codes.device)
+    st = w.struct(use_double_quant)
+    _check("qlora_merge", load().qlora_merge(ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(out), dt[0],
+                                             _stream()))
     return out
 
 
@@ -364,7 +382,7 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_
 
 
 TRACE_KINDS = {1: "quantize", 2: "double_quant", 3: "dequant", 4: "gemv", 5: "gemm_fwd", 6: "gemm_dx",
-               7: "gemm_db", 8: "gemm_da", 9: "lowrank"}
+               7: "gemm_db", 8: "gemm_da", 9: "lowrank", 10: "merge"}
 
 
 def trace_enable(on=True):

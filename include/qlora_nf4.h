@@ -124,6 +124,24 @@ int nf4_double_quant(const float *absmax, int64_t nb, uint8_t *absmax_q,
  * Bit-exact with that definition.  out 16-byte aligned. */
 int nf4_dequant(const qn_nf4_weight *W, void *out, int out_dtype, void *stream);
 
+/* Merge a trained adapter into the frozen weight, for export ([LQ] "How LoRA
+ * Works": W + (alpha/r) B A, folded in once; its FAQ: a QLoRA adapter is merged
+ * into a dequantised full-precision copy of the base; [QE] "Ship the result,
+ * and plan for the merge before you need it": save a 16-bit checkpoint; merged
+ * into the 4-bit codes, an update smaller than the gap between rows would be
+ * lost).  With w = fl32(table[q] * A_b) (as nf4_dequant, fp32) and s = fl32(alpha/r):
+ *     acc = sum_j B[n][j] * A[j][k]   in fp32, j increasing, rounded each step
+ *     out[n][k] = fl32(w + fl32(s * acc))       (QN_F32), or its bf16 RNE (QN_BF16)
+ *   W    the weight [N, K]; K % 64 == 0, K <= 2^25, N <= 2097120.
+ *   A    device bf16 [r, K];  B device bf16 [N, r];  1 <= r <= QN_MAX_RANK.
+ *   out  device [N, K] of out_dtype, 16-byte aligned; A, B 16-byte aligned.
+ * Bit-exact with that definition whenever no product B[n][j] * A[j][k] falls
+ * into fp32's subnormal range (a product of two bf16 values is otherwise exact
+ * in fp32, and the kernel adds it with one fused multiply-add).  Asynchronous
+ * on `stream`; QN_ERR_* as elsewhere. */
+int qlora_merge(const qn_nf4_weight *W, const void *A, const void *B, int64_t r,
+                float alpha, void *out, int out_dtype, void *stream);
+
 /* Workspace size in bytes for op = QN_OP_FWD or QN_OP_BWD at the given shape.
  * Returns 0 for an invalid op or shape. */
 #define QN_OP_FWD 0
@@ -237,6 +255,7 @@ int qlora_linear_bwd(const void *dY, const void *X, const float *H, int64_t M,
                                  /* launch carries both)                         */
 #define QN_TRACE_GEMM_DA 8       /* reserved (dA shares the launch of kind 7)    */
 #define QN_TRACE_LOWRANK 9       /* X A^T or dY B low-rank product               */
+#define QN_TRACE_MERGE 10        /* qlora_merge kernel                           */
 int qn_trace_enable(int on);
 int qn_trace_read(int *kinds, float *ms, int cap);
 
