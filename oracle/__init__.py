@@ -33,6 +33,9 @@ Parity status per function:
                             the pages' third-party library: UNPINNED (that
                             table is not available here).
   nf4.quantize / dequant    pinned (pages' worked example, brute force).
+  codebook.fp4_table        pinned (the E2M1 values from the bit fields,
+                            brute-force nearest value, same storage, worse
+                            fit to bell-shaped weights than NF4).
   dq.double_quant           pinned (closed forms, brute force).
   linear.forward / backward pinned (merged-weight identity, finite
                             differences, adjoint identity).
@@ -42,16 +45,16 @@ Parity status per function:
                             W_m loses the update as the pages say).
 """
 
-from .codebook import nf4_codebook, uniform_table, midpoints
+from .codebook import nf4_codebook, uniform_table, midpoints, fp4_table, sorted_levels
 from .bf16 import bf16_round, bf16_bits, bf16_from_bits
-from .nf4 import quantize, pack_codes, unpack_codes, dequant, block_absmax
+from .nf4 import quantize, pack_codes, unpack_codes, dequant, block_absmax, table_of
 from .dq import double_quant, dq_absmax
 from .linear import forward, backward, dequant_bf16_weight
 from .merge import merge, adapter_delta
 from . import sizes
 
 __all__ = [
-    "nf4_codebook", "uniform_table", "midpoints",
+    "nf4_codebook", "uniform_table", "midpoints", "fp4_table", "sorted_levels", "table_of",
     "bf16_round", "bf16_bits", "bf16_from_bits",
     "quantize", "pack_codes", "unpack_codes", "dequant", "block_absmax",
     "double_quant", "dq_absmax",

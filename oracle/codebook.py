@@ -77,6 +77,48 @@ def uniform_table():
     return np.array([(2 * i - 15) / 15 for i in range(16)], dtype=np.float64).astype(np.float32)
 
 
+def fp4_table():
+    """The 4-bit floating-point table as float32[16], indexed by code.
+
+    "QLoRA Explained ...", "Turn a LoRA script into a QLoRA script with one
+    config object": the library's other 4-bit option is a small floating-point
+    layout, not shaped around how weights are distributed, at the same memory;
+    the codefinity course page: FP4 uses a floating-point-like structure.
+
+    READING (the pages give no layout): the plainest 4-bit float, one sign bit,
+    two exponent bits and one mantissa bit (E2M1, exponent bias 1): for code
+    c = s e1 e0 m, exponent field e = 2 e1 + e0,
+        e = 0:  (-1)^s * m/2                (0 and 0.5, the subnormals)
+        e > 0:  (-1)^s * 2^(e-1) * (1 + m/2)  (1, 1.5, 2, 3, 4, 6)
+    divided by the largest magnitude, 6, so that the table spans [-1, 1] like
+    the NF4 table (the block scale stretches it the same way); formed in fp64,
+    rounded to fp32.  Codes 0 and 8 are +0 and -0: fifteen distinct values.
+    """
+    vals = []
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        mag = (m / 2.0) if e == 0 else (2.0 ** (e - 1)) * (1.0 + m / 2.0)
+        vals.append((-1.0 if s else 1.0) * mag / 6.0)
+    return np.array(vals, dtype=np.float64).astype(np.float32)
+
+
+def sorted_levels(table):
+    """(distinct values ascending as float32, code of each value).
+
+    Where two codes hold the same value (+0 and -0 of the float table) the
+    smaller code is the one a quantiser writes."""
+    t = np.asarray(table, dtype=np.float32)
+    vals, codes = [], []
+    for c in np.argsort(t.astype(np.float64), kind="stable"):
+        v = float(t[c])
+        if vals and v == vals[-1]:
+            codes[-1] = min(codes[-1], int(c))
+            continue
+        vals.append(v)
+        codes.append(int(c))
+    return np.array(vals, dtype=np.float32), np.array(codes, dtype=np.uint8)
+
+
 def midpoints(table):
     """Exact midpoints between neighbouring rows, as fp64[15].
 

@@ -30,9 +30,9 @@ from .bf16 import bf16_round
 from .nf4 import dequant
 
 
-def dequant_bf16_weight(packed, N, K, scale, table=None):
+def dequant_bf16_weight(packed, N, K, scale, table=None, quant_type="nf4"):
     """W_hat = bf16(fl32(table[q] * A_b)) as fp32 values, [N, K]."""
-    w = dequant(packed, N * K, scale, table)
+    w = dequant(packed, N * K, scale, table, quant_type)
     return bf16_round(w).reshape(N, K)
 
 

@@ -48,9 +48,9 @@ def adapter_delta(A, B, alpha):
     return (s * acc).astype(np.float32)
 
 
-def merge(packed, N, K, scale, A, B, alpha, out="bf16", table=None):
+def merge(packed, N, K, scale, A, B, alpha, out="bf16", table=None, quant_type="nf4"):
     """The merged weight W_m [N, K]: fp32 values, bf16-rounded when out == "bf16"."""
-    w = dequant(packed, N * K, scale, table).reshape(N, K)
+    w = dequant(packed, N * K, scale, table, quant_type).reshape(N, K)
     m = (w + adapter_delta(A, B, alpha)).astype(np.float32)
     if out == "bf16":
         return bf16_round(m)

@@ -31,7 +31,7 @@ READINGS (the pages leave these open):
 
 import numpy as np
 
-from .codebook import midpoints, nf4_codebook
+from .codebook import fp4_table, midpoints, nf4_codebook, sorted_levels
 
 BLOCK = 64
 
@@ -111,28 +111,43 @@ def unpack_codes(packed, n):
     return out[:n]
 
 
-def quantize(w, table=None):
+def table_of(quant_type):
+    """The 16-entry table (by code) of a 4-bit type: "nf4" or "fp4"."""
+    if quant_type == "nf4":
+        return nf4_codebook()
+    if quant_type == "fp4":
+        return fp4_table()
+    raise ValueError("quant_type is 'nf4' or 'fp4'")
+
+
+def quantize(w, table=None, quant_type="nf4"):
     """Blockwise quantisation of a weight array.
+
+    ``table`` (16 values by code) overrides ``quant_type``.  The closest
+    distinct value of the table is found with ties to the lower value, then
+    written as its code (for a table that is sorted and distinct, like NF4, the
+    code is that value's rank).
 
     Returns (packed uint8[ceil(n/2)], absmax fp32[ceil(n/64)], codes uint8[n]).
     """
     if table is None:
-        table = nf4_codebook()
+        table = table_of(quant_type)
     flat = _flat_f32(w)
     absmax = block_absmax(flat)
     nrm = normalise(flat, absmax)
-    q = nearest_code(nrm, table)
+    levels, codes_of = sorted_levels(table)
+    q = codes_of[nearest_code(nrm, levels)]
     return pack_codes(q), absmax, q
 
 
-def dequant(packed, n, scale, table=None):
+def dequant(packed, n, scale, table=None, quant_type="nf4"):
     """w = fl32(table[q] * A_b) for each element; fp32[n].
 
     ``scale`` is the per-block fp32 A_b: the absmax itself, or its
     double-quantised reconstruction.
     """
     if table is None:
-        table = nf4_codebook()
+        table = table_of(quant_type)
     table = np.asarray(table, dtype=np.float32)
     q = unpack_codes(packed, n)
     A = np.asarray(scale, dtype=np.float32)[np.arange(n) // BLOCK]
