@@ -645,6 +645,13 @@ def other_stages(torch, lib, dev, cap, log):
     sw_out = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
 
     def round_trip():
+        # quantise with the double quantisation in the same launch, then dequantise
+        for j in range(16):
+            w = sw[j]
+            lib.quantize_4bit(tiles[j], "nf4", codes=w.codes, absmax=w.absmax, absmax_q=w.absmax_q, scale2=w.scale2)
+            lib.nf4_dequant(w, "bf16", out=sw_out)
+
+    def round_trip_3():
         for j in range(16):
             w = sw[j]
             lib.nf4_quantize(tiles[j], codes=w.codes, absmax=w.absmax)
@@ -652,26 +659,49 @@ def other_stages(torch, lib, dev, cap, log):
             lib.nf4_dequant(w, "bf16", out=sw_out)
 
     tile_us = graph_time_us(torch, cap, round_trip, calls=16)
-    q_us = graph_time_us(torch, cap, lambda: [lib.nf4_quantize(tiles[j], codes=sw[j].codes, absmax=sw[j].absmax)
-                                              for j in range(16)], calls=16)
-    nb_t = TILE // 64
-    q_bytes = 2 * TILE + TILE // 2 + 4 * nb_t
-    tile_bytes = q_bytes + (4 * nb_t + nb_t + 4 * (nb_t // 256)) + (TILE // 2 + nb_t + 4 * (nb_t // 256) + 2 * TILE)
-    # round-trip error over the 16 tiles (bf16 source vs bf16 dequantised)
+    # round-trip error over the 16 tiles (bf16 source vs bf16 dequantised), on
+    # the NF4 weights the round trip just wrote
     se = sr = 0.0
     for j in range(16):
         d = lib.nf4_dequant(sw[j], "bf16")
         se += float(((d.float() - tiles[j].float()).double() ** 2).sum())
         sr += float((tiles[j].double() ** 2).sum())
+    tile3_us = graph_time_us(torch, cap, round_trip_3, calls=16)
+    q_us = graph_time_us(torch, cap, lambda: [lib.nf4_quantize(tiles[j], codes=sw[j].codes, absmax=sw[j].absmax)
+                                              for j in range(16)], calls=16)
+    qdq_us = graph_time_us(torch, cap, lambda: [lib.quantize_4bit(tiles[j], "nf4", codes=sw[j].codes,
+                                                                  absmax=sw[j].absmax, absmax_q=sw[j].absmax_q,
+                                                                  scale2=sw[j].scale2) for j in range(16)], calls=16)
+    fw = [lib.quantize_4bit(tiles[j], "fp4") for j in range(16)]      # own buffers, FP4 codes
+    fq_us = graph_time_us(torch, cap, lambda: [lib.quantize_4bit(tiles[j], "fp4", codes=fw[j].codes,
+                                                                 absmax=fw[j].absmax, absmax_q=fw[j].absmax_q,
+                                                                 scale2=fw[j].scale2) for j in range(16)], calls=16)
+    del fw
+    dq_us = graph_time_us(torch, cap, lambda: [lib.nf4_double_quant(sw[j].absmax, absmax_q=sw[j].absmax_q,
+                                                                    scale2=sw[j].scale2) for j in range(16)], calls=16)
+    nb_t = TILE // 64
+    q_bytes = 2 * TILE + TILE // 2 + 4 * nb_t
+    dq_bytes = 4 * nb_t + nb_t + 4 * (nb_t // 256)
+    qdq_bytes = q_bytes + nb_t + 4 * (nb_t // 256)          # quantise writes the 8-bit scales and steps too
+    deq_bytes = TILE // 2 + nb_t + 4 * (nb_t // 256) + 2 * TILE
+    tile_bytes = qdq_bytes + deq_bytes
     st["bulk_round_trip_bf16_tiles"] = {
         "tile_round_trip_us": round(tile_us, 2),
         "round_trip_GBps": round(tile_bytes / tile_us / 1e3, 1),
+        "tile_round_trip_3_launches_us": round(tile3_us, 2),
         "quantize_us": round(q_us, 2),
         "quantize_GBps": round(q_bytes / q_us / 1e3, 1),
+        "quantize_with_double_quant_us": round(qdq_us, 2),
+        "quantize_with_double_quant_GBps": round(qdq_bytes / qdq_us / 1e3, 1),
+        "fp4_quantize_with_double_quant_GBps": round(qdq_bytes / fq_us / 1e3, 1),
+        "double_quant_alone_us": round(dq_us, 2),
+        "double_quant_alone_GBps": round(dq_bytes / dq_us / 1e3, 1),
         "sweep_7.62e9_weights_ms": round(SWEEP_WEIGHTS / TILE * tile_us * 1e-3, 2),
         "stored_bits_per_param": round((TILE // 2 + nb_t + 4 * (nb_t // 256)) * 8 / TILE, 6),
         "round_trip_rel_rmse": round((se / sr) ** 0.5, 5),
-        "note": "16 distinct tiles (537 MB of bf16 source) stand in for the 454-tile stream; sweep time = per-tile "
+        "note": "16 distinct tiles (537 MB of bf16 source) stand in for the 454-tile stream; the round trip is "
+                "qn_quantize_4bit with the double quantisation in the same launch, then nf4_dequant to bf16 "
+                "(the 3-launch figure runs nf4_quantize, nf4_double_quant, nf4_dequant); sweep time = per-tile "
                 "time x 7.62e9 / 4096^2",
     }
     del tiles, sw, sw_out

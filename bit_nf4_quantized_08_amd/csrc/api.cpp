@@ -15,6 +15,7 @@ constexpr int64_t kMaxElems = (int64_t)1 << 40;  // far above any HBM size; guar
 
 int check_weight(const qn_nf4_weight *W) {
   if (!W || !W->codes) return QN_ERR_NULL;
+  if (W->quant_type != QN_NF4 && W->quant_type != QN_FP4) return QN_ERR_DTYPE;
   if (W->N <= 0 || W->K <= 0 || W->N > kMaxElems / W->K) return QN_ERR_SHAPE;
   if (W->absmax_q) {
     if (!W->scale2) return QN_ERR_NULL;
@@ -52,15 +53,31 @@ int qn_codebook(float out[16]) {
   return QN_OK;
 }
 
-int nf4_quantize(const void *W, int w_dtype, int64_t N, int64_t K, uint8_t *codes, float *absmax,
-                 void *stream) {
+int qn_table(int quant_type, float out[16]) {
+  if (!out) return QN_ERR_NULL;
+  if (quant_type != QN_NF4 && quant_type != QN_FP4) return QN_ERR_DTYPE;
+  if (!qn::codec_tables_ok()) return QN_ERR_VALUE;
+  std::memcpy(out, qn::codec_tables(quant_type).code, 16 * sizeof(float));
+  return QN_OK;
+}
+
+int qn_quantize_4bit(const void *W, int w_dtype, int64_t N, int64_t K, int quant_type, uint8_t *codes,
+                     float *absmax, uint8_t *absmax_q, float *scale2, void *stream) {
   if (!W || !codes || !absmax) return QN_ERR_NULL;
+  if ((absmax_q == nullptr) != (scale2 == nullptr)) return QN_ERR_NULL;
   if (w_dtype != QN_F32 && w_dtype != QN_BF16) return QN_ERR_DTYPE;
+  if (quant_type != QN_NF4 && quant_type != QN_FP4) return QN_ERR_DTYPE;
   if (N <= 0 || K <= 0 || N > kMaxElems / K) return QN_ERR_SHAPE;
   if (!aligned(W, 16) || !aligned(codes, 8) || !aligned(absmax, 4)) return QN_ERR_ALIGN;
+  if (absmax_q && (!aligned(absmax_q, 4) || !aligned(scale2, 4))) return QN_ERR_ALIGN;
   if (!qn::codec_tables_ok()) return QN_ERR_VALUE;
-  return hip_status(qn::launch_quantize(W, w_dtype == QN_BF16, N * K, codes, absmax,
+  return hip_status(qn::launch_quantize(W, w_dtype == QN_BF16, N * K, quant_type, codes, absmax, absmax_q, scale2,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int nf4_quantize(const void *W, int w_dtype, int64_t N, int64_t K, uint8_t *codes, float *absmax,
+                 void *stream) {
+  return qn_quantize_4bit(W, w_dtype, N, K, QN_NF4, codes, absmax, nullptr, nullptr, stream);
 }
 
 int nf4_double_quant(const float *absmax, int64_t nb, uint8_t *absmax_q, float *scale2, void *stream) {
@@ -121,7 +138,7 @@ int qlora_linear_fwd(const void *X, int64_t M, const qn_nf4_weight *W, const voi
   a.X = static_cast<const uint16_t *>(X);
   a.M = M; a.N = W->N; a.K = W->K; a.r = r;
   a.codes = W->codes;
-  a.sc = qn::ScaleSrc{W->absmax, W->absmax_q, W->scale2};
+  a.sc = qn::ScaleSrc{W->absmax, W->absmax_q, W->scale2, W->quant_type};
   a.A = static_cast<const uint16_t *>(A);
   a.B = static_cast<const uint16_t *>(B);
   a.s = alpha / (float)r;
@@ -162,7 +179,7 @@ int qlora_linear_fwd_grouped(int n, const qlora_fwd_problem *problems, void *wor
     a.X = static_cast<const uint16_t *>(p.X);
     a.M = p.M; a.N = p.W.N; a.K = p.W.K; a.r = p.r;
     a.codes = p.W.codes;
-    a.sc = qn::ScaleSrc{p.W.absmax, p.W.absmax_q, p.W.scale2};
+    a.sc = qn::ScaleSrc{p.W.absmax, p.W.absmax_q, p.W.scale2, p.W.quant_type};
     a.A = static_cast<const uint16_t *>(p.A);
     a.B = static_cast<const uint16_t *>(p.B);
     a.s = p.alpha / (float)p.r;
@@ -197,7 +214,7 @@ int qlora_linear_fwd_noalloc(const void *X, int64_t M, const qn_nf4_weight *W, c
   a.X = static_cast<const uint16_t *>(X);
   a.M = M; a.N = W->N; a.K = W->K; a.r = r;
   a.codes = W->codes;
-  a.sc = qn::ScaleSrc{W->absmax, W->absmax_q, W->scale2};
+  a.sc = qn::ScaleSrc{W->absmax, W->absmax_q, W->scale2, W->quant_type};
   a.A = static_cast<const uint16_t *>(A);
   a.B = static_cast<const uint16_t *>(B);
   a.s = alpha / (float)r;
@@ -228,7 +245,7 @@ int qlora_linear_bwd(const void *dY, const void *X, const float *H, int64_t M, c
   a.H = H;
   a.M = M; a.N = W->N; a.K = W->K; a.r = r;
   a.codes = W->codes;
-  a.sc = qn::ScaleSrc{W->absmax, W->absmax_q, W->scale2};
+  a.sc = qn::ScaleSrc{W->absmax, W->absmax_q, W->scale2, W->quant_type};
   a.A = static_cast<const uint16_t *>(A);
   a.B = static_cast<const uint16_t *>(B);
   a.s = alpha / (float)r;

@@ -17,6 +17,7 @@
 // changes z.  Accuracy is that of erfc (about 1 ulp of fp64), far finer than
 // the fp32 rounding that follows.
 
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
 #include <cstring>
@@ -62,10 +63,69 @@ float next_f32_above(double m) {
   return std::nextafterf(f, INFINITY);
 }
 
-CodecTables g_tables;
+CodecTables g_tables[2];
 double g_rows64[16];
 std::once_flag g_once;
 bool g_ok = true;
+
+// The 4-bit float of the second table: sign, two exponent bits, one mantissa
+// bit (exponent bias 1), divided by the largest magnitude 6 so that the table
+// spans [-1, 1].  Codes 0 and 8 are +0 and -0.
+double fp4_value(int c) {
+  const int s = c >> 3, e = (c >> 1) & 3, m = c & 1;
+  const double mag = e == 0 ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+  return (s ? -mag : mag) / 6.0;
+}
+
+// Decision table of one 16-entry table (values by code): the distinct values
+// ascending (a repeated value keeps its smaller code); threshold i is the
+// smallest fp32 strictly above the exact midpoint of levels i and i+1, so an
+// fp32 value equal to a representable midpoint stays with the lower level.
+// Buckets of width 1/16 over [-1, 1] each hold at most one threshold:
+// base[b] = levels below the bucket, thr[b] = its threshold (or +inf),
+// lohi[b] = code of level base[b] | code of level base[b] + 1 << 8.  The
+// kernel's bucket index floor(16 n + 16) can only come out one too high, for an
+// n within a few 1e-8 below a bucket edge, so no threshold may lie just below
+// an edge (checked).
+void build_decisions(CodecTables &t) {
+  int order[16];
+  for (int i = 0; i < 16; ++i) order[i] = i;
+  std::sort(order, order + 16, [&](int x, int y) {
+    return t.code[x] < t.code[y] || (t.code[x] == t.code[y] && x < y);
+  });
+  float lev[16];
+  uint32_t lcode[16];
+  int L = 0;
+  for (int k = 0; k < 16; ++k) {
+    const int c = order[k];
+    if (L > 0 && t.code[c] == lev[L - 1]) continue;   // same value: the smaller code was taken
+    lev[L] = t.code[c];
+    lcode[L] = (uint32_t)c;
+    ++L;
+  }
+  float T[15];
+  for (int i = 0; i + 1 < L; ++i) T[i] = next_f32_above(((double)lev[i] + (double)lev[i + 1]) / 2.0);
+  for (int b = 0; b < 32; ++b) {
+    const double lo = b / 16.0 - 1.0, hi = (b + 1) / 16.0 - 1.0;
+    uint32_t below = 0;
+    float inside = INFINITY;
+    int n_inside = 0;
+    for (int i = 0; i + 1 < L; ++i) {
+      if ((double)T[i] < lo) ++below;
+      else if ((double)T[i] < hi) { inside = T[i]; ++n_inside; }
+    }
+    if (n_inside > 1) g_ok = false;
+    t.base[b] = below;
+    t.thr[b] = inside;
+    const uint32_t c_lo = lcode[below], c_hi = lcode[below + 1 < (uint32_t)L ? below + 1 : below];
+    t.lohi[b] = c_lo | (c_hi << 8);
+  }
+  for (int i = 0; i + 1 < L; ++i) {
+    const double u = ((double)T[i] + 1.0) * 16.0;
+    const double to_edge = (std::ceil(u) - u) / 16.0;   // distance up to the next edge
+    if (to_edge > 0.0 && to_edge < 1e-6) g_ok = false;
+  }
+}
 
 void build() {
   const double delta = (1.0 / 30.0 + 1.0 / 32.0) / 2.0;  // 31/960
@@ -81,59 +141,39 @@ void build() {
   }
   g_rows64[0] = -1.0;
   g_rows64[15] = 1.0;
-  for (int i = 0; i < 16; ++i) g_tables.code[i] = (float)g_rows64[i];
-
-  // Decision thresholds: the row index of n is #{i : n >= T_i}, T_i being the
-  // smallest fp32 above the exact midpoint of rows i and i+1 (an fp32 n equal
-  // to a representable midpoint stays with the lower row).
-  float T[15];
-  for (int i = 0; i < 15; ++i) {
-    double m = ((double)g_tables.code[i] + (double)g_tables.code[i + 1]) / 2.0;
-    T[i] = next_f32_above(m);
-  }
-  // Buckets of width 1/16 over [-1, 1].
+  for (int i = 0; i < 16; ++i) g_tables[QN_NF4].code[i] = (float)g_rows64[i];
+  for (int i = 0; i < 16; ++i) g_tables[QN_FP4].code[i] = (float)fp4_value(i);
+  build_decisions(g_tables[QN_NF4]);
+  build_decisions(g_tables[QN_FP4]);
+  // The NF4 rows are distinct and ascending: the code of a level is its rank,
+  // which the quantiser's NF4 path relies on.
   for (int b = 0; b < 32; ++b) {
-    double lo = b / 16.0 - 1.0, hi = (b + 1) / 16.0 - 1.0;
-    uint32_t below = 0;
-    float inside = INFINITY;
-    int n_inside = 0;
-    for (int i = 0; i < 15; ++i) {
-      if ((double)T[i] < lo) ++below;
-      else if ((double)T[i] < hi) { inside = T[i]; ++n_inside; }
-    }
-    if (n_inside > 1) g_ok = false;
-    g_tables.base[b] = below;
-    g_tables.thr[b] = inside;
-  }
-  for (int i = 0; i < 15; ++i) {
-    double t = ((double)T[i] + 1.0) * 16.0;
-    double frac = t - std::floor(t);
-    double dist = std::fmin(frac, 1.0 - frac) / 16.0;
-    if (dist < 1e-4) g_ok = false;
+    const uint32_t lo = g_tables[QN_NF4].lohi[b] & 0xFF;
+    if (lo != g_tables[QN_NF4].base[b]) g_ok = false;
   }
 }
 
 }  // namespace
 
-const CodecTables &codec_tables() {
+const CodecTables &codec_tables(int qtype) {
   std::call_once(g_once, build);
-  return g_tables;
+  return g_tables[qtype == QN_FP4 ? QN_FP4 : QN_NF4];
 }
 
 bool codec_tables_ok() {
-  codec_tables();
+  codec_tables(QN_NF4);
   return g_ok;
 }
 
-Code16 code16() {
+Code16 code16(int qtype) {
   Code16 c;
-  const CodecTables &t = codec_tables();
+  const CodecTables &t = codec_tables(qtype);
   for (int i = 0; i < 16; ++i) c.v[i] = t.code[i];
   return c;
 }
 
 void nf4_rows_f64(double out[16]) {
-  codec_tables();
+  codec_tables(QN_NF4);
   std::memcpy(out, g_rows64, sizeof(g_rows64));
 }
 

@@ -522,6 +522,7 @@ static void fwd_mfma_args(const FwdArgs &a, LowRankArgs &la, QGemmArgs &g) {
   g = QGemmArgs{};
   g.L = a.X; g.ldl = a.K; g.M = a.M; g.Nout = a.N; g.Kc = a.K;
   g.codes = a.codes; g.absmax = a.sc.absmax; g.absmax_q = a.sc.absmax_q; g.scale2 = a.sc.scale2;
+  g.qtype = a.sc.qtype;
   g.L2 = sH; g.ldl2 = rp; g.R2 = a.B; g.ldr2 = a.r; g.r = a.r;
   g.out = a.Y; g.ldo = a.N;
 }
@@ -539,7 +540,7 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
     GemvArgs ga{a.X, a.M, a.N, a.K, a.codes, a.sc, a.A, a.r, y_part, h_part, p.kps, p.splits, p.row_waves,
                 h_blocks, p.hsplits, p.hkps};
     dim3 grid((unsigned)(h_blocks + p.row_wgs));
-    const Code16 cb = code16();
+    const Code16 cb = code16(a.sc.qtype);
     {
       // The trace brackets the streaming kernel alone, not the epilogue.
       TraceScope tr(QN_TRACE_GEMV, st);
@@ -562,21 +563,21 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
 
 hipError_t run_fwd_group(const FwdArgs *a, int n, hipStream_t st) {
   LowRankArgs la[QN_MAX_GROUP];
-  QGemmArgs g[2][QN_MAX_GROUP];   // [double-quantised scales?][problem]
-  int nl = 0, ng[2] = {0, 0};
+  QGemmArgs g[4][QN_MAX_GROUP];   // [2 * (4-bit type) + (double-quantised scales?)][problem]
+  int nl = 0, ng[4] = {0, 0, 0, 0};
   for (int i = 0; i < n; ++i) {
     if (a[i].M <= GEMV_MAX_M) {
       QN_TRY(run_fwd(a[i], st));
       continue;
     }
-    const int dq = a[i].sc.absmax_q != nullptr;
-    fwd_mfma_args(a[i], la[nl], g[dq][ng[dq]]);
+    const int kind = 2 * (a[i].sc.qtype == QN_FP4) + (a[i].sc.absmax_q != nullptr);
+    fwd_mfma_args(a[i], la[nl], g[kind][ng[kind]]);
     ++nl;
-    ++ng[dq];
+    ++ng[kind];
   }
   if (nl) QN_TRY(launch_lowrank_n(la, nl, st));
-  for (int dq = 0; dq < 2; ++dq)
-    if (ng[dq]) QN_TRY(launch_qgemm_fwd_group(g[dq], ng[dq], st));
+  for (int kind = 0; kind < 4; ++kind)
+    if (ng[kind]) QN_TRY(launch_qgemm_fwd_group(g[kind], ng[kind], st));
   return hipSuccess;
 }
 
@@ -641,6 +642,7 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
     QGemmArgs g{};
     g.L = a.dY; g.ldl = a.N; g.M = a.M; g.Nout = a.K; g.Kc = a.N;
     g.codes = a.codes; g.absmax = a.sc.absmax; g.absmax_q = a.sc.absmax_q; g.scale2 = a.sc.scale2;
+    g.qtype = a.sc.qtype;
     g.L2 = dHb; g.ldl2 = rp; g.R2 = a.A; g.ldr2 = a.K; g.r = a.r;
     g.out = a.dX; g.ldo = a.K;
     QN_TRY(launch_qgemm_dx(g, st));

@@ -141,9 +141,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a, Code16 cb)
 
 hipError_t launch_merge(const qn_nf4_weight &W, const uint16_t *A, const uint16_t *B, int64_t r, float alpha,
                         void *out, int out_bf16, hipStream_t st) {
-  MergeArgs a{W.codes, ScaleSrc{W.absmax, W.absmax_q, W.scale2}, W.N, W.K, A, B, r, alpha / (float)r, out};
+  MergeArgs a{W.codes, ScaleSrc{W.absmax, W.absmax_q, W.scale2, W.quant_type}, W.N, W.K, A, B, r, alpha / (float)r, out};
   const dim3 grid((unsigned)((W.K + COLS - 1) / COLS), (unsigned)((W.N + ROWS - 1) / ROWS));
-  const Code16 cb = code16();
+  const Code16 cb = code16(W.quant_type);
   const bool dq = W.absmax_q != nullptr;
   TraceScope tr(QN_TRACE_MERGE, st);
   if (out_bf16) {

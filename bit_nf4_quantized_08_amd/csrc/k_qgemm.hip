@@ -708,7 +708,7 @@ hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
   int64_t total = 0;
   for (int k = 0; k < n; ++k) {
     QGemmArgs a = in[order[k]];
-    if ((a.absmax_q != nullptr) != dq || !plan(a)) return hipErrorInvalidValue;
+    if ((a.absmax_q != nullptr) != dq || a.qtype != in[0].qtype || !plan(a)) return hipErrorInvalidValue;
     grp.p[k] = a;
     grp.start[k] = (int)total;
     total += (int64_t)((a.tiles_m * a.tiles_n + 7) / 8) * 8;
@@ -719,9 +719,9 @@ hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
   const dim3 grid((unsigned)total);
   TraceScope tr(trace_kind, st);
   if (dq)
-    hipLaunchKernelGGL((qgemm_kernel<KN, true, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16());
+    hipLaunchKernelGGL((qgemm_kernel<KN, true, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16(in[0].qtype));
   else
-    hipLaunchKernelGGL((qgemm_kernel<KN, false, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16());
+    hipLaunchKernelGGL((qgemm_kernel<KN, false, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16(in[0].qtype));
   return hipGetLastError();
 }
 

@@ -9,22 +9,24 @@
 namespace qn {
 
 // Tables handed to the codec kernels by value (they live in the kernel argument
-// segment; kernels copy what they index dynamically into LDS).
-//   code[16]      the NF4 rows (fp32).
-//   thr[32], base[32]  bucket table for the nearest-row search: a normalised
-//   value n in [-1, 1] falls into bucket b = clamp(int(16 n + 16), 0, 31); the
-//   row index is base[b] + (n >= thr[b]).  Built on the host so that each bucket
-//   holds at most one decision threshold and every threshold lies far (>1e-4)
-//   from a bucket edge, which makes the bucket's own rounding irrelevant.
+// segment; kernels copy what they index dynamically into LDS), one per 4-bit
+// type (QN_NF4, QN_FP4).
+//   code[16]      the table's values by code (fp32).
+//   thr[32], base[32], lohi[32]  bucket table for the nearest-value search: a
+//   normalised value n in [-1, 1] falls into bucket b = clamp(int(16 n + 16),
+//   0, 31); its level is base[b] + (n >= thr[b]) among the distinct values in
+//   ascending order, and its code is byte (n >= thr[b]) of lohi[b].  For NF4
+//   the code of a level is the level itself.
 struct CodecTables {
   float code[16];
   float thr[32];
   uint32_t base[32];
+  uint32_t lohi[32];
 };
 
-// Host: the NF4 table and the bucket table (codebook.cpp).  Idempotent, thread-safe.
-const CodecTables &codec_tables();
-// False if the bucket table failed its self-check (never expected).
+// Host: the tables of a 4-bit type (codebook.cpp).  Idempotent, thread-safe.
+const CodecTables &codec_tables(int qtype = QN_NF4);
+// False if a decision table failed its self-check (never expected).
 bool codec_tables_ok();
 
 // Host: fp64 NF4 rows before rounding (exposed for the library's own checks).
@@ -50,8 +52,10 @@ class TraceScope {
 };
 
 // Kernel launchers (return hipError_t of the launch).
-hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, uint8_t *codes,
-                           float *absmax, hipStream_t s);
+// Quantise n weights; with absmax_q and scale2 non-null the same launch also
+// double-quantises the block scales (a workgroup per group of 256 blocks).
+hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, int qtype, uint8_t *codes,
+                           float *absmax, uint8_t *absmax_q, float *scale2, hipStream_t s);
 hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *absmax_q,
                                float *scale2, hipStream_t s);
 hipError_t launch_dequant(const qn_nf4_weight &W, void *out, int out_bf16, hipStream_t s);
@@ -59,18 +63,21 @@ hipError_t launch_dequant(const qn_nf4_weight &W, void *out, int out_bf16, hipSt
 hipError_t launch_merge(const qn_nf4_weight &W, const uint16_t *A, const uint16_t *B, int64_t r, float alpha,
                         void *out, int out_bf16, hipStream_t s);
 
-// Scale of block b: fl32(k_b * step_g) with double quantisation, else absmax[b].
+// Scale of block b: fl32(k_b * step_g) with double quantisation, else
+// absmax[b]; qtype names the table the codes index.
 struct ScaleSrc {
   const float *absmax;
   const uint8_t *absmax_q;
   const float *scale2;
+  int qtype;
 };
 
-// The 16 NF4 rows passed by value to kernels that build LDS tables from them.
+// The 16 values of a 4-bit table, passed by value to kernels that build LDS
+// tables from them.
 struct Code16 {
   float v[16];
 };
-Code16 code16();
+Code16 code16(int qtype = QN_NF4);
 
 // Dequant-GEMM (k_qgemm.hip).  out[M, Nout] (bf16) =
 //   sum_k L[m, k] * W_hat(k, n)  +  sum_{j<r} L2[m, j] * R2(j, n)
@@ -87,6 +94,7 @@ struct QGemmArgs {
   const float *absmax;
   const uint8_t *absmax_q;
   const float *scale2;
+  int qtype;
   const uint16_t *L2;
   int64_t ldl2;
   const uint16_t *R2;
@@ -99,7 +107,8 @@ struct QGemmArgs {
 hipError_t launch_qgemm_fwd(const QGemmArgs &a, hipStream_t s);
 hipError_t launch_qgemm_dx(const QGemmArgs &a, hipStream_t s);
 // Several independent forward products in one launch (n <= QN_MAX_GROUP); the
-// problems must agree on the scale source (all double-quantised or none).
+// problems must agree on the scale source (all double-quantised or none) and
+// on the 4-bit type.
 hipError_t launch_qgemm_fwd_group(const QGemmArgs *a, int n, hipStream_t s);
 
 // Problems of one grouped launch, passed by value in the kernel arguments.

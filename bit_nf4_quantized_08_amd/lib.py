@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_PKG, "libqlora_nf4.so")
 
 QN_OK = 0
 QN_F32, QN_BF16 = 0, 1
+QN_NF4, QN_FP4 = 0, 1
+QUANT_TYPES = {"nf4": QN_NF4, "fp4": QN_FP4}
 QN_OP_FWD, QN_OP_BWD = 0, 1
 QN_ERR_SCRATCH = 8
 QN_NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -43,6 +45,7 @@ class NF4WeightStruct(ctypes.Structure):
         ("scale2", ctypes.c_void_p),
         ("N", ctypes.c_int64),
         ("K", ctypes.c_int64),
+        ("quant_type", ctypes.c_int32),
     ]
 
 
@@ -73,6 +76,8 @@ def load():
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     sig = {
         "qn_codebook": (i32, [ctypes.POINTER(ctypes.c_float)]),
+        "qn_table": (i32, [i32, ctypes.POINTER(ctypes.c_float)]),
+        "qn_quantize_4bit": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]),
         "nf4_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "nf4_double_quant": (i32, [vp, i64, vp, vp, vp]),
         "nf4_dequant": (i32, [ctypes.POINTER(NF4WeightStruct), vp, i32, vp]),
@@ -99,7 +104,7 @@ def load():
 
 
 def exported_symbols():
-    return ["qn_codebook", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_merge", "qlora_workspace_size",
+    return ["qn_codebook", "qn_table", "qn_quantize_4bit", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_merge", "qlora_workspace_size",
             "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_workspace_size_grouped",
             "qlora_linear_fwd_grouped", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_trace_enable",
             "qn_trace_read"]
@@ -118,6 +123,13 @@ def qn_codebook():
     """The library's NF4 table (host call, no device work): numpy float32[16]."""
     out = (ctypes.c_float * 16)()
     _check("qn_codebook", load().qn_codebook(out))
+    return np.frombuffer(out, dtype=np.float32).copy()
+
+
+def qn_table(quant_type="nf4"):
+    """The library's table of a 4-bit type ("nf4" or "fp4"), by code: numpy float32[16]."""
+    out = (ctypes.c_float * 16)()
+    _check("qn_table", load().qn_table(QUANT_TYPES[quant_type], out))
     return np.frombuffer(out, dtype=np.float32).copy()
 
 
@@ -159,6 +171,7 @@ class NF4Weight:
     scale2: Optional[object]        # fp32 [ceil(nb/256)] or None
     N: int
     K: int
+    quant_type: int = QN_NF4        # QN_NF4 or QN_FP4: the table the codes index
 
     def struct(self, use_double_quant=True):
         dq = use_double_quant and self.absmax_q is not None
@@ -167,7 +180,7 @@ class NF4Weight:
             self.absmax.data_ptr() if (self.absmax is not None and not dq) else 0,
             self.absmax_q.data_ptr() if dq else 0,
             self.scale2.data_ptr() if dq else 0,
-            self.N, self.K)
+            self.N, self.K, self.quant_type)
 
 
 def nf4_quantize(W, codes=None, absmax=None):
@@ -199,8 +212,41 @@ def nf4_double_quant(absmax, absmax_q=None, scale2=None):
     return absmax_q, scale2
 
 
-def quantize_weight(W, double_quant=True):
-    """W (2-D device tensor) -> NF4Weight, optionally double-quantised."""
+def quantize_4bit(W, quant_type="nf4", codes=None, absmax=None, absmax_q=None, scale2=None, double_quant=True):
+    """qn_quantize_4bit: blockwise 4-bit quantisation of a 2-D fp32 or bf16 device
+    tensor, with the block scales double-quantised in the same launch when
+    ``double_quant``.  Returns an NF4Weight (absmax kept either way)."""
+    torch = _torch()
+    _need(W, "W", ndim=2)
+    if W.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("W must be float32 or bfloat16")
+    N, K = W.shape
+    n = N * K
+    nb = (n + 63) // 64
+    if codes is None:
+        codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=W.device)
+    if absmax is None:
+        absmax = torch.empty(nb, dtype=torch.float32, device=W.device)
+    if double_quant:
+        if absmax_q is None:
+            absmax_q = torch.empty(nb, dtype=torch.uint8, device=W.device)
+        if scale2 is None:
+            scale2 = torch.empty((nb + 255) // 256, dtype=torch.float32, device=W.device)
+    else:
+        absmax_q = scale2 = None
+    dt = QN_BF16 if W.dtype == torch.bfloat16 else QN_F32
+    qt = QUANT_TYPES[quant_type]
+    _check("qn_quantize_4bit", load().qn_quantize_4bit(_ptr(W), dt, N, K, qt, _ptr(codes), _ptr(absmax),
+                                                       _ptr(absmax_q), _ptr(scale2), _stream()))
+    return NF4Weight(codes, absmax, absmax_q, scale2, int(N), int(K), qt)
+
+
+def quantize_weight(W, double_quant=True, quant_type="nf4", fused=True):
+    """W (2-D device tensor) -> NF4Weight, optionally double-quantised: by default
+    in one launch (qn_quantize_4bit); ``fused=False`` (NF4 only) runs
+    nf4_quantize and then nf4_double_quant."""
+    if fused or quant_type != "nf4":
+        return quantize_4bit(W, quant_type, double_quant=double_quant)
     codes, absmax = nf4_quantize(W)
     aq = s2 = None
     if double_quant:

@@ -58,6 +58,17 @@ typedef enum {
 
 typedef enum { QN_F32 = 0, QN_BF16 = 1 } qn_dtype;
 
+/* 4-bit types: the table a weight's codes index.  [QE] "Turn a LoRA script
+ * into a QLoRA script with one config object": bnb_4bit_quant_type picks NF4,
+ * the quantile table; the library's other option is a small floating-point
+ * layout at the same memory.  QN_FP4 reads that as the E2M1 float (sign, two
+ * exponent bits, one mantissa bit; 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ * negatives) divided by 6 so the table spans [-1, 1] like NF4; code c has
+ * sign bit 3, exponent bits 2..1, mantissa bit 0; +0 (code 0) is the code
+ * written for zero. */
+#define QN_NF4 0
+#define QN_FP4 1
+
 /* One frozen weight W[N, K] in quantised form.  Caller-owned device buffers.
  *   codes    uint8[ceil(N*K/2)]: element e of the row-major flattening has its
  *            4-bit row index in byte e/2, low nibble for even e, high nibble for
@@ -69,6 +80,8 @@ typedef enum { QN_F32 = 0, QN_BF16 = 1 } qn_dtype;
  *   scale2   fp32[ceil(nb/256)]: grid step of each group of 256 blocks; required
  *            when absmax_q is non-NULL.  The scale of block b is then
  *            fl32(absmax_q[b] * scale2[b/256]).
+ *   quant_type QN_NF4 (0, the default of a zero-initialised struct) or QN_FP4:
+ *            the table the codes index.
  * codes 16-byte aligned; absmax, absmax_q and scale2 4-byte aligned.
  */
 typedef struct {
@@ -78,6 +91,7 @@ typedef struct {
   const float *scale2;
   int64_t N;
   int64_t K;
+  int32_t quant_type;
 } qn_nf4_weight;
 
 /* The NF4 table, written to host memory out[16] (index 0 = -1, 7 = 0, 15 = +1).
@@ -88,6 +102,10 @@ typedef struct {
  * probability 31/960, scaled to end at exactly -1 and +1) and rounded to fp32.
  * No device work.  Returns QN_ERR_NULL if out is NULL. */
 int qn_codebook(float out[16]);
+
+/* The table of a 4-bit type (QN_NF4 or QN_FP4) in host memory out[16], by
+ * code.  QN_ERR_NULL if out is NULL, QN_ERR_DTYPE for an unknown type. */
+int qn_table(int quant_type, float out[16]);
 
 /* Blockwise NF4 quantisation of W[N, K] ([QE] "The table, and the number that
  * stretches it", "Why the groups are small", "That is NF4").
@@ -103,6 +121,21 @@ int qn_codebook(float out[16]);
  * absmax 4-byte aligned. */
 int nf4_quantize(const void *W, int w_dtype, int64_t N, int64_t K,
                  uint8_t *codes, float *absmax, void *stream);
+
+/* Blockwise quantisation to either 4-bit type, with the block scales'
+ * double quantisation optionally in the same launch ([QE] "Shrink the scale
+ * factors too, and total up the real bill").
+ *   quant_type  QN_NF4 or QN_FP4 (QN_ERR_DTYPE otherwise).
+ *   codes, absmax  as nf4_quantize (same values for QN_NF4).
+ *   absmax_q, scale2  both NULL (no double quantisation), or both device
+ *       outputs as nf4_double_quant writes them from absmax (same values):
+ *       uint8[ceil(N*K/64)] and fp32[ceil(N*K/64/256)].
+ * For FP4 the closest of the fifteen distinct values is found as for NF4 (an
+ * exact tie goes to the lower value) and written as its code; zero is code 0.
+ * Alignment as nf4_quantize; absmax_q 4-byte aligned. */
+int qn_quantize_4bit(const void *W, int w_dtype, int64_t N, int64_t K, int quant_type,
+                     uint8_t *codes, float *absmax, uint8_t *absmax_q, float *scale2,
+                     void *stream);
 
 /* Double quantisation of nb block scales ([QE] "Shrink the scale factors too,
  * and total up the real bill": 8 bits per scale, one 32-bit constant per 256).

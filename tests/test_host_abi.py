@@ -51,8 +51,8 @@ def test_status_strings():
     assert lib.status_string(99) == "unknown status"
 
 
-def _w(N=64, K=64, codes=FAKE, absmax=FAKE, absmax_q=0, scale2=0):
-    return lib.NF4WeightStruct(codes, absmax, absmax_q, scale2, N, K)
+def _w(N=64, K=64, codes=FAKE, absmax=FAKE, absmax_q=0, scale2=0, quant_type=0):
+    return lib.NF4WeightStruct(codes, absmax, absmax_q, scale2, N, K, quant_type)
 
 
 def test_quantize_rejects_bad_arguments():
@@ -162,3 +162,25 @@ def test_grouped_forward_rejects_bad_arguments():
     arr[1].r = 16
     arr[1].W.K = 500
     assert L.qlora_linear_fwd_grouped(2, arr, vp(FAKE), 1 << 40, vp(0)) == 2
+
+
+def test_library_fp4_table_equals_oracle_bits():
+    """Two derivations of the 4-bit float table from its bit layout (C++ and
+    the oracle) give the same fp32 bits."""
+    np.testing.assert_array_equal(lib.qn_table("fp4").view(np.uint32), oracle.fp4_table().view(np.uint32))
+    np.testing.assert_array_equal(lib.qn_table("nf4").view(np.uint32), oracle.nf4_codebook().view(np.uint32))
+
+
+def test_quantize_4bit_and_types_reject_bad_arguments():
+    L = lib.load()
+    vp = ctypes.c_void_p
+    assert L.qn_table(2, (ctypes.c_float * 16)()) == 3
+    assert L.qn_table(0, None) == 1
+    q = lambda qt=0, aq=0, s2=0: L.qn_quantize_4bit(vp(FAKE), 0, 4, 64, qt, vp(FAKE), vp(FAKE), vp(aq), vp(s2),
+                                                    vp(0))
+    assert q(qt=2) == 3
+    assert q(aq=FAKE) == 1                     # absmax_q without scale2
+    assert q(s2=FAKE) == 1
+    assert q(aq=FAKE + 2, s2=FAKE) == 4
+    w = _w(quant_type=5)
+    assert L.nf4_dequant(ctypes.byref(w), vp(FAKE), 0, vp(0)) == 3

@@ -59,7 +59,7 @@ def test_noalloc_rejects_problems_beyond_the_scratch():
     say("noalloc rejects oversize problems")
     need = lib.workspace_size(lib.QN_OP_FWD, 1 << 18, 1024, 1024, 64)
     assert need > lib.QN_NOALLOC_SCRATCH_BYTES
-    w = lib.NF4WeightStruct(0x10000, 0x10000, 0, 0, 1024, 1024)
+    w = lib.NF4WeightStruct(0x10000, 0x10000, 0, 0, 1024, 1024, 0)
     vp = ctypes.c_void_p
     rc = lib.load().qlora_linear_fwd_noalloc(vp(0x10000), 1 << 18, ctypes.byref(w), vp(0x10000), vp(0x10000), 64,
                                              ctypes.c_float(128.0), vp(0x10000), vp(0), vp(0))
