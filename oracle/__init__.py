@@ -39,6 +39,9 @@ Parity status per function:
   dq.double_quant           pinned (closed forms, brute force).
   linear.forward / backward pinned (merged-weight identity, finite
                             differences, adjoint identity).
+  adamw8.adamw8_step        pinned (first step and trajectory against plain
+                            fp64 AdamW, brute-force state rounding, pure weight
+                            decay); AdamW itself is a reading (not on the pages).
   merge.merge               pinned (exact rational sum within its rounding
                             bound, zero adapter reads back the dequantised
                             weight, X W_m^T against the forward, re-quantising
@@ -51,6 +54,7 @@ from .nf4 import quantize, pack_codes, unpack_codes, dequant, block_absmax, tabl
 from .dq import double_quant, dq_absmax
 from .linear import forward, backward, dequant_bf16_weight
 from .merge import merge, adapter_delta
+from . import adamw8
 from . import sizes
 
 __all__ = [
@@ -59,5 +63,5 @@ __all__ = [
     "quantize", "pack_codes", "unpack_codes", "dequant", "block_absmax",
     "double_quant", "dq_absmax",
     "forward", "backward", "dequant_bf16_weight", "merge", "adapter_delta",
-    "sizes",
+    "sizes", "adamw8",
 ]
