@@ -440,6 +440,20 @@ def main():
              "note": "all 7 linears merged to bf16 (r = 64): r fused multiply-adds per weight, bound by the fp32 "
                      "vector rate (157.3 TFLOP/s) rather than by its bytes"}
     del mo
+    # one 8-bit AdamW step over the layer's adapters (A and B of every linear)
+    ad_t = [(t, t.clone(), lib.AdamW8State(t.numel(), dev)) for it in L.items for t in (it["A"], it["B"])]
+    ad_n = sum(t.numel() for t, _, _ in ad_t)
+    for t, gr, stt in ad_t:
+        lib.adamw8_step(t, gr, stt, lr=1e-4, step=1)
+    adam_us = graph_time_us(torch, cap, lambda: [lib.adamw8_step(t, gr, stt, lr=1e-4, step=2) for t, gr, stt in ad_t],
+                            replays=10)
+    adam_bytes = ad_n * (2 + 2 + 2 + 2 + 1 + 1) + 2 * 2 * 4 * ((ad_n + 63) // 64)
+    adamw8 = {"us": round(adam_us, 2), "params": ad_n, "GBps": round(adam_bytes / adam_us / 1e3, 1),
+              "hbm_frac": round(adam_bytes / adam_us / 1e3 / PEAK_HBM_GBPS, 4),
+              "state_bytes_per_param": 2.125,
+              "note": "14 calls (A and B of the 7 linears, r = 64); bytes = bf16 parameter read and written, bf16 "
+                      "gradient, both 8-bit codes read and written, block steps"}
+    del ad_t
     quality = L.quality
     weight_bytes = L.weight_bytes()
     del L
@@ -455,6 +469,7 @@ def main():
                             "per_linear": per_linear,
                             "dequant_rel_rmse": {k: round(v, 6) for k, v in quality.items()},
                             "merge_export_bf16": merge,
+                            "adamw8_adapter_step": adamw8,
                             "gemv_roofline": gemv_roof}}
     metrics = {"prefill_dequant_gemm_TFLOPs": round(flops_pre / pre_us / 1e6, 1),
                "decode_gemv_weight_GBps": round(weight_bytes / dec_us / 1e3, 1)}

@@ -112,6 +112,27 @@ int qlora_merge(const qn_nf4_weight *W, const void *A, const void *B, int64_t r,
                                      alpha, out, out_dtype == QN_BF16, static_cast<hipStream_t>(stream)));
 }
 
+int qn_adamw8_step(void *param, const void *grad, int64_t n, int8_t *m_q, float *m_step, uint8_t *u_q,
+                   float *u_step, const qn_adamw_config *cfg, void *stream) {
+  if (!param || !grad || !m_q || !m_step || !u_q || !u_step || !cfg) return QN_ERR_NULL;
+  if (n <= 0 || n > kMaxElems) return QN_ERR_SHAPE;
+  const qn_adamw_config &h = *cfg;
+  if (h.step < 1 || !std::isfinite(h.lr) || !std::isfinite(h.eps) || !(h.eps > 0.0f) ||
+      !std::isfinite(h.weight_decay) || !(h.beta1 >= 0.0f && h.beta1 < 1.0f) || !(h.beta2 >= 0.0f && h.beta2 < 1.0f))
+    return QN_ERR_VALUE;
+  if (!aligned(param, 16) || !aligned(grad, 16) || !aligned(m_q, 4) || !aligned(u_q, 4) || !aligned(m_step, 4) ||
+      !aligned(u_step, 4))
+    return QN_ERR_ALIGN;
+  qn::AdamConsts c{};
+  c.lr = h.lr; c.b1 = h.beta1; c.b2 = h.beta2; c.eps = h.eps; c.wd = h.weight_decay;
+  c.c1 = (float)(1.0 - (double)h.beta1);
+  c.c2 = (float)(1.0 - (double)h.beta2);
+  c.bc1 = (float)(1.0 - std::pow((double)h.beta1, (double)h.step));
+  c.bc2 = (float)(1.0 - std::pow((double)h.beta2, (double)h.step));
+  return hip_status(qn::launch_adamw8(static_cast<uint16_t *>(param), static_cast<const uint16_t *>(grad), n, m_q,
+                                      m_step, u_q, u_step, c, static_cast<hipStream_t>(stream)));
+}
+
 size_t qlora_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t r) {
   if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QN_MAX_RANK) return 0;
   if (K % QN_BLOCK != 0 || N % QN_BLOCK != 0) return 0;

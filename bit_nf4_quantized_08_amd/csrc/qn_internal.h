@@ -59,6 +59,15 @@ hipError_t launch_quantize(const void *W, int w_is_bf16, int64_t n, int qtype, u
 hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *absmax_q,
                                float *scale2, hipStream_t s);
 hipError_t launch_dequant(const qn_nf4_weight &W, void *out, int out_bf16, hipStream_t s);
+// One 8-bit AdamW step (k_adamw8.hip): the fp32 constants of the step, with
+// c1 = 1 - b1, c2 = 1 - b2, bc1 = 1 - b1^t, bc2 = 1 - b2^t formed in fp64 and
+// rounded once on the host.
+struct AdamConsts {
+  float lr, b1, b2, eps, wd, c1, c2, bc1, bc2;
+};
+hipError_t launch_adamw8(uint16_t *p, const uint16_t *g, int64_t n, int8_t *mq, float *ms, uint8_t *uq, float *us,
+                         const AdamConsts &c, hipStream_t s);
+
 // Adapter merged into the dequantised base (k_merge.hip).  W.K % 64 == 0, 1 <= r <= 64.
 hipError_t launch_merge(const qn_nf4_weight &W, const uint16_t *A, const uint16_t *B, int64_t r, float alpha,
                         void *out, int out_bf16, hipStream_t s);

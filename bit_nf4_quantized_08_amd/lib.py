@@ -63,6 +63,17 @@ class FwdProblemStruct(ctypes.Structure):
     ]
 
 
+class AdamWConfigStruct(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float),
+        ("beta1", ctypes.c_float),
+        ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("weight_decay", ctypes.c_float),
+        ("step", ctypes.c_int64),
+    ]
+
+
 def load():
     """Load the shared library (once).  Raises if it has not been built."""
     global _lib
@@ -81,6 +92,7 @@ def load():
         "nf4_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "nf4_double_quant": (i32, [vp, i64, vp, vp, vp]),
         "nf4_dequant": (i32, [ctypes.POINTER(NF4WeightStruct), vp, i32, vp]),
+        "qn_adamw8_step": (i32, [vp, vp, i64, vp, vp, vp, vp, ctypes.POINTER(AdamWConfigStruct), vp]),
         "qlora_merge": (i32, [ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, i32, vp]),
         "qlora_workspace_size": (ctypes.c_size_t, [i32, i64, i64, i64, i64]),
         "qlora_linear_fwd": (i32, [vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp,
@@ -104,7 +116,7 @@ def load():
 
 
 def exported_symbols():
-    return ["qn_codebook", "qn_table", "qn_quantize_4bit", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_merge", "qlora_workspace_size",
+    return ["qn_codebook", "qn_table", "qn_quantize_4bit", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_merge", "qn_adamw8_step", "qlora_workspace_size",
             "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_workspace_size_grouped",
             "qlora_linear_fwd_grouped", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_trace_enable",
             "qn_trace_read"]
@@ -281,6 +293,39 @@ def qlora_merge(w: NF4Weight, A, B, alpha, out_dtype="bf16", use_double_quant=Tr
     return out
 
 
+class AdamW8State:
+    """8-bit block-wise AdamW state of one bf16 tensor (zeros: before the first step)."""
+
+    def __init__(self, n, device="cuda"):
+        torch = _torch()
+        nb = (n + 63) // 64
+        self.n = n
+        self.m_q = torch.zeros(n, dtype=torch.int8, device=device)
+        self.m_step = torch.zeros(nb, dtype=torch.float32, device=device)
+        self.u_q = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.u_step = torch.zeros(nb, dtype=torch.float32, device=device)
+        self.step = 0
+
+
+def adamw8_step(param, grad, state: AdamW8State, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                step=None):
+    """One qn_adamw8_step on a bf16 tensor in place; advances state.step
+    unless an explicit step number is given."""
+    torch = _torch()
+    _need(param, "param", torch.bfloat16)
+    _need(grad, "grad", torch.bfloat16)
+    if param.numel() != state.n or grad.numel() != state.n:
+        raise ValueError("param, grad and state sizes differ")
+    if step is None:
+        state.step += 1
+        step = state.step
+    cfg = AdamWConfigStruct(lr, beta1, beta2, eps, weight_decay, int(step))
+    _check("qn_adamw8_step", load().qn_adamw8_step(
+        _ptr(param), _ptr(grad), state.n, _ptr(state.m_q), _ptr(state.m_step), _ptr(state.u_q), _ptr(state.u_step),
+        ctypes.byref(cfg), _stream()))
+    return param
+
+
 def workspace_size(op, M, N, K, r):
     return int(load().qlora_workspace_size(op, M, N, K, r))
 
@@ -428,7 +473,7 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_
 
 
 TRACE_KINDS = {1: "quantize", 2: "double_quant", 3: "dequant", 4: "gemv", 5: "gemm_fwd", 6: "gemm_dx",
-               7: "gemm_db", 8: "gemm_da", 9: "lowrank", 10: "merge"}
+               7: "gemm_db", 8: "gemm_da", 9: "lowrank", 10: "merge", 11: "adamw8"}
 
 
 def trace_enable(on=True):

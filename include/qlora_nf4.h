@@ -175,6 +175,38 @@ int nf4_dequant(const qn_nf4_weight *W, void *out, int out_dtype, void *stream);
 int qlora_merge(const qn_nf4_weight *W, const void *A, const void *B, int64_t r,
                 float alpha, void *out, int out_dtype, void *stream);
 
+/* One AdamW step on a bf16 adapter tensor (A or B of a linear) with 8-bit
+ * block-wise optimizer state.  [QE] "Why the groups are small": block-wise
+ * quantisation (blocks of 64, a scale each) is what makes 8-bit optimizer
+ * state work; "Turn a LoRA script into a QLoRA script with one config object":
+ * the optimizer is an 8-bit AdamW, its state belongs to the adapter only.
+ * The AdamW rule is the published one (decoupled weight decay, bias-corrected
+ * moments, step t >= 1); in fp32, each operation rounded once in this order:
+ *   m = k_m step_m,  u = k_u step_u,  v = u u            (state read back)
+ *   m' = b1 m + (1-b1) g,   v' = b2 v + (1-b2) (g g)
+ *   p' = bf16(p - lr ((m'/(1-b1^t)) / (sqrt(v'/(1-b2^t)) + eps) + wd p))
+ * with 1-b1, 1-b2, 1-b1^t, 1-b2^t formed in double from the fp32 betas and
+ * rounded once.  The new state, per block of 64 consecutive parameters: the
+ * first moment signed, step_m = max|m'|/127, k_m = clamp(ceil(m'/step_m - 1/2),
+ * -127, 127); the second through its square root u' = sqrt(v'), step_u =
+ * max u'/255, k_u = clamp(ceil(u'/step_u - 1/2), 0, 255); a zero block has step
+ * 0 and codes 0.  2.125 bytes of state per parameter.
+ *   param  device bf16 [n], updated in place;  grad device bf16 [n].
+ *   m_q    device int8 [n];  m_step device fp32 [ceil(n/64)];
+ *   u_q    device uint8 [n]; u_step device fp32 [ceil(n/64)]: read and rewritten;
+ *          all zero before the first step.
+ * param, grad 16-byte aligned; m_q, u_q, m_step, u_step 4-byte aligned.
+ * QN_ERR_VALUE for step < 1, lr, eps or weight_decay not finite, a beta
+ * outside [0, 1) or eps <= 0.  (The pages' "paged" placement of this state in
+ * host memory is a property of where the caller puts the buffers; the
+ * library allocates none.) */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int64_t step;
+} qn_adamw_config;
+int qn_adamw8_step(void *param, const void *grad, int64_t n, int8_t *m_q, float *m_step,
+                   uint8_t *u_q, float *u_step, const qn_adamw_config *cfg, void *stream);
+
 /* Workspace size in bytes for op = QN_OP_FWD or QN_OP_BWD at the given shape.
  * Returns 0 for an invalid op or shape. */
 #define QN_OP_FWD 0
@@ -289,6 +321,7 @@ int qlora_linear_bwd(const void *dY, const void *X, const float *H, int64_t M,
 #define QN_TRACE_GEMM_DA 8       /* reserved (dA shares the launch of kind 7)    */
 #define QN_TRACE_LOWRANK 9       /* X A^T or dY B low-rank product               */
 #define QN_TRACE_MERGE 10        /* qlora_merge kernel                           */
+#define QN_TRACE_ADAMW8 11       /* qn_adamw8_step kernel                        */
 int qn_trace_enable(int on);
 int qn_trace_read(int *kinds, float *ms, int cap);
 

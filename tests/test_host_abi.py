@@ -184,3 +184,22 @@ def test_quantize_4bit_and_types_reject_bad_arguments():
     assert q(aq=FAKE + 2, s2=FAKE) == 4
     w = _w(quant_type=5)
     assert L.nf4_dequant(ctypes.byref(w), vp(FAKE), 0, vp(0)) == 3
+
+
+def test_adamw8_rejects_bad_arguments():
+    L = lib.load()
+    vp = ctypes.c_void_p
+    ok = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1)
+
+    def call(n=64, p=FAKE, aq=FAKE, **kw):
+        cfg = lib.AdamWConfigStruct(**dict(ok, **kw))
+        return L.qn_adamw8_step(vp(p), vp(FAKE), n, vp(aq), vp(FAKE), vp(FAKE), vp(FAKE), ctypes.byref(cfg), vp(0))
+    assert call(p=0) == 1
+    assert call(n=0) == 2
+    assert call(step=0) == 7
+    assert call(beta1=1.0) == 7
+    assert call(beta2=-0.1) == 7
+    assert call(eps=0.0) == 7
+    assert call(lr=float("inf")) == 7
+    assert call(p=FAKE + 2) == 4
+    assert call(aq=FAKE + 1) == 4
