@@ -381,6 +381,11 @@ def main():
     dec_us = graph_time_us(torch, cap, lambda: [grp.run() for grp in dec_groups])
     pre_single_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE))
     pre_all7_us = graph_time_us(torch, cap, lambda: all7[0].run())
+    tilings = {}
+    for v in (1, 2, 3):
+        lib.set_gemm_variant(v)
+        tilings[v] = graph_time_us(torch, cap, lambda: [grp.run() for grp in pre_groups])
+    lib.set_gemm_variant(0)
     per_linear = {}
     for it in L.items:
         us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE, [it]))
@@ -464,6 +469,10 @@ def main():
                             "prefill_M4096_TFLOPs": round(flops_pre / pre_us / 1e6, 1),
                             "prefill_M4096_single_calls_TFLOPs": round(flops_pre / pre_single_us / 1e6, 1),
                             "prefill_M4096_one_call_all7_TFLOPs": round(flops_pre / pre_all7_us / 1e6, 1),
+                            "prefill_M4096_TFLOPs_by_tiling": {"256x128": round(flops_pre / tilings[1] / 1e6, 1),
+                                                               "256x256_8waves": round(flops_pre / tilings[2] / 1e6, 1),
+                                                               "256x256_4waves": round(flops_pre / tilings[3] / 1e6, 1),
+                                                               "automatic": round(flops_pre / pre_us / 1e6, 1)},
                             "decode_M1_us": round(dec_us, 2),
                             "decode_M1_weight_GBps": round(weight_bytes / dec_us / 1e3, 1),
                             "per_linear": per_linear,

@@ -292,6 +292,12 @@ const char *qn_status_string(int status) {
   }
 }
 
+int qn_set_gemm_variant(int variant) {
+  if (variant < 0 || variant > 3) return QN_ERR_VALUE;
+  qn::set_gemm_variant(variant);
+  return QN_OK;
+}
+
 const char *qn_version(void) { return "qlora_nf4 0.1 (gfx950)"; }
 
 }  // extern "C"

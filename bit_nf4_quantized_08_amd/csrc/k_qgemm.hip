@@ -44,6 +44,7 @@
 // the activation-stage comment below).
 
 #include <algorithm>
+#include <atomic>
 
 #include "qn_device.h"
 #include "qn_internal.h"
@@ -669,23 +670,639 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
   }
 }
 
+// ============================================================ 256 x 256 tiles
+// Second tiling of the forward product (row-major weights): a workgroup
+// computes a 256 x 256 output tile with 8 waves, two per SIMD, and every wave
+// both multiplies and dequantises.  Wave w owns rows 64 (w & 3) .. +63 and
+// columns 128 (w >> 2) .. +127 of the tile (2 x 4 MFMA tiles of 32 x 32, as an
+// MMA wave above), and the 512 threads together dequantise the 256 x 64
+// weight stage of the next step (thread t: the producer row and half of the
+// tiling above, over 256 rows) while the MFMAs of the current step run on the
+// matrix cores.  Against the 256 x 128 tile, the activation rows staged per
+// step serve twice the columns (half the activation traffic per FLOP), and the
+// dequantisation sits in the same instruction streams as the MFMAs of two
+// waves per SIMD instead of in one producer wave per SIMD, so the matrix cores
+// and the vector units overlap without a producer wave setting the pace.
+//
+// LDS: two activation stages (256 rows x 64, XOR-swizzled as above, 32 KB
+// each) and two weight stages (256 columns x LD, 36 KB each): one step ahead.
+// Step s reads activation stage s & 1 and weight stage s & 1; during it the
+// waves issue the direct-to-LDS loads of activation step s + 1, write weight
+// step s + 1 from the register set loaded two steps earlier and reload that set
+// for step s + 3; one barrier per step.  The adapter term is one more step
+// whose left operand (H or sH, zero beyond ldl2) comes through the activation
+// stage and whose right operand (B, zero beyond r) is loaded after the main
+// loop and written as the weight stage.
+constexpr int kThreads2 = 512;
+constexpr int BM2 = 256, BN2 = 256;
+constexpr int R_TILE2 = BN2 * LD;
+constexpr int XSTAGE2 = BM2 * BK;
+
+template <bool DQ>
+__global__ __launch_bounds__(kThreads2, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < QN_MAX_GROUP; ++i) gi += (i < grp.n && (int)blockIdx.x >= grp.start[i]) ? 1 : 0;
+  gi = __builtin_amdgcn_readfirstlane(gi);
+  const QGemmArgs a = grp.p[gi];
+  const int tile = (int)blockIdx.x - grp.start[gi];
+  if (tile >= a.tiles_m * a.tiles_n) return;
+
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[XSTAGE2];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[XSTAGE2];
+  __shared__ __attribute__((aligned(16))) uint16_t ws0[R_TILE2];
+  __shared__ __attribute__((aligned(16))) uint16_t ws1[R_TILE2];
+
+  int tm, tn;
+  tile_coords(tile, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM2, n0 = (int64_t)tn * BN2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave & 3, cg = wave >> 2;
+  const int nsteps = __builtin_amdgcn_readfirstlane((int)(a.Kc / BK));   // >= 1
+  const int last = nsteps - 1, ntotal = nsteps + 1;
+
+  // ---- activation stages: wave w loads rows 32 cg .. +31 of row group rg
+  // (loads g = 4 cg .. 4 cg + 3 of that group's eight 8-row loads; chunk
+  // swizzle and lane layout as in the tiling above).
+  const int64_t grow0 = m0 + (int64_t)rg * WM;
+  const rsrc_t xr = make_rsrc(a.L + grow0 * a.ldl, (a.M - grow0) * a.ldl * 2);
+  const rsrc_t l2r = make_rsrc(a.L2 + grow0 * a.ldl2, (a.M - grow0) * a.ldl2 * 2);
+  const uint32_t c0 = (uint32_t)((lane & 7) ^ (lane >> 4));
+  const uint32_t xbase0 = (uint32_t)((lane >> 3) * a.ldl * 2 + c0 * 16);
+  const uint32_t xbase1 = (uint32_t)((lane >> 3) * a.ldl * 2 + (c0 ^ 4u) * 16);
+  const uint32_t xrow8 = (uint32_t)(8 * a.ldl * 2);
+  const uint32_t l2base0 = (uint32_t)((lane >> 3) * a.ldl2 * 2 + c0 * 16);
+  const uint32_t l2base1 = (uint32_t)((lane >> 3) * a.ldl2 * 2 + (c0 ^ 4u) * 16);
+  const bool l2ok0 = 8 * (int64_t)c0 < a.ldl2, l2ok1 = 8 * (int64_t)(c0 ^ 4u) < a.ldl2;
+  const uint32_t l2row8 = (uint32_t)(8 * a.ldl2 * 2);
+  auto issue_x = [&](uint16_t *stage, int t) {
+    const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(stage + rg * XW));
+    const bool main_step = t < nsteps, live = t < ntotal;
+    const rsrc_t r = main_step ? xr : l2r;
+    const int soff = main_step ? t * BK * 2 : 0;
+#pragma unroll
+    for (int g = 4 * cg; g < 4 * cg + 4; ++g) {
+      const bool odd = g & 1;
+      const uint32_t l2off =
+          live && (odd ? l2ok1 : l2ok0) ? (odd ? l2base1 : l2base0) + (uint32_t)g * l2row8 : kOutOfRange;
+      const uint32_t off = main_step ? (odd ? xbase1 : xbase0) + (uint32_t)g * xrow8 : l2off;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(size_t)(base + g * 1024),
+                                               16, off, soff, 0, 0);
+    }
+  };
+
+  // ---- weight stages: the producer of the tiling above, over 256 rows.
+  Producer<false, DQ> P;
+  P.init(a, tid, n0);
+  typename Producer<false, DQ>::Set s0, s1;
+
+  // ---- fragments
+  const int lr = lane & 31, lh = lane >> 5;
+  uint32_t aoff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) aoff[c] = (uint32_t)(rg * XW + lr * BK + (((4 * lh + c) ^ ((lr >> 1) & 7)) * 8));
+  const int rb = (128 * cg + lr) * LD + 32 * (lh ^ (((lr >> 3) ^ (lr >> 4)) & 1));
+  struct Frag {
+    bf16x8 a[TM];
+    bf16x8 b[TN];
+  };
+  auto read_f = [&](Frag &f, const uint16_t *xc, const uint16_t *wc, int c) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(&xc[aoff[c] + i * 32 * BK]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * (c ^ j)]);
+  };
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto mma = [&](const Frag &f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+
+  // ---- prologue: code sets of steps 0 and 1, activation stage 0, weight stage 0.
+  constexpr int kReload = DQ ? 3 : 2;
+  P.issue(s0, 0);
+  issue_x(xs0, 0);
+  P.issue(s1, __builtin_amdgcn_readfirstlane(min(1, last)));
+  P.store(s0, ws0, nullptr, cb.v, lane, [&](int) {});
+  P.issue(s0, __builtin_amdgcn_readfirstlane(min(2, last)));
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kReload));
+  lds_barrier();
+
+  // Step s: multiply stage s while staging step s + 1 (its activations by
+  // direct-to-LDS loads, its weights from register set `set`), then reload the
+  // set for step s + 3 (clamped: past the end it re-reads the last step, whose
+  // stage the adapter operand later replaces).  The dequantisation runs one
+  // k-slice behind the MFMAs in the same instruction stream: the MFMAs of
+  // slice 0 go with building the block's sixteen products, those of slice c
+  // (c = 1..3) with expanding code word c - 1, and the scheduling groups below
+  // alternate one MFMA with a few vector instructions, so that each wave keeps
+  // the matrix core busy while it dequantises (the two waves of a SIMD start
+  // every step together, so they cannot cover for each other).
+  const uint16_t *wrow = nullptr;
+  (void)wrow;
+  const int wcol = P.wr_col, wk = P.wr_k;
+  const int wsw = kswz(wcol);
+  auto step = [&](int s, const uint16_t *xc, const uint16_t *wc, uint16_t *xn, uint16_t *wn,
+                  typename Producer<false, DQ>::Set &set) {
+    issue_x(xn, s + 1);
+    Frag f0, f1;
+    read_f(f0, xc, wc, 0);
+    read_f(f1, xc, wc, 1);
+    uint32_t LO[4], HI[4];
+    // slice 0 + the block's products
+    {
+      const float A = P.scale(set);
+      uint32_t Pp[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) Pp[k] = pack_bf16x2(cb.v[2 * k] * A, cb.v[2 * k + 1] * A);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        LO[m] = __builtin_amdgcn_perm(Pp[2 * m + 1], Pp[2 * m], 0x06040200u);
+        HI[m] = __builtin_amdgcn_perm(Pp[2 * m + 1], Pp[2 * m], 0x07050301u);
+      }
+      mma(f0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+    }
+    read_f(f0, xc, wc, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    auto look = [&](uint32_t x, uint32_t &lo, uint32_t &hi) {
+      const uint32_t s7 = x & 0x07070707u;
+      const u16x2 bit3 = __builtin_bit_cast(u16x2, (x >> 3) & 0x01010101u);
+      const uint32_t upper = __builtin_bit_cast(uint32_t, bit3 * (u16x2){0xFF, 0xFF});
+      const uint32_t l0 = __builtin_amdgcn_perm(LO[1], LO[0], s7), l1 = __builtin_amdgcn_perm(LO[3], LO[2], s7);
+      const uint32_t h0 = __builtin_amdgcn_perm(HI[1], HI[0], s7), h1 = __builtin_amdgcn_perm(HI[3], HI[2], s7);
+      lo = (upper & l1) | (~upper & l0);
+      hi = (upper & h1) | (~upper & h0);
+    };
+    auto word = [&](int i) {
+      const uint32_t w = set.code[i], w4 = w >> 4;
+      uint32_t o[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t lo, hi;
+        look(__builtin_amdgcn_perm(w4, w, h ? 0x07030602u : 0x05010400u), lo, hi);
+        o[2 * h + 0] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+        o[2 * h + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+      }
+      *reinterpret_cast<u32x4 *>(&wn[wcol * LD + ((wk + 8 * i) ^ wsw)]) = u32x4{o[0], o[1], o[2], o[3]};
+    };
+    // slice 1 + word 0
+    mma(f1);
+    word(0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    read_f(f1, xc, wc, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 2 + word 1
+    mma(f0);
+    word(1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 3 + word 2
+    mma(f1);
+    word(2);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    word(3);
+    __builtin_amdgcn_sched_barrier(0);
+    P.issue(set, __builtin_amdgcn_readfirstlane(min(s + 3, last)));
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload));
+    lds_barrier();
+  };
+  int s = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    step(s, xs0, ws0, xs1, ws1, s1);
+    step(s + 1, xs1, ws1, xs0, ws0, s0);
+  }
+  if (s < nsteps) {
+    step(s, xs0, ws0, xs1, ws1, s1);
+    ++s;
+  }
+  // ---- adapter step: left operand in activation stage nsteps & 1 (loaded by
+  // the last step); right operand B (zero beyond r) into weight stage nsteps & 1.
+  uint16_t *xa = (nsteps & 1) ? xs1 : xs0;
+  uint16_t *wa = (nsteps & 1) ? ws1 : ws0;
+  {
+    const int col = tid & (BN2 - 1), j0 = 32 * (tid >> 8);
+    const int64_t gn = n0 + col;
+    const rsrc_t rr = make_rsrc(a.R2, a.Nout * a.ldr2 * 2);
+    uint32_t h[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int64_t j = j0 + i;
+      const bool in = j < a.r && gn < a.Nout;
+      h[i] = __builtin_amdgcn_raw_buffer_load_b16(rr, in ? (uint32_t)((gn * a.ldr2 + j) * 2) : kOutOfRange, 0, 0);
+    }
+    uint32_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (h[2 * i] & 0xFFFFu) | (h[2 * i + 1] << 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4 *>(&wa[col * LD + ((j0 + 8 * q) ^ kswz(col))]) = u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  lds_barrier();
+  {
+    Frag f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      read_f(f, xa, wa, c);
+      mma(f);
+    }
+  }
+  lds_barrier();
+
+  // ---- store bf16 through LDS, one 32 x 128 block per wave at a time (the
+  // layout and the 16-byte row stores of the tiling above); a wave reuses its
+  // own block region, so the two passes need no barrier between them.
+  constexpr int kOutPitch = BN + 8;
+  const rsrc_t rout = make_rsrc(a.out + m0 * a.ldo, (a.M - m0) * a.ldo * 2);
+  const bool vec_ok = (a.ldo & 7) == 0 && ((uint64_t)a.out & 15) == 0;
+  uint16_t *blk = (wave < 3 ? xs0 : (wave < 6 ? xs1 : ws0)) + (wave < 6 ? wave % 3 : wave - 6) * 32 * kOutPitch;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        blk[(8 * (e >> 2) + 4 * lh + (e & 3)) * kOutPitch + j * 32 + lr] = f32_to_bf16(acc[i][j][e]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 4 * q + (lane >> 4), c8 = 8 * (lane & 15);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&blk[row * kOutPitch + c8]);
+      const int64_t lrow = (int64_t)rg * WM + i * 32 + row, gn = n0 + 128 * cg + c8;
+      if (vec_ok && gn + 8 <= a.Nout) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, rout, (uint32_t)((lrow * a.ldo + gn) * 2), 0, 0);
+      } else if (m0 + lrow < a.M) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (gn + t < a.Nout) a.out[(m0 + lrow) * a.ldo + gn + t] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
+      }
+    }
+  }
+}
+
+// ============================================================ 256 x 256, 4 waves
+// Third tiling of the forward product: the same 256 x 256 output tile with
+// four waves, one per SIMD, each owning 128 x 128 (4 x 4 MFMA tiles of 32 x 32,
+// the accumulators in the accumulation registers).  A wave's fragment reads
+// per step are (128 + 128) x 64 values for 128 x 128 x 64 multiply-adds, a
+// third less LDS read traffic per FLOP than 64 x 128 per wave, and each k-slice
+// gives a wave sixteen MFMAs (512 matrix-core cycles) behind which it issues
+// the next slice's fragment reads and its share of the dequantisation.
+// Thread t dequantises weight row t of the tile: the 64 codes of a step are one
+// NF4 block (one scale, one table of products), 32 bytes read as two 16-byte
+// loads; they are written as eight 16-byte chunks of the swizzled weight stage.
+constexpr int kThreads3 = 256;
+constexpr int TM3 = 4, TN3 = 4;
+
+template <bool DQ>
+struct RowProducer {
+  struct Set {
+    u32x4 c0, c1;   // 64 codes of one row, one step
+    uint32_t q;
+    float st;
+  };
+  rsrc_t rc, rq, rs;
+  uint32_t cvoff, qvoff;
+  int64_t blk_base;
+  int row;
+  __device__ void init(const QGemmArgs &a, int tid, int64_t n0) {
+    row = tid;
+    rc = make_rsrc(a.codes + n0 * (a.Kc / 2), (a.Nout - n0) * (a.Kc / 2));
+    cvoff = (uint32_t)(row * (a.Kc / 2));
+    blk_base = (n0 + row) * (a.Kc / 64);
+    if constexpr (DQ) {
+      rq = make_rsrc(a.absmax_q + n0 * (a.Kc / 64), (a.Nout - n0) * (a.Kc / 64));
+      qvoff = (uint32_t)(row * (a.Kc / 64));
+      rs = make_rsrc(a.scale2, (a.Nout * a.Kc / 64 + 255) / 256 * 4);
+    } else {
+      rq = make_rsrc(a.absmax + n0 * (a.Kc / 64), (a.Nout - n0) * (a.Kc / 64) * 4);
+      qvoff = (uint32_t)(row * (a.Kc / 64) * 4);
+    }
+    if (n0 + row >= a.Nout) cvoff = qvoff = kOutOfRange;
+  }
+  __device__ __forceinline__ void issue(Set &t, int s) {
+    t.c0 = __builtin_amdgcn_raw_buffer_load_b128(rc, cvoff, s * (BK / 2), 0);
+    t.c1 = __builtin_amdgcn_raw_buffer_load_b128(rc, cvoff == kOutOfRange ? kOutOfRange : cvoff + 16, s * (BK / 2), 0);
+    if constexpr (DQ) {
+      t.q = __builtin_amdgcn_raw_buffer_load_b8(rq, qvoff, s, 0);
+      const int64_t b = blk_base + s;
+      t.st = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
+          rs, qvoff == kOutOfRange ? kOutOfRange : (uint32_t)((b >> 8) * 4), 0, 0));
+    } else {
+      t.q = __builtin_amdgcn_raw_buffer_load_b32(rq, qvoff, s * 4, 0);
+    }
+  }
+  __device__ __forceinline__ float scale(const Set &t) const {
+    if constexpr (DQ) return (float)t.q * t.st;
+    else return as_f32(t.q);
+  }
+};
+
+template <bool DQ>
+__global__ __launch_bounds__(kThreads3, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void qgemm3_kernel(QGemmGroup grp, Code16 cb) {
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < QN_MAX_GROUP; ++i) gi += (i < grp.n && (int)blockIdx.x >= grp.start[i]) ? 1 : 0;
+  gi = __builtin_amdgcn_readfirstlane(gi);
+  const QGemmArgs a = grp.p[gi];
+  const int tile = (int)blockIdx.x - grp.start[gi];
+  if (tile >= a.tiles_m * a.tiles_n) return;
+
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[XSTAGE2];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[XSTAGE2];
+  __shared__ __attribute__((aligned(16))) uint16_t ws0[R_TILE2];
+  __shared__ __attribute__((aligned(16))) uint16_t ws1[R_TILE2];
+
+  int tm, tn;
+  tile_coords(tile, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM2, n0 = (int64_t)tn * BN2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = wave & 1, ch = wave >> 1;       // rows 128 rh .., columns 128 ch ..
+  const int nsteps = __builtin_amdgcn_readfirstlane((int)(a.Kc / BK));   // >= 1
+  const int last = nsteps - 1, ntotal = nsteps + 1;
+
+  // ---- activation stages: wave w loads the 64 rows of row block w (eight
+  // 8-row loads, chunk swizzle and lane layout of the first tiling).
+  const int64_t grow0 = m0 + (int64_t)wave * WM;
+  const rsrc_t xr = make_rsrc(a.L + grow0 * a.ldl, (a.M - grow0) * a.ldl * 2);
+  const rsrc_t l2r = make_rsrc(a.L2 + grow0 * a.ldl2, (a.M - grow0) * a.ldl2 * 2);
+  const uint32_t c0 = (uint32_t)((lane & 7) ^ (lane >> 4));
+  const uint32_t xbase0 = (uint32_t)((lane >> 3) * a.ldl * 2 + c0 * 16);
+  const uint32_t xbase1 = (uint32_t)((lane >> 3) * a.ldl * 2 + (c0 ^ 4u) * 16);
+  const uint32_t xrow8 = (uint32_t)(8 * a.ldl * 2);
+  const uint32_t l2base0 = (uint32_t)((lane >> 3) * a.ldl2 * 2 + c0 * 16);
+  const uint32_t l2base1 = (uint32_t)((lane >> 3) * a.ldl2 * 2 + (c0 ^ 4u) * 16);
+  const bool l2ok0 = 8 * (int64_t)c0 < a.ldl2, l2ok1 = 8 * (int64_t)(c0 ^ 4u) < a.ldl2;
+  const uint32_t l2row8 = (uint32_t)(8 * a.ldl2 * 2);
+  auto issue_x = [&](uint16_t *stage, int t) {
+    const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(stage + wave * XW));
+    const bool main_step = t < nsteps, live = t < ntotal;
+    const rsrc_t r = main_step ? xr : l2r;
+    const int soff = main_step ? t * BK * 2 : 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const bool odd = g & 1;
+      const uint32_t l2off =
+          live && (odd ? l2ok1 : l2ok0) ? (odd ? l2base1 : l2base0) + (uint32_t)g * l2row8 : kOutOfRange;
+      const uint32_t off = main_step ? (odd ? xbase1 : xbase0) + (uint32_t)g * xrow8 : l2off;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(size_t)(base + g * 1024),
+                                               16, off, soff, 0, 0);
+    }
+  };
+
+  RowProducer<DQ> P;
+  P.init(a, tid, n0);
+  typename RowProducer<DQ>::Set s0, s1;
+  const int wsw = kswz(tid);
+
+  // ---- fragments: A row tile i of the wave is rows 128 rh + 32 i + lr (row
+  // block 2 rh + i / 2); B column tile j is column 128 ch + 32 j + lr.
+  const int lr = lane & 31, lh = lane >> 5;
+  uint32_t aoff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) aoff[c] = (uint32_t)(2 * rh * XW + lr * BK + (((4 * lh + c) ^ ((lr >> 1) & 7)) * 8));
+  const int rb = (128 * ch + lr) * LD + 32 * (lh ^ (((lr >> 3) ^ (lr >> 4)) & 1));
+  struct Frag {
+    bf16x8 a[TM3];
+    bf16x8 b[TN3];
+  };
+  auto read_f = [&](Frag &f, const uint16_t *xc, const uint16_t *wc, int c) {
+#pragma unroll
+    for (int i = 0; i < TM3; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(&xc[aoff[c] + i * 32 * BK]);
+#pragma unroll
+    for (int j = 0; j < TN3; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * (c ^ j)]);
+  };
+  f32x16 acc[TM3][TN3];
+#pragma unroll
+  for (int i = 0; i < TM3; ++i)
+#pragma unroll
+    for (int j = 0; j < TN3; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto mma = [&](const Frag &f) {
+#pragma unroll
+    for (int i = 0; i < TM3; ++i)
+#pragma unroll
+      for (int j = 0; j < TN3; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Dequantise one row-step: the block's sixteen bf16 products, split into
+  // low-byte and high-byte planes, looked up four codes at a time with byte
+  // permutes (as the first tiling's producer), written as 16-byte chunks.
+  uint32_t LO[4], HI[4];
+  auto prep = [&](const typename RowProducer<DQ>::Set &t) {
+    const float A = P.scale(t);
+    uint32_t Pp[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) Pp[k] = pack_bf16x2(cb.v[2 * k] * A, cb.v[2 * k + 1] * A);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      LO[m] = __builtin_amdgcn_perm(Pp[2 * m + 1], Pp[2 * m], 0x06040200u);
+      HI[m] = __builtin_amdgcn_perm(Pp[2 * m + 1], Pp[2 * m], 0x07050301u);
+    }
+  };
+  auto look = [&](uint32_t x, uint32_t &lo, uint32_t &hi) {
+    const uint32_t s7 = x & 0x07070707u;
+    const u16x2 bit3 = __builtin_bit_cast(u16x2, (x >> 3) & 0x01010101u);
+    const uint32_t upper = __builtin_bit_cast(uint32_t, bit3 * (u16x2){0xFF, 0xFF});
+    const uint32_t l0 = __builtin_amdgcn_perm(LO[1], LO[0], s7), l1 = __builtin_amdgcn_perm(LO[3], LO[2], s7);
+    const uint32_t h0 = __builtin_amdgcn_perm(HI[1], HI[0], s7), h1 = __builtin_amdgcn_perm(HI[3], HI[2], s7);
+    lo = (upper & l1) | (~upper & l0);
+    hi = (upper & h1) | (~upper & h0);
+  };
+  // code word i (0..7) of the row-step: positions 8 i .. 8 i + 7
+  auto word = [&](const typename RowProducer<DQ>::Set &t, int i, uint16_t *wn) {
+    const uint32_t cw[8] = {t.c0.x, t.c0.y, t.c0.z, t.c0.w, t.c1.x, t.c1.y, t.c1.z, t.c1.w};
+    const uint32_t w = cw[i], w4 = w >> 4;
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t lo, hi;
+      look(__builtin_amdgcn_perm(w4, w, h ? 0x07030602u : 0x05010400u), lo, hi);
+      o[2 * h + 0] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+      o[2 * h + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+    }
+    *reinterpret_cast<u32x4 *>(&wn[tid * LD + ((8 * i) ^ wsw)]) = u32x4{o[0], o[1], o[2], o[3]};
+  };
+
+  // ---- prologue
+  constexpr int kReload3 = DQ ? 4 : 3;
+  P.issue(s0, 0);
+  issue_x(xs0, 0);
+  P.issue(s1, __builtin_amdgcn_readfirstlane(min(1, last)));
+  prep(s0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) word(s0, i, ws0);
+  P.issue(s0, __builtin_amdgcn_readfirstlane(min(2, last)));
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kReload3));
+  lds_barrier();
+
+  // Step s: four k-slices of sixteen MFMAs; slice c goes with two code words
+  // of step s + 1 (slice 0 also with building the products) and the fragment
+  // reads of slice c + 1.
+  auto step = [&](int s, const uint16_t *xc, const uint16_t *wc, uint16_t *xn, uint16_t *wn,
+                  typename RowProducer<DQ>::Set &set) {
+    issue_x(xn, s + 1);
+    Frag f0, f1;
+    read_f(f0, xc, wc, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      Frag &cur = (c & 1) ? f1 : f0;
+      Frag &nxt = (c & 1) ? f0 : f1;
+      if (c < 3) read_f(nxt, xc, wc, c + 1);
+      mma(cur);
+      if (c == 0) prep(set);
+      word(set, 2 * c, wn);
+      word(set, 2 * c + 1, wn);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    P.issue(set, __builtin_amdgcn_readfirstlane(min(s + 3, last)));
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload3));
+    lds_barrier();
+  };
+  int s = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    step(s, xs0, ws0, xs1, ws1, s1);
+    step(s + 1, xs1, ws1, xs0, ws0, s0);
+  }
+  if (s < nsteps) {
+    step(s, xs0, ws0, xs1, ws1, s1);
+    ++s;
+  }
+  // ---- adapter step: left operand in activation stage nsteps & 1; right
+  // operand row t of B (positions j < r, zero beyond) into weight stage
+  // nsteps & 1, eight 16-byte chunks per thread.
+  uint16_t *xa = (nsteps & 1) ? xs1 : xs0;
+  uint16_t *wa = (nsteps & 1) ? ws1 : ws0;
+  {
+    const int64_t gn = n0 + tid;
+    const rsrc_t rr = make_rsrc(a.R2, a.Nout * a.ldr2 * 2);
+    const bool vec = (a.r % 8) == 0 && (a.ldr2 % 8) == 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t v[16];
+      if (vec) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t j = 32 * half + 8 * q;
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+              rr, (j < a.r && gn < a.Nout) ? (uint32_t)((gn * a.ldr2 + j) * 2) : kOutOfRange, 0, 0);
+          v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+        }
+      } else {
+        uint32_t h[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int64_t j = 32 * half + i;
+          h[i] = __builtin_amdgcn_raw_buffer_load_b16(
+              rr, (j < a.r && gn < a.Nout) ? (uint32_t)((gn * a.ldr2 + j) * 2) : kOutOfRange, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = (h[2 * i] & 0xFFFFu) | (h[2 * i + 1] << 16);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x4 *>(&wa[tid * LD + ((32 * half + 8 * q) ^ wsw)]) =
+            u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  lds_barrier();
+  {
+    Frag f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      read_f(f, xa, wa, c);
+      mma(f);
+    }
+  }
+  lds_barrier();
+
+  // ---- store bf16 through LDS, one 32 x 128 block per wave at a time.
+  constexpr int kOutPitch = BN + 8;
+  const rsrc_t rout = make_rsrc(a.out + m0 * a.ldo, (a.M - m0) * a.ldo * 2);
+  const bool vec_ok = (a.ldo & 7) == 0 && ((uint64_t)a.out & 15) == 0;
+  uint16_t *blk = xs0 + wave * 32 * kOutPitch;
+#pragma unroll
+  for (int i = 0; i < TM3; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN3; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        blk[(8 * (e >> 2) + 4 * lh + (e & 3)) * kOutPitch + j * 32 + lr] = f32_to_bf16(acc[i][j][e]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 4 * q + (lane >> 4), c8 = 8 * (lane & 15);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&blk[row * kOutPitch + c8]);
+      const int64_t lrow = (int64_t)rh * 128 + i * 32 + row, gn = n0 + 128 * ch + c8;
+      if (vec_ok && gn + 8 <= a.Nout) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, rout, (uint32_t)((lrow * a.ldo + gn) * 2), 0, 0);
+      } else if (m0 + lrow < a.M) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (gn + t < a.Nout) a.out[(m0 + lrow) * a.ldo + gn + t] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
+      }
+    }
+  }
+}
+
 int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
 // Tiles, and the row-tile group size of the XCD-aware order: each XCD runs T/8
 // tiles; the group is chosen so that an XCD's share covers about as many
 // activation bytes (rows x Kc x 2) as weight bytes (columns x Kc / 2).
-bool plan(QGemmArgs &a) {
+bool plan(QGemmArgs &a, int bm = BM, int bn = BN) {
   // The adapter term is exactly one extra contraction step, and the producer
   // and MMA waves count their barriers on that: reject any other rank here.
   if (a.r < 1 || a.r > BK || a.Kc < BK || a.Kc % BK != 0) return false;
-  a.tiles_m = (int)cdiv(a.M, BM);
-  a.tiles_n = (int)cdiv(a.Nout, BN);
+  a.tiles_m = (int)cdiv(a.M, bm);
+  a.tiles_n = (int)cdiv(a.Nout, bn);
   const int T8 = std::max(1, a.tiles_m * a.tiles_n / 8);
   int best = 1;
   double best_cost = 1e300;
   for (int g = 1; g <= a.tiles_m; ++g) {
     const int cols = std::max(1, std::min(a.tiles_n, T8 / g));
-    const double cost = (double)g * BM * 2 + (double)cols * BN / 2;
+    const double cost = (double)g * bm * 2 + (double)cols * bn / 2;
     if (cost < best_cost) { best_cost = cost; best = g; }
   }
   a.group_m = best;
@@ -697,9 +1314,31 @@ bool plan(QGemmArgs &a) {
 // the end; each problem's workgroup range is rounded up to a multiple of 8 so
 // that the XCD-aware order within it holds (workgroups are dealt to the XCDs
 // round-robin by their global index).
+std::atomic<int> g_variant{0};   // 0 automatic, 1 256 x 128, 2 256 x 256 (8 waves), 3 256 x 256 (4 waves)
+
 template <bool KN, bool EPI_NK>
 hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
   if (n < 1 || n > QN_MAX_GROUP) return hipErrorInvalidValue;
+  // Tiling: the 256 x 256 one (forward only) when it gives the GPU at least
+  // two rounds of tiles, else the 256 x 128 one.
+  bool wide = false;
+  const int v = g_variant.load(std::memory_order_relaxed);
+  if (!KN) {
+    // Automatic choice: each tiling's time is its rounds of tiles over the
+    // compute units (one workgroup per CU) times the time of one tile; a
+    // 256 x 256 tile measures about 1.74 times a 256 x 128 one on the
+    // configured shapes (the same work per tile costs about 13 % less).
+    int64_t t1 = 0, t2 = 0;
+    for (int i = 0; i < n; ++i) {
+      t1 += cdiv(in[i].M, BM) * cdiv(in[i].Nout, BN);
+      t2 += cdiv(in[i].M, BM2) * cdiv(in[i].Nout, BN2);
+    }
+    const int64_t cus = device_cus();
+    const double c1 = (double)cdiv(t1, cus), c2 = 1.74 * (double)cdiv(t2, cus);
+    wide = v >= 2 || (v == 0 && c2 < c1);
+  }
+  const int wide_kind = v == 3 ? 3 : 2;
+  const int bm = wide ? BM2 : BM, bn = wide ? BN2 : BN;
   QGemmGroup grp{};
   int order[QN_MAX_GROUP];
   for (int i = 0; i < n; ++i) order[i] = i;
@@ -708,7 +1347,7 @@ hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
   int64_t total = 0;
   for (int k = 0; k < n; ++k) {
     QGemmArgs a = in[order[k]];
-    if ((a.absmax_q != nullptr) != dq || a.qtype != in[0].qtype || !plan(a)) return hipErrorInvalidValue;
+    if ((a.absmax_q != nullptr) != dq || a.qtype != in[0].qtype || !plan(a, bm, bn)) return hipErrorInvalidValue;
     grp.p[k] = a;
     grp.start[k] = (int)total;
     total += (int64_t)((a.tiles_m * a.tiles_n + 7) / 8) * 8;
@@ -718,6 +1357,18 @@ hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
   grp.n = n;
   const dim3 grid((unsigned)total);
   TraceScope tr(trace_kind, st);
+  if constexpr (!KN) {
+    if (wide && wide_kind == 3) {
+      if (dq) hipLaunchKernelGGL((qgemm3_kernel<true>), grid, dim3(kThreads3), 0, st, grp, code16(in[0].qtype));
+      else hipLaunchKernelGGL((qgemm3_kernel<false>), grid, dim3(kThreads3), 0, st, grp, code16(in[0].qtype));
+      return hipGetLastError();
+    }
+    if (wide) {
+      if (dq) hipLaunchKernelGGL((qgemm2_kernel<true>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      else hipLaunchKernelGGL((qgemm2_kernel<false>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      return hipGetLastError();
+    }
+  }
   if (dq)
     hipLaunchKernelGGL((qgemm_kernel<KN, true, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16(in[0].qtype));
   else
@@ -738,5 +1389,7 @@ hipError_t launch_qgemm_fwd_group(const QGemmArgs *a, int n, hipStream_t st) {
 hipError_t launch_qgemm_dx(const QGemmArgs &a, hipStream_t st) {
   return launch<true, false>(&a, 1, st, QN_TRACE_GEMM_DX);
 }
+
+void set_gemm_variant(int v) { g_variant.store(v, std::memory_order_relaxed); }
 
 }  // namespace qn

@@ -104,6 +104,7 @@ def load():
                                    vp, vp, ctypes.c_size_t, vp]),
         "qn_status_string": (ctypes.c_char_p, [i32]),
         "qn_trace_enable": (i32, [i32]),
+        "qn_set_gemm_variant": (i32, [i32]),
         "qn_trace_read": (i32, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float), i32]),
         "qn_version": (ctypes.c_char_p, []),
     }
@@ -118,7 +119,7 @@ def load():
 def exported_symbols():
     return ["qn_codebook", "qn_table", "qn_quantize_4bit", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_merge", "qn_adamw8_step", "qlora_workspace_size",
             "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_workspace_size_grouped",
-            "qlora_linear_fwd_grouped", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_trace_enable",
+            "qlora_linear_fwd_grouped", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_set_gemm_variant", "qn_trace_enable",
             "qn_trace_read"]
 
 
@@ -474,6 +475,11 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A, B, alpha, want_dX=True, use_double_
 
 TRACE_KINDS = {1: "quantize", 2: "double_quant", 3: "dequant", 4: "gemv", 5: "gemm_fwd", 6: "gemm_dx",
                7: "gemm_db", 8: "gemm_da", 9: "lowrank", 10: "merge", 11: "adamw8"}
+
+
+def set_gemm_variant(variant):
+    """Forward dequant-GEMM tiling for later calls: 0 automatic, 1 256x128, 2 256x256."""
+    _check("qn_set_gemm_variant", load().qn_set_gemm_variant(int(variant)))
 
 
 def trace_enable(on=True):

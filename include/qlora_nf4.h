@@ -325,6 +325,19 @@ int qlora_linear_bwd(const void *dY, const void *X, const float *H, int64_t M,
 int qn_trace_enable(int on);
 int qn_trace_read(int *kinds, float *ms, int cap);
 
+/* Tiling of the forward dequant-GEMM for the calls that follow, process-wide
+ * (for measurement and tests; results are the same either way up to the order
+ * of fp32 accumulation within a tile, which both tilings share):
+ *   0  automatic (the default): per launch, the tiling whose rounds of tiles
+ *      over the compute units, weighted by the measured time of one tile,
+ *      finish first (256 x 256 tiles for large launches, 256 x 128 for small
+ *      ones or where the wide tiles leave a partial round);
+ *   1  256 x 128 tiles: four MFMA waves and four dequantising waves;
+ *   2  256 x 256 tiles: eight waves that all multiply and dequantise;
+ *   3  256 x 256 tiles: four such waves, 128 x 128 each.
+ * QN_ERR_VALUE for any other value. */
+int qn_set_gemm_variant(int variant);
+
 /* Human-readable name of a qn_status (static storage). */
 const char *qn_status_string(int status);
 

@@ -1,0 +1,102 @@
+"""Both tilings of the forward dequant-GEMM against the oracle.
+
+The forward picks 256 x 256 tiles for launches with at least two tiles per
+compute unit and 256 x 128 tiles otherwise; qn_set_gemm_variant forces any of
+the three tilings (256 x 128 with producer waves, 256 x 256 with eight waves
+that all multiply and dequantise, 256 x 256 with four such waves).  Each case runs with both forced:
+ragged M and N (partial tiles in both directions), 1 to 5 contraction steps
+(the pipeline's prologue and the adapter step at both stage parities), ranks
+1 to 64, fp32 and 8-bit block scales, both 4-bit types, and a grouped launch.
+Y and H: relative Frobenius <= 5e-3 against the fp64 oracle and the
+elementwise bound, Y guard-banded; the two tilings also agree with each other
+within that bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_nf4_quantized_08_amd import lib, synth
+from tests.gpu_util import REL_FRO_TOL, dev, guarded, guards_intact, host, rel_fro, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _reset_variant():
+    yield
+    lib.set_gemm_variant(0)
+
+
+def _case(M, N, K, r, seed, qt="nf4", dq=True):
+    W = synth.gaussian((N, K), 0.02, synth.SEED_W + seed)
+    X = synth.to_bf16(synth.gaussian((M, K), 1.0, synth.SEED_X + seed))
+    A = synth.to_bf16(synth.gaussian((r, K), 0.01, synth.SEED_A + seed))
+    B = synth.to_bf16(synth.gaussian((N, r), 0.02, synth.SEED_B + seed))
+    w = lib.quantize_weight(to_dev(W), quant_type=qt)
+    p, a, _ = oracle.quantize(W, quant_type=qt)
+    scale = oracle.dq_absmax(*oracle.double_quant(a)) if dq else a
+    Wh = oracle.dequant_bf16_weight(p, N, K, scale, quant_type=qt)
+    return w, X, A, B, Wh
+
+
+def _fwd(w, X, A, B, alpha, dq):
+    M, N = X.shape[0], w.N
+    full, Y = guarded(M * N * 2, torch.bfloat16)
+    Y = Y.view(M, N)
+    Y, H = lib.qlora_linear_fwd(X.to(dev()), w, A.to(dev()), B.to(dev()), alpha, Y=Y, want_H=True,
+                                use_double_quant=dq)
+    assert guards_intact(full, M * N * 2), "Y guard band overwritten"
+    return host(Y), host(H)
+
+
+def _check(Y, H, X, A, B, Wh, alpha):
+    Xv, Av, Bv = (synth.bf16_values(t) for t in (X, A, B))
+    Yr, Hr = oracle.forward(Xv, Wh, Av, Bv, alpha)
+    assert rel_fro(Y, Yr) <= REL_FRO_TOL
+    assert rel_fro(H, Hr) <= REL_FRO_TOL
+    s = alpha / A.shape[0]
+    bound = np.abs(Xv.astype(np.float64)) @ np.abs(Wh.astype(np.float64)).T + s * np.abs(Hr) @ np.abs(Bv).T
+    assert np.all(np.abs(Y - Yr) <= 2 * 2.0 ** -8 * bound + 1e-30)
+
+
+@pytest.mark.parametrize("M,N,K,r,qt,dq", [
+    (300, 320, 512, 16, "nf4", True),
+    (77, 192, 64, 8, "nf4", True),       # one contraction step
+    (257, 256, 128, 64, "nf4", False),   # two steps, fp32 scales
+    (513, 576, 192, 24, "fp4", True),    # three steps
+    (256, 64, 256, 1, "nf4", True),
+    (130, 448, 320, 40, "nf4", False),   # five steps
+    (1024, 1024, 2048, 16, "nf4", True),
+])
+def test_both_tilings_match_the_oracle(M, N, K, r, qt, dq):
+    w, X, A, B, Wh = _case(M, N, K, r, seed=M + N + K, qt=qt, dq=dq)
+    out = {}
+    for v in (1, 2, 3):
+        say(f"tiling {v}: M={M} N={N} K={K} r={r} {qt} dq={dq}")
+        lib.set_gemm_variant(v)
+        out[v] = _fwd(w, X, A, B, 2.0 * r, dq)
+        _check(*out[v], X, A, B, Wh, 2.0 * r)
+
+
+@pytest.mark.parametrize("variant", [2, 3])
+def test_wide_tiling_grouped_launch(variant):
+    """A grouped launch of three problems on a 256 x 256 tiling equals the
+    single calls on it bit for bit, and the oracle within the bars."""
+    lib.set_gemm_variant(variant)
+    cases = [_case(300, 320, 512, 16, seed=1), _case(700, 1024, 256, 64, seed=2), _case(65, 64, 192, 8, seed=3)]
+    items, outs = [], []
+    for (w, X, A, B, Wh) in cases:
+        M, N = X.shape[0], w.N
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+        H = torch.empty((M, A.shape[0]), dtype=torch.float32, device=dev())
+        items.append((X.to(dev()), w, A.to(dev()), B.to(dev()), 2.0 * A.shape[0], Y, H))
+    say("wide tiling grouped")
+    lib.FwdGroup(items).run()
+    torch.cuda.synchronize()
+    for (X, w, A, B, alpha, Y, H), (_, Xh, Ah, Bh, Wh) in zip(items, cases):
+        Y1, H1 = lib.qlora_linear_fwd(X, w, A, B, alpha, want_H=True)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y1) and torch.equal(H, H1)
+        _check(host(Y), host(H), Xh, Ah, Bh, Wh, alpha)
