@@ -379,6 +379,9 @@ def main():
     # one call over all 7 linears
     pre_us = graph_time_us(torch, cap, lambda: [grp.run() for grp in pre_groups])
     dec_us = graph_time_us(torch, cap, lambda: [grp.run() for grp in dec_groups])
+    dec_single_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_DEC))
+    dec_all7 = L.groups(lib, M70_DEC, [tuple(L70B)])
+    dec_all7_us = graph_time_us(torch, cap, lambda: dec_all7[0].run())
     pre_single_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE))
     pre_all7_us = graph_time_us(torch, cap, lambda: all7[0].run())
     tilings = {}
@@ -475,6 +478,8 @@ def main():
                                                                "automatic": round(flops_pre / pre_us / 1e6, 1)},
                             "decode_M1_us": round(dec_us, 2),
                             "decode_M1_weight_GBps": round(weight_bytes / dec_us / 1e3, 1),
+                            "decode_M1_single_calls_weight_GBps": round(weight_bytes / dec_single_us / 1e3, 1),
+                            "decode_M1_one_call_all7_weight_GBps": round(weight_bytes / dec_all7_us / 1e3, 1),
                             "per_linear": per_linear,
                             "dequant_rel_rmse": {k: round(v, 6) for k, v in quality.items()},
                             "merge_export_bf16": merge,

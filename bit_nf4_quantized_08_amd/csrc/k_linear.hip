@@ -159,22 +159,43 @@ __device__ __forceinline__ float wave_sum_multi(float (&v)[MM], int lane) {
   return t;
 }
 
+// Several decode problems in one launch: workgroups [start[g], start[g+1])
+// run problem g (its H blocks first, then its row blocks).
+struct GemvGroup {
+  GemvArgs p[QN_MAX_GROUP];
+  int start[QN_MAX_GROUP + 1];
+  int n;
+};
+
 template <int MM, bool DQ, int KW>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
+__device__ __forceinline__ void gemv_body(const GemvArgs &a, int block, const uint32_t *pairs);
+
+template <int MM, bool DQ, int KW>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvGroup g, Code16 cb) {
   __shared__ uint32_t pairs[256];  // byte -> bf16(row lo) | bf16(row hi) << 16
   {
     const uint32_t v = threadIdx.x;
     pairs[v] = pack_bf16x2(cb.v[v & 15], cb.v[v >> 4]);
   }
   __syncthreads();
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < QN_MAX_GROUP; ++i) gi += (i < g.n && (int)blockIdx.x >= g.start[i]) ? 1 : 0;
+  gi = __builtin_amdgcn_readfirstlane(gi);
+  const GemvArgs a = g.p[gi];
+  gemv_body<MM, DQ, KW>(a, (int)blockIdx.x - g.start[gi], pairs);
+}
+
+template <int MM, bool DQ, int KW>
+__device__ __forceinline__ void gemv_body(const GemvArgs &a, int block, const uint32_t *pairs) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  if ((int)blockIdx.x < a.h_blocks) {
+  if (block < a.h_blocks) {
     // ---- H partials (see above).
-    const int hb = (int)blockIdx.x % a.hsplits;
+    const int hb = block % a.hsplits;
     const int64_t kb = (int64_t)hb * a.hk_per_split;
     const int64_t ke = min(a.K, kb + a.hk_per_split);
-    const int j = 4 * ((int)blockIdx.x / a.hsplits) + wave;
+    const int j = 4 * (block / a.hsplits) + wave;
     if (j < a.r) {
       float hm[MM];
 #pragma unroll
@@ -205,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
   }
 
   static_assert(KW * MM <= 4 || KW == 1, "activation registers");
-  const int64_t v = (int64_t)((int)blockIdx.x - a.h_blocks) * (kThreads / 64) + wave;
+  const int64_t v = (int64_t)(block - a.h_blocks) * (kThreads / 64) + wave;
   const int split = (int)(v % a.splits);
   const int64_t n_first = v / a.splits;
   if (n_first >= a.row_waves) return;
@@ -337,14 +358,42 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, Code16 cb) {
 // eight partial sums are added with lane shuffles.
 constexpr int EPI_ROWS = kThreads / 8;
 
-__global__ __launch_bounds__(kThreads) void gemv_epilogue_kernel(const float *__restrict__ y_part, int splits,
-                                                                 const float *__restrict__ h_part, int hsplits,
-                                                                 int64_t M, int64_t N, int64_t r,
-                                                                 const uint16_t *__restrict__ B, float s_lora,
-                                                                 uint16_t *__restrict__ Y, float *H_out) {
+struct EpiArgs {
+  const float *y_part;
+  int splits;
+  const float *h_part;
+  int hsplits;
+  int64_t M, N, r;
+  const uint16_t *B;
+  float s_lora;
+  uint16_t *Y;
+  float *H_out;
+};
+struct EpiGroup {
+  EpiArgs p[QN_MAX_GROUP];
+  int start[QN_MAX_GROUP + 1];   // N / EPI_ROWS workgroups per problem
+  int n;
+};
+
+__global__ __launch_bounds__(kThreads) void gemv_epilogue_kernel(EpiGroup g) {
   __shared__ float Hs[8 * 64];          // H[m][j], zero for j >= r
   __shared__ float Ls[8 * EPI_ROWS];    // sum_j H[m][j] B[n][j] for the workgroup's rows
-  const int64_t n0 = (int64_t)blockIdx.x * EPI_ROWS;
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < QN_MAX_GROUP; ++i) gi += (i < g.n && (int)blockIdx.x >= g.start[i]) ? 1 : 0;
+  gi = __builtin_amdgcn_readfirstlane(gi);
+  const EpiArgs ea = g.p[gi];
+  const float *__restrict__ y_part = ea.y_part;
+  const int splits = ea.splits;
+  const float *__restrict__ h_part = ea.h_part;
+  const int hsplits = ea.hsplits;
+  const int64_t M = ea.M, N = ea.N, r = ea.r;
+  const uint16_t *__restrict__ B = ea.B;
+  const float s_lora = ea.s_lora;
+  uint16_t *__restrict__ Y = ea.Y;
+  float *H_out = ea.H_out;
+  const int eblock = (int)blockIdx.x - g.start[gi];
+  const int64_t n0 = (int64_t)eblock * EPI_ROWS;
   // The split sums of this thread's outputs first, so that their loads
   // overlap those of H and B.
   float ysum[(8 * EPI_ROWS + kThreads - 1) / kThreads];
@@ -365,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void gemv_epilogue_kernel(const float *__
       for (int s = 0; s < hsplits; ++s) v += h_part[((int64_t)s * M + m) * 64 + j];
     }
     Hs[idx] = v;
-    if (H_out && blockIdx.x == 0 && j < r) H_out[m * r + j] = v;
+    if (H_out && eblock == 0 && j < r) H_out[m * r + j] = v;
   }
   const int t = threadIdx.x, row = t >> 3, j0 = 8 * (t & 7);
   const int64_t n = n0 + row;  // N % EPI_ROWS == 0
@@ -527,30 +576,68 @@ static void fwd_mfma_args(const FwdArgs &a, LowRankArgs &la, QGemmArgs &g) {
   g.out = a.Y; g.ldo = a.N;
 }
 
-hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
+// Launch arguments of one decode-path problem (its workspace carved from a.ws).
+struct DecodePlan {
+  const void *fn;      // kernel instance (rows of X, scale source, chunks per segment)
+  GemvArgs ga;
+  EpiArgs ea;
+  int blocks;          // H blocks + row blocks
+  int qtype;
+};
+
+static DecodePlan decode_plan(const FwdArgs &a) {
   Carve c(a.ws);
+  DecodePlan d;
+  GemvPlan p = gemv_plan(a.M, a.N, a.K);
+  const int64_t kw = p.kps / 2048;
+  d.fn = a.sc.absmax_q ? gemv_fn<true>(a.M, kw) : gemv_fn<false>(a.M, kw);
+  gemv_rows(p, a.N, d.fn);
+  float *y_part = c.take<float>((int64_t)p.splits * a.M * a.N);
+  float *h_part = c.take<float>((int64_t)p.hsplits * a.M * 64);
+  const int h_blocks = p.hsplits * (int)cdiv(a.r, 4);
+  d.ga = GemvArgs{a.X, a.M, a.N, a.K, a.codes, a.sc, a.A, a.r, y_part, h_part, p.kps, p.splits, p.row_waves,
+                  h_blocks, p.hsplits, p.hkps};
+  d.ea = EpiArgs{y_part, p.splits, h_part, p.hsplits, a.M, a.N, a.r, a.B, a.s, a.Y, a.H_out};
+  d.blocks = h_blocks + p.row_wgs;
+  d.qtype = a.sc.qtype;
+  return d;
+}
+
+// One streaming launch and one epilogue launch over n decode problems that
+// share the kernel instance and the 4-bit type.
+static hipError_t launch_decode(const DecodePlan *d, int n, hipStream_t st) {
+  GemvGroup gg{};
+  EpiGroup eg{};
+  int64_t gb = 0, eb = 0;
+  for (int i = 0; i < n; ++i) {
+    gg.p[i] = d[i].ga;
+    gg.start[i] = (int)gb;
+    gb += d[i].blocks;
+    eg.p[i] = d[i].ea;
+    eg.start[i] = (int)eb;
+    eb += d[i].ea.N / EPI_ROWS;
+  }
+  for (int k = n; k <= QN_MAX_GROUP; ++k) {
+    gg.start[k] = (int)gb;
+    eg.start[k] = (int)eb;
+  }
+  gg.n = eg.n = n;
+  const Code16 cb = code16(d[0].qtype);
+  {
+    // The trace brackets the streaming kernel alone, not the epilogue.
+    TraceScope tr(QN_TRACE_GEMV, st);
+    void *args[] = {&gg, const_cast<Code16 *>(&cb)};
+    QN_TRY(hipLaunchKernel(d[0].fn, dim3((unsigned)gb), dim3(kThreads), args, 0, st));
+  }
+  QN_TRY(hipGetLastError());
+  hipLaunchKernelGGL(gemv_epilogue_kernel, dim3((unsigned)eb), dim3(kThreads), 0, st, eg);
+  return hipGetLastError();
+}
+
+hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
   if (a.M <= GEMV_MAX_M) {
-    GemvPlan p = gemv_plan(a.M, a.N, a.K);
-    const int64_t kw = p.kps / 2048;
-    const void *fn = a.sc.absmax_q ? gemv_fn<true>(a.M, kw) : gemv_fn<false>(a.M, kw);
-    gemv_rows(p, a.N, fn);
-    float *y_part = c.take<float>((int64_t)p.splits * a.M * a.N);
-    float *h_part = c.take<float>((int64_t)p.hsplits * a.M * 64);
-    const int h_blocks = p.hsplits * (int)cdiv(a.r, 4);
-    GemvArgs ga{a.X, a.M, a.N, a.K, a.codes, a.sc, a.A, a.r, y_part, h_part, p.kps, p.splits, p.row_waves,
-                h_blocks, p.hsplits, p.hkps};
-    dim3 grid((unsigned)(h_blocks + p.row_wgs));
-    const Code16 cb = code16(a.sc.qtype);
-    {
-      // The trace brackets the streaming kernel alone, not the epilogue.
-      TraceScope tr(QN_TRACE_GEMV, st);
-      void *args[] = {&ga, const_cast<Code16 *>(&cb)};
-      QN_TRY(hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, st));
-    }
-    QN_TRY(hipGetLastError());
-    hipLaunchKernelGGL(gemv_epilogue_kernel, dim3((unsigned)(a.N / EPI_ROWS)), dim3(kThreads), 0, st,
-                       y_part, p.splits, h_part, p.hsplits, a.M, a.N, a.r, a.B, a.s, a.Y, a.H_out);
-    return hipGetLastError();
+    const DecodePlan d = decode_plan(a);
+    return launch_decode(&d, 1, st);
   }
   // MFMA path: H = X A^T (low-rank kernel) -> sH bf16 -> tile GEMM with the
   // adapter term as extra contraction steps.
@@ -565,11 +652,25 @@ hipError_t run_fwd_group(const FwdArgs *a, int n, hipStream_t st) {
   LowRankArgs la[QN_MAX_GROUP];
   QGemmArgs g[4][QN_MAX_GROUP];   // [2 * (4-bit type) + (double-quantised scales?)][problem]
   int nl = 0, ng[4] = {0, 0, 0, 0};
+  // Decode-path problems: one launch pair per kernel instance and type.
+  DecodePlan dp[QN_MAX_GROUP];
+  bool done[QN_MAX_GROUP] = {};
+  int nd = 0;
+  for (int i = 0; i < n; ++i)
+    if (a[i].M <= GEMV_MAX_M) dp[nd++] = decode_plan(a[i]);
+  for (int i = 0; i < nd; ++i) {
+    if (done[i]) continue;
+    DecodePlan batch[QN_MAX_GROUP];
+    int nb = 0;
+    for (int k = i; k < nd; ++k)
+      if (!done[k] && dp[k].fn == dp[i].fn && dp[k].qtype == dp[i].qtype) {
+        batch[nb++] = dp[k];
+        done[k] = true;
+      }
+    QN_TRY(launch_decode(batch, nb, st));
+  }
   for (int i = 0; i < n; ++i) {
-    if (a[i].M <= GEMV_MAX_M) {
-      QN_TRY(run_fwd(a[i], st));
-      continue;
-    }
+    if (a[i].M <= GEMV_MAX_M) continue;
     const int kind = 2 * (a[i].sc.qtype == QN_FP4) + (a[i].sc.absmax_q != nullptr);
     fwd_mfma_args(a[i], la[nl], g[kind][ng[kind]]);
     ++nl;

@@ -89,3 +89,15 @@ def test_layer_group_matches_single_calls(layer):
     probs = [_problem(N, K, M, r, seed=300 + i, w_std=std) for i, (N, K) in enumerate(cfg["linears"].values())]
     items, outs = _run_grouped(probs)
     _check_against_single_calls(probs, items, outs)
+
+
+@pytest.mark.parametrize("layer,M", [("70b", 1), ("qwen", 2), ("qwen", 8)])
+def test_decode_group_matches_single_calls(layer, M):
+    """All seven linears of a layer on the decode path (M <= 8) in one grouped
+    call: the linears that share a kernel instance run as one streaming launch
+    and one epilogue launch; every Y and H equals the single calls bit for bit."""
+    cfg, r, std = (synth.L70B, 64, 0.015) if layer == "70b" else (synth.QWEN7B, 16, 0.02)
+    say(f"grouped decode {layer} layer M={M}")
+    probs = [_problem(N, K, M, r, seed=400 + i, w_std=std) for i, (N, K) in enumerate(cfg["linears"].values())]
+    items, outs = _run_grouped(probs)
+    _check_against_single_calls(probs, items, outs)
