@@ -375,28 +375,9 @@ def main():
     step_flops = L.flops(M70_DEC) + L.flops(M70_PRE)
     value = step_flops / (ms_step * 1e-3) / 1e12
 
-    # the two halves of the step alone, and the forward as 7 single calls and as
-    # one call over all 7 linears
+    # the two halves of the step alone
     pre_us = graph_time_us(torch, cap, lambda: [grp.run() for grp in pre_groups])
-    dec_us = graph_time_us(torch, cap, lambda: [grp.run() for grp in dec_groups])
-    dec_single_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_DEC))
-    dec_all7 = L.groups(lib, M70_DEC, [tuple(L70B)])
-    dec_all7_us = graph_time_us(torch, cap, lambda: dec_all7[0].run())
-    pre_single_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE))
-    pre_all7_us = graph_time_us(torch, cap, lambda: all7[0].run())
-    tilings = {}
-    for v in (1, 2, 3):
-        lib.set_gemm_variant(v)
-        tilings[v] = graph_time_us(torch, cap, lambda: [grp.run() for grp in pre_groups])
-    lib.set_gemm_variant(0)
-    per_linear = {}
-    for it in L.items:
-        us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE, [it]))
-        dus = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_DEC, [it]), replays=20)
-        per_linear[it["name"]] = {"prefill_us": round(us, 1),
-                                  "prefill_TFLOPs": round(fwd_flops(M70_PRE, it["N"], it["K"], R70) / us / 1e6, 1),
-                                  "decode_us": round(dus, 2),
-                                  "decode_weight_GBps": round(nf4_bytes(it["N"], it["K"]) / dus / 1e3, 1)}
+    dec_us = graph_time_us(torch, cap, lambda: [grp.run() for grp in dec_groups], replays=20)
 
     # kernel trace over one eager step
     # One untraced step first: while the GPU runs its M = 4096 GEMMs the host
@@ -435,56 +416,34 @@ def main():
                      "launches": len(gemv), "avg_ms": round(sum(gemv) / len(gemv), 5),
                      "note": "the streaming kernel alone (its epilogue launch excluded); bytes = NF4 weights + "
                              "x + y + A read by the H blocks"}
-    # merge/export of the layer's adapters into bf16 weights (one call per linear)
-    mo = {it["name"]: torch.empty((it["N"], it["K"]), dtype=torch.bfloat16, device=dev) for it in L.items}
-    merge_us = graph_time_us(torch, cap, lambda: [lib.qlora_merge(it["w"], it["A"], it["B"], L.alpha, out=mo[it["name"]])
-                                                  for it in L.items], replays=3)
-    n_el = sum(it["N"] * it["K"] for it in L.items)
-    merge_bytes = sum(nf4_bytes(it["N"], it["K"]) + 2 * it["N"] * it["K"] + 2 * R70 * (it["N"] + it["K"])
-                      for it in L.items)
-    merge = {"us": round(merge_us, 1), "GBps": round(merge_bytes / merge_us / 1e3, 1),
-             "fma_TFLOPs": round(2 * R70 * n_el / merge_us / 1e6, 1),
-             "alu_frac": round(2 * R70 * n_el / merge_us / 1e6 / PEAK_FP32_TFLOPS, 4),
-             "note": "all 7 linears merged to bf16 (r = 64): r fused multiply-adds per weight, bound by the fp32 "
-                     "vector rate (157.3 TFLOP/s) rather than by its bytes"}
-    del mo
-    # one 8-bit AdamW step over the layer's adapters (A and B of every linear)
-    ad_t = [(t, t.clone(), lib.AdamW8State(t.numel(), dev)) for it in L.items for t in (it["A"], it["B"])]
-    ad_n = sum(t.numel() for t, _, _ in ad_t)
-    for t, gr, stt in ad_t:
-        lib.adamw8_step(t, gr, stt, lr=1e-4, step=1)
-    adam_us = graph_time_us(torch, cap, lambda: [lib.adamw8_step(t, gr, stt, lr=1e-4, step=2) for t, gr, stt in ad_t],
-                            replays=10)
-    adam_bytes = ad_n * (2 + 2 + 2 + 2 + 1 + 1) + 2 * 2 * 4 * ((ad_n + 63) // 64)
-    adamw8 = {"us": round(adam_us, 2), "params": ad_n, "GBps": round(adam_bytes / adam_us / 1e3, 1),
-              "hbm_frac": round(adam_bytes / adam_us / 1e3 / PEAK_HBM_GBPS, 4),
-              "state_bytes_per_param": 2.125,
-              "note": "14 calls (A and B of the 7 linears, r = 64); bytes = bf16 parameter read and written, bf16 "
-                      "gradient, both 8-bit codes read and written, block steps"}
-    del ad_t
-    quality = L.quality
+    lowr = kern.get("lowrank", [])
+    lowrank_roof = None
+    if lowr:
+        # per problem: X read once, A read, H written fp32 and bf16(s H)
+        lr_bytes = sum(2 * M70_PRE * it["K"] + 2 * R70 * it["K"] + 6 * M70_PRE * R70 for it in L.items)
+        a = lr_bytes / (sum(lowr) * 1e-3) / 1e9
+        lowrank_roof = {"kernel": "lowrank", "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBPS,
+                        "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4), "launches": len(lowr),
+                        "launch_ms": [round(x, 5) for x in lowr],
+                        "note": "H = X A^T of the prefill step, one launch per dependency group (its finishing "
+                                "launch excluded); bytes = X, A and H per linear"}
+    flops_pre = sum(fwd_flops(M70_PRE, n_, k_, R70) for n_, k_ in L70B.values())
     weight_bytes = L.weight_bytes()
+    layer_stage = {}
+    if not args.no_stages:
+        layer_stage = layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weight_bytes, pre_us)
+    quality = L.quality
     del L
     torch.cuda.empty_cache()
 
-    flops_pre = sum(fwd_flops(M70_PRE, n_, k_, R70) for n_, k_ in L70B.values())
     stages = {"70b_layer": {"prefill_M4096_us": round(pre_us, 1),
                             "prefill_M4096_TFLOPs": round(flops_pre / pre_us / 1e6, 1),
-                            "prefill_M4096_single_calls_TFLOPs": round(flops_pre / pre_single_us / 1e6, 1),
-                            "prefill_M4096_one_call_all7_TFLOPs": round(flops_pre / pre_all7_us / 1e6, 1),
-                            "prefill_M4096_TFLOPs_by_tiling": {"256x128": round(flops_pre / tilings[1] / 1e6, 1),
-                                                               "256x256_8waves": round(flops_pre / tilings[2] / 1e6, 1),
-                                                               "256x256_4waves": round(flops_pre / tilings[3] / 1e6, 1),
-                                                               "automatic": round(flops_pre / pre_us / 1e6, 1)},
                             "decode_M1_us": round(dec_us, 2),
                             "decode_M1_weight_GBps": round(weight_bytes / dec_us / 1e3, 1),
-                            "decode_M1_single_calls_weight_GBps": round(weight_bytes / dec_single_us / 1e3, 1),
-                            "decode_M1_one_call_all7_weight_GBps": round(weight_bytes / dec_all7_us / 1e3, 1),
-                            "per_linear": per_linear,
                             "dequant_rel_rmse": {k: round(v, 6) for k, v in quality.items()},
-                            "merge_export_bf16": merge,
-                            "adamw8_adapter_step": adamw8,
-                            "gemv_roofline": gemv_roof}}
+                            "gemv_roofline": gemv_roof,
+                            "lowrank_roofline": lowrank_roof}}
+    stages["70b_layer"].update(layer_stage)
     metrics = {"prefill_dequant_gemm_TFLOPs": round(flops_pre / pre_us / 1e6, 1),
                "decode_gemv_weight_GBps": round(weight_bytes / dec_us / 1e3, 1)}
 
@@ -525,6 +484,70 @@ def main():
         torch.cuda.synchronize()
         print("copy calibration: 3 x 268435456 B read + written", file=sys.stderr, flush=True)
 
+
+
+def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weight_bytes, pre_us):
+    """The 70B layer's other timings: the forward as 7 single calls and as one
+    call over all 7 linears, each forward tiling, each linear alone, the merge
+    of all adapters into bf16 weights and one 8-bit AdamW step over them."""
+    log("70B layer: single calls, tilings, per linear, merge, AdamW")
+    dec_single_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_DEC), replays=20)
+    dec_all7 = L.groups(lib, M70_DEC, [tuple(L70B)])
+    dec_all7_us = graph_time_us(torch, cap, lambda: dec_all7[0].run(), replays=20)
+    pre_single_us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE))
+    pre_all7_us = graph_time_us(torch, cap, lambda: all7[0].run())
+    tilings = {}
+    for v in (1, 2, 3):
+        lib.set_gemm_variant(v)
+        tilings[v] = graph_time_us(torch, cap, lambda: [grp.run() for grp in pre_groups])
+    lib.set_gemm_variant(0)
+    per_linear = {}
+    for it in L.items:
+        us = graph_time_us(torch, cap, lambda: L.fwd(lib, M70_PRE, [it]))
+        # ten calls per graph: one small call is shorter than a graph launch
+        dus = graph_time_us(torch, cap, lambda: [L.fwd(lib, M70_DEC, [it]) for _ in range(10)], replays=5, calls=10)
+        per_linear[it["name"]] = {"prefill_us": round(us, 1),
+                                  "prefill_TFLOPs": round(fwd_flops(M70_PRE, it["N"], it["K"], R70) / us / 1e6, 1),
+                                  "decode_us": round(dus, 2),
+                                  "decode_weight_GBps": round(nf4_bytes(it["N"], it["K"]) / dus / 1e3, 1)}
+    # merge/export of the layer's adapters into bf16 weights (one call per linear)
+    mo = {it["name"]: torch.empty((it["N"], it["K"]), dtype=torch.bfloat16, device=dev) for it in L.items}
+    merge_us = graph_time_us(torch, cap, lambda: [lib.qlora_merge(it["w"], it["A"], it["B"], L.alpha, out=mo[it["name"]])
+                                                  for it in L.items], replays=3)
+    n_el = sum(it["N"] * it["K"] for it in L.items)
+    merge_bytes = sum(nf4_bytes(it["N"], it["K"]) + 2 * it["N"] * it["K"] + 2 * R70 * (it["N"] + it["K"])
+                      for it in L.items)
+    merge = {"us": round(merge_us, 1), "GBps": round(merge_bytes / merge_us / 1e3, 1),
+             "fma_TFLOPs": round(2 * R70 * n_el / merge_us / 1e6, 1),
+             "alu_frac": round(2 * R70 * n_el / merge_us / 1e6 / PEAK_FP32_TFLOPS, 4),
+             "note": "all 7 linears merged to bf16 (r = 64): r fused multiply-adds per weight, bound by the fp32 "
+                     "vector rate (157.3 TFLOP/s) rather than by its bytes"}
+    del mo
+    # one 8-bit AdamW step over the layer's adapters (A and B of every linear)
+    ad_t = [(t, t.clone(), lib.AdamW8State(t.numel(), dev)) for it in L.items for t in (it["A"], it["B"])]
+    ad_n = sum(t.numel() for t, _, _ in ad_t)
+    for t, gr, stt in ad_t:
+        lib.adamw8_step(t, gr, stt, lr=1e-4, step=1)
+    adam_us = graph_time_us(torch, cap, lambda: [lib.adamw8_step(t, gr, stt, lr=1e-4, step=2) for t, gr, stt in ad_t],
+                            replays=10)
+    adam_bytes = ad_n * (2 + 2 + 2 + 2 + 1 + 1) + 2 * 2 * 4 * ((ad_n + 63) // 64)
+    adamw8 = {"us": round(adam_us, 2), "params": ad_n, "GBps": round(adam_bytes / adam_us / 1e3, 1),
+              "hbm_frac": round(adam_bytes / adam_us / 1e3 / PEAK_HBM_GBPS, 4),
+              "state_bytes_per_param": 2.125,
+              "note": "14 calls (A and B of the 7 linears, r = 64); bytes = bf16 parameter read and written, bf16 "
+                      "gradient, both 8-bit codes read and written, block steps"}
+    del ad_t
+    f, w = flops_pre, weight_bytes
+    return {"prefill_M4096_single_calls_TFLOPs": round(f / pre_single_us / 1e6, 1),
+            "prefill_M4096_one_call_all7_TFLOPs": round(f / pre_all7_us / 1e6, 1),
+            "prefill_M4096_TFLOPs_by_tiling": {
+                "256x128": round(f / tilings[1] / 1e6, 1), "256x256_8waves": round(f / tilings[2] / 1e6, 1),
+                "256x256_4waves": round(f / tilings[3] / 1e6, 1), "automatic": round(f / pre_us / 1e6, 1)},
+            "decode_M1_single_calls_weight_GBps": round(w / dec_single_us / 1e3, 1),
+            "decode_M1_one_call_all7_weight_GBps": round(w / dec_all7_us / 1e3, 1),
+            "per_linear": per_linear,
+            "merge_export_bf16": merge,
+            "adamw8_adapter_step": adamw8}
 
 
 def other_stages(torch, lib, dev, cap, log):

@@ -34,6 +34,8 @@ int check_linear_shapes(int64_t M, const qn_nf4_weight *W, int64_t r, float alph
   // The GEMM kernels address the code array with 32-bit byte offsets (the
   // transposed reader of the backward spans all of it): N*K/2 bytes must fit.
   if (W->N * W->K / 2 > (int64_t)INT32_MAX) return QN_ERR_SHAPE;
+  // The low-rank kernels address 128 rows of X (or dY) with 32-bit offsets.
+  if (W->K > (int64_t)1 << 23 || W->N > (int64_t)1 << 23) return QN_ERR_SHAPE;
   if (M > kMaxElems / W->K || M > kMaxElems / W->N) return QN_ERR_SHAPE;
   if (M > INT32_MAX / 64 || W->N > INT32_MAX / 64) return QN_ERR_SHAPE;
   if (!std::isfinite(alpha)) return QN_ERR_VALUE;

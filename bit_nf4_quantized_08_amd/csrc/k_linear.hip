@@ -553,6 +553,7 @@ size_t fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
     c.take<float>((int64_t)p.hsplits * M * 64);
   } else {
     c.take<uint16_t>(M * align_up(r, 8));
+    c.take<char>((int64_t)lowrank_part_bytes(M, K, r));
   }
   return c.off;
 }
@@ -564,10 +565,11 @@ static void fwd_mfma_args(const FwdArgs &a, LowRankArgs &la, QGemmArgs &g) {
   Carve c(a.ws);
   const int64_t rp = align_up(a.r, 8);
   uint16_t *sH = c.take<uint16_t>(a.M * rp);
+  float *part = reinterpret_cast<float *>(c.take<char>((int64_t)lowrank_part_bytes(a.M, a.K, a.r)));
   la = LowRankArgs{};
   la.L = a.X; la.ldl = a.K; la.M = a.M; la.Kc = a.K;
   la.P = a.A; la.ldp = a.K; la.R = a.r; la.scale = a.s;
-  la.out_f32 = a.H_out; la.out_b = sH; la.ldb = rp; la.out_t = nullptr; la.Mp = a.M;
+  la.out_f32 = a.H_out; la.out_b = sH; la.ldb = rp; la.out_t = nullptr; la.Mp = a.M; la.part = part;
   g = QGemmArgs{};
   g.L = a.X; g.ldl = a.K; g.M = a.M; g.Nout = a.N; g.Kc = a.K;
   g.codes = a.codes; g.absmax = a.sc.absmax; g.absmax_q = a.sc.absmax_q; g.scale2 = a.sc.scale2;
@@ -694,6 +696,8 @@ size_t bwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
   c.take<uint16_t>(rp * Mp);                // (sH)^T bf16 [rp, Mp]
   c.take<float>((int64_t)colred_splits(M) * r * N);   // dB partials
   c.take<float>((int64_t)colred_splits(M) * r * K);   // dA partials
+  c.take<char>((int64_t)lowrank_part_bytes(M, N, r));  // dH partial products
+  c.take<char>((int64_t)lowrank_part_bytes(M, K, r));  // H partial products (H not given)
   return c.off;
 }
 
@@ -707,6 +711,8 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
   uint16_t *sHt = c.take<uint16_t>(rp * Mp);
   float *bpart = c.take<float>((int64_t)colred_splits(a.M) * a.r * a.N);
   float *apart = c.take<float>((int64_t)colred_splits(a.M) * a.r * a.K);
+  float *dhpart = reinterpret_cast<float *>(c.take<char>((int64_t)lowrank_part_bytes(a.M, a.N, a.r)));
+  float *hpart = reinterpret_cast<float *>(c.take<char>((int64_t)lowrank_part_bytes(a.M, a.K, a.r)));
 
   // B^T [rp, N] (rows >= r zero) so that dH = dY (B^T)^T runs on the low-rank
   // kernel; with the forward's H given, (sH)^T from it in the same launch.
@@ -722,10 +728,10 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
     LowRankArgs ld{}, lh{};
     ld.L = a.dY; ld.ldl = a.N; ld.M = a.M; ld.Kc = a.N;
     ld.P = Bt; ld.ldp = a.N; ld.R = a.r; ld.scale = a.s;
-    ld.out_b = dHb; ld.ldb = rp; ld.out_t = dHt; ld.ldt_rows = rp; ld.Mp = Mp;
+    ld.out_b = dHb; ld.ldb = rp; ld.out_t = dHt; ld.ldt_rows = rp; ld.Mp = Mp; ld.part = dhpart;
     lh.L = a.X; lh.ldl = a.K; lh.M = a.M; lh.Kc = a.K;
     lh.P = a.A; lh.ldp = a.K; lh.R = a.r; lh.scale = a.s;
-    lh.out_t = sHt; lh.ldt_rows = rp; lh.Mp = Mp;
+    lh.out_t = sHt; lh.ldt_rows = rp; lh.Mp = Mp; lh.part = hpart;
     QN_TRY(launch_lowrank2(ld, a.H ? nullptr : &lh, st));
   }
 

@@ -7,16 +7,22 @@
 // product through them is cheap next to the base weight, and this kernel
 // streams the activations once at HBM rate.
 //
-// A workgroup of 8 waves owns 16 rows.  The contraction is cut into 32-wide
-// chunks dealt round-robin to the 8 waves; each wave accumulates its chunks with
-// v_mfma_f32_16x16x32_bf16 (lane group g = lane/16 takes indices [8g, 8g+8) of
-// a chunk for both operands), keeping 16 / RT chunks of loads in flight.  The 8
-// partial 16 x R results are summed in LDS in a fixed order, and the workgroup
-// writes the requested outputs directly: fp32 unscaled, bf16 scaled
-// (row-major, zero-padded to ldb columns), bf16 scaled and transposed
-// (zero-padded to ldt_rows rows and Mp columns).  No split partials in global
-// memory, no second pass.  One launch can carry two independent products
-// (blockIdx.y selects the argument set), which the backward uses for H and dH.
+// Work layout.  A workgroup of 4 waves owns 128 rows of L (32 per wave) and one
+// range of the contraction; the ranges (lowrank_splits of them) give the GPU
+// enough workgroups when M is small.  Per 64-deep step each wave loads its own
+// 32 x 64 slab of L straight into registers (a lane: one row, 32 consecutive
+// elements), LR_DEPTH steps ahead, while the R x 64 slab of the factor is
+// loaded once for the workgroup, LR_DEPTH steps ahead as well, and staged in
+// LDS (row pitch 144 bytes: sixteen consecutive rows read at one 16-byte
+// column fall on 16 distinct 4-bank groups).  v_mfma_f32_32x32x16_bf16 takes
+// both operands with the same permutation of the step's 64 contraction
+// indices (lane half h, sub-step i: indices 32h + 8i .. 32h + 8i + 7), which
+// leaves the sum unchanged.  The fp32 partial product of each range goes to a
+// workspace; a second kernel adds the ranges in order and writes the requested
+// outputs: fp32 unscaled, bf16 scaled (row-major, zero-padded to ldb
+// columns), bf16 scaled and transposed (zero-padded to ldt_rows rows and Mp
+// columns).  One launch carries up to QN_MAX_GROUP independent products
+// (blockIdx.y selects one).
 
 #include <algorithm>
 
@@ -26,12 +32,6 @@
 namespace qn {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int ROWS = 16;
-constexpr int CHUNK = 32;
-constexpr int UNROLL = 16;
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
@@ -41,112 +41,207 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 
+constexpr int LR_THREADS = 256;   // 4 waves
+constexpr int LR_BM = 128;        // rows of L per workgroup
+constexpr int LR_CK = 64;         // contraction depth of one step
+constexpr int LR_DEPTH = 4;       // steps of loads in flight
+constexpr int LR_PITCH = 144;     // LDS bytes per factor row
+constexpr int LR_TARGET_WGS = 256;
+constexpr int LR_MAX_SPLITS = 16;
+constexpr int LR_MIN_RANGE = 256; // contraction depth of the shortest range
+constexpr int FIN_ROWS = 16;      // rows per workgroup of the finishing kernel
+
 __host__ __device__ inline int64_t lowrank_rows(const LowRankArgs &a) {
   return a.out_t && a.Mp > a.M ? a.Mp : a.M;
 }
+__host__ __device__ inline int64_t align32(int64_t v) { return (v + 31) / 32 * 32; }
 
 struct LowRankGroup {
   LowRankArgs p[QN_MAX_GROUP];
 };
 
-template <int RT>  // 16-column tiles of the output: R <= 16 * RT
-__global__ __launch_bounds__(kThreads) void lowrank_kernel(LowRankGroup grp) {
-  __shared__ float red[kWaves][ROWS][RT * 16];
+template <int RT>   // 32-column tiles of the factor: R <= 32 * RT
+__global__ __launch_bounds__(LR_THREADS) void lowrank_part_kernel(LowRankGroup grp) {
+  __shared__ __attribute__((aligned(16))) uint8_t ps[2][32 * RT * LR_PITCH];
   const LowRankArgs a = grp.p[__builtin_amdgcn_readfirstlane((int)blockIdx.y)];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * ROWS;
-  if (m0 >= lowrank_rows(a)) return;   // the other product has more rows
+  const int S = a.splits;
+  const int64_t rb = blockIdx.x / S;
+  const int s = (int)(blockIdx.x % S);
+  const int64_t m0 = rb * LR_BM;
+  if (m0 >= a.M) return;   // another product of the launch has more rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lh = lane >> 5;
 
+  const int64_t steps = a.Kc / LR_CK;
+  const int64_t per = (steps + S - 1) / S;
+  const int64_t c0 = std::min<int64_t>(steps, (int64_t)s * per), c1 = std::min<int64_t>(steps, c0 + per);
+
+  // L: this lane's row, elements [32 lh, 32 lh + 32) of each step (rows past M
+  // read zeros).  Offsets stay below 2^32: 128 rows of at most 2^31 / 64 bytes.
   const rsrc_t rl = make_rsrc(a.L + m0 * a.ldl, (a.M - m0) * a.ldl * 2);
+  const uint32_t lvoff = (uint32_t)((32 * wave + lr) * a.ldl * 2 + 64 * lh);
+  // P: thread t moves 16-byte unit (t & 7) of rows t / 8 + 32 i, i < RT (rows
+  // past R read zeros).
   const rsrc_t rp = make_rsrc(a.P, a.R * a.ldp * 2);
-  const uint32_t lvoff = (uint32_t)(lr * a.ldl * 2 + lg * 16);
-  uint32_t pvoff[RT];
+  uint32_t pvoff[RT], pls[RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int j = t * 16 + lr;
-    pvoff[t] = j < a.R ? (uint32_t)(j * a.ldp * 2 + lg * 16) : kOutOfRange;
+  for (int i = 0; i < RT; ++i) {
+    const int j = tid / 8 + 32 * i, u = tid & 7;
+    pvoff[i] = j < a.R ? (uint32_t)(j * a.ldp * 2 + 16 * u) : kOutOfRange;
+    pls[i] = (uint32_t)(j * LR_PITCH + 16 * u);
   }
 
-  f32x4_t acc[RT];
+  u32x4 xr[LR_DEPTH][4];
+  u32x4 pr[LR_DEPTH][RT];
+  // Loads of step c (steps at or past c1 read zeros and move no data).
+  auto load_step = [&](int slot, int64_t c) {
+    const bool in = c < c1;
+    const int soff = in ? (int)(c * LR_CK * 2) : 0;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < 4; ++i)
+      xr[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rl, in ? lvoff + 16 * i : kOutOfRange, soff, 0);
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+      pr[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rp, in ? pvoff[i] : kOutOfRange, soff, 0);
+  };
+  auto stage = [&](int slot, int buf) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i) *reinterpret_cast<u32x4 *>(&ps[buf][pls[i]]) = pr[slot][i];
+  };
 
-  const int64_t chunks = a.Kc / CHUNK;
-  constexpr int U = UNROLL / RT;   // chunks of loads in flight per wave (registers: 4 * U * (1 + RT))
-  for (int64_t q0 = wave; q0 < chunks; q0 += (int64_t)kWaves * U) {
-    u32x4 xv[U], pv[U][RT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t q = q0 + (int64_t)u * kWaves;
-      const bool in = q < chunks;
-      const int soff = (int)(q * CHUNK * 2);
-      xv[u] = in ? __builtin_amdgcn_raw_buffer_load_b128(rl, lvoff, soff, 0) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-        pv[u][t] = in ? __builtin_amdgcn_raw_buffer_load_b128(rp, pvoff[t], soff, 0) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[u]),
-                                                        __builtin_bit_cast(bf16x8, pv[u][t]), acc[t], 0, 0, 0);
-  }
-
-  // acc[t][e] is row 4*lg + e, column 16*t + lr.
+  f32x16 acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave][4 * lg + e][16 * t + lr] = acc[t][e];
-  __syncthreads();
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
 
-  for (int idx = threadIdx.x; idx < ROWS * RT * 16; idx += kThreads) {
-    const int row = idx / (RT * 16), j = idx % (RT * 16);
+  // The step loop runs a whole number of LR_DEPTH-step groups with no branch
+  // inside a group (the padding steps multiply zeros), so that the loads of
+  // the next LR_DEPTH - 1 steps stay in flight across the loop's back edge.
+  // Step cb + d reads register slot d and LDS buffer d & 1 (LR_DEPTH is even).
+  static_assert(LR_DEPTH % 2 == 0, "LDS buffer parity follows the slot");
+  const int64_t n = c1 - c0;
+  if (n > 0) {
+    const int64_t np = (n + LR_DEPTH - 1) / LR_DEPTH * LR_DEPTH;
+#pragma unroll
+    for (int d = 0; d < LR_DEPTH; ++d) load_step(d, c0 + d);
+    stage(0, 0);
+    __syncthreads();
+    for (int64_t cb = 0; cb < np; cb += LR_DEPTH) {
+#pragma unroll
+      for (int d = 0; d < LR_DEPTH; ++d) {
+        const uint8_t *pb = ps[d & 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 xa = __builtin_bit_cast(bf16x8, xr[d][i]);
+#pragma unroll
+          for (int t = 0; t < RT; ++t) {
+            const u32x4 pf = *reinterpret_cast<const u32x4 *>(pb + (32 * t + lr) * LR_PITCH + 16 * (4 * lh + i));
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, __builtin_bit_cast(bf16x8, pf), acc[t], 0, 0, 0);
+          }
+        }
+        load_step(d, c0 + cb + d + LR_DEPTH);
+        stage((d + 1) % LR_DEPTH, (d + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // acc[t][e] is row 32 wave + 8 (e / 4) + 4 lh + e % 4, column 32 t + lr.
+  const int64_t Rp = align32(a.R);
+  float *part = a.part + (int64_t)s * a.M * Rp;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int j = 32 * t + lr;
+    if (j >= Rp) break;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t m = m0 + 32 * wave + 8 * (e >> 2) + 4 * lh + (e & 3);
+      if (m < a.M) part[m * Rp + j] = acc[t][e];
+    }
+  }
+}
+
+// Adds the ranges' partial products in range order and writes the outputs.  A
+// workgroup owns FIN_ROWS rows x 64 columns (a thread: one column of four
+// rows, every range's partial loaded before the in-order sum), staged in LDS
+// so that both the row-major and the transposed outputs are written along
+// their rows.
+__global__ __launch_bounds__(256) void lowrank_finish_kernel(LowRankGroup grp) {
+  __shared__ float tile[FIN_ROWS][65];
+  const LowRankArgs a = grp.p[__builtin_amdgcn_readfirstlane((int)blockIdx.y)];
+  const int64_t m0 = (int64_t)blockIdx.x * FIN_ROWS;
+  if (m0 >= lowrank_rows(a)) return;
+  const int tid = threadIdx.x, j = tid & 63, rq = tid >> 6;
+  const int64_t Rp = align32(a.R), plane = a.M * Rp;
+  const int S = a.splits;
+#pragma unroll
+  for (int q = 0; q < FIN_ROWS / 4; ++q) {
+    const int r = rq + 4 * q;
+    const int64_t m = m0 + r;
+    const bool in = m < a.M && j < a.R;
+    const float *p = a.part + (in ? m * Rp + j : 0);
+    float pv[LR_MAX_SPLITS];
+#pragma unroll
+    for (int s = 0; s < LR_MAX_SPLITS; ++s) pv[s] = (in && s < S) ? p[s * plane] : 0.0f;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += red[w][row][j];
-    const int64_t m = m0 + row;
-    const uint16_t b = (j < a.R) ? f32_to_bf16(v * a.scale) : (uint16_t)0;
-    if (m < a.M) {
-      if (a.out_f32 && j < a.R) a.out_f32[m * a.R + j] = v;
-      if (a.out_b && j < a.ldb) a.out_b[m * a.ldb + j] = b;
-    }
-    if (a.out_t && j < a.ldt_rows && m < a.Mp) a.out_t[(int64_t)j * a.Mp + m] = b;
+    for (int s = 0; s < LR_MAX_SPLITS; ++s)
+      if (s < S) v += pv[s];
+    tile[r][j] = v;
   }
-  // Columns of out_b between RT*16 and ldb (only when ldb > RT*16) are zero.
-  if (a.out_b && a.ldb > RT * 16) {
-    for (int idx = threadIdx.x; idx < ROWS * (a.ldb - RT * 16); idx += kThreads) {
-      const int row = idx / (int)(a.ldb - RT * 16), j = RT * 16 + idx % (int)(a.ldb - RT * 16);
-      const int64_t m = m0 + row;
-      if (m < a.M) a.out_b[m * a.ldb + j] = 0;
-    }
+  __syncthreads();
+  for (int idx = tid; idx < FIN_ROWS * 64; idx += 256) {
+    const int r = idx >> 6, jj = idx & 63;
+    const int64_t m = m0 + r;
+    if (m >= a.M) continue;
+    const float v = tile[r][jj];
+    if (a.out_f32 && jj < a.R) a.out_f32[m * a.R + jj] = v;
+    if (a.out_b && jj < a.ldb) a.out_b[m * a.ldb + jj] = jj < a.R ? f32_to_bf16(v * a.scale) : (uint16_t)0;
   }
-  if (a.out_t && a.ldt_rows > RT * 16) {
-    for (int idx = threadIdx.x; idx < ROWS * (a.ldt_rows - RT * 16); idx += kThreads) {
-      const int row = idx % ROWS, j = RT * 16 + idx / ROWS;
-      const int64_t m = m0 + row;
-      if (m < a.Mp) a.out_t[(int64_t)j * a.Mp + m] = 0;
+  if (a.out_t) {
+    for (int idx = tid; idx < FIN_ROWS * 64; idx += 256) {
+      const int jj = idx / FIN_ROWS, r = idx % FIN_ROWS;
+      const int64_t m = m0 + r;
+      if (jj < a.ldt_rows && m < a.Mp)
+        a.out_t[(int64_t)jj * a.Mp + m] = (jj < a.R && m < a.M) ? f32_to_bf16(tile[r][jj] * a.scale) : (uint16_t)0;
     }
   }
 }
 
 }  // namespace
 
+int lowrank_splits(int64_t M, int64_t Kc) {
+  const int64_t rb = (M + LR_BM - 1) / LR_BM;
+  const int64_t want = (LR_TARGET_WGS + rb - 1) / rb;
+  const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(LR_MAX_SPLITS, Kc / LR_MIN_RANGE));
+  return (int)std::max<int64_t>(1, std::min(want, cap));
+}
+
+size_t lowrank_part_bytes(int64_t M, int64_t Kc, int64_t R) {
+  return (size_t)lowrank_splits(M, Kc) * (size_t)M * (size_t)align32(R) * sizeof(float);
+}
+
 hipError_t launch_lowrank_n(const LowRankArgs *a, int n, hipStream_t st) {
   if (n < 1 || n > QN_MAX_GROUP) return hipErrorInvalidValue;
   LowRankGroup grp{};
-  int64_t rows = 0, R = 0;
+  int64_t wgs = 0, fin = 0, R = 0;
   for (int i = 0; i < n; ++i) {
     grp.p[i] = a[i];
-    rows = std::max(rows, lowrank_rows(a[i]));
+    grp.p[i].splits = lowrank_splits(a[i].M, a[i].Kc);
+    wgs = std::max<int64_t>(wgs, (a[i].M + LR_BM - 1) / LR_BM * grp.p[i].splits);
+    fin = std::max<int64_t>(fin, (lowrank_rows(a[i]) + FIN_ROWS - 1) / FIN_ROWS);
     R = std::max(R, a[i].R);
   }
-  const dim3 grid((unsigned)((rows + ROWS - 1) / ROWS), (unsigned)n);
-  TraceScope tr(QN_TRACE_LOWRANK, st);
-  if (R <= 16) hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(kThreads), 0, st, grp);
-  else if (R <= 32) hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(kThreads), 0, st, grp);
-  else hipLaunchKernelGGL(lowrank_kernel<4>, grid, dim3(kThreads), 0, st, grp);
+  {
+    TraceScope tr(QN_TRACE_LOWRANK, st);
+    const dim3 grid((unsigned)wgs, (unsigned)n);
+    if (R <= 32) hipLaunchKernelGGL(lowrank_part_kernel<1>, grid, dim3(LR_THREADS), 0, st, grp);
+    else hipLaunchKernelGGL(lowrank_part_kernel<2>, grid, dim3(LR_THREADS), 0, st, grp);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lowrank_finish_kernel, dim3((unsigned)fin, (unsigned)n), dim3(256), 0, st, grp);
   return hipGetLastError();
 }
 

@@ -132,9 +132,12 @@ struct QGemmGroup {
 };
 
 // Low-rank product (k_lowrank.hip): C[M, R] = L[M, Kc] * P[R, Kc]^T, R <= 64,
-// Kc % 32 == 0.  Writes any of: out_f32 [M, R] (unscaled), out_b [M, ldb] =
+// Kc % 64 == 0.  Writes any of: out_f32 [M, R] (unscaled), out_b [M, ldb] =
 // bf16(scale * C) zero beyond R, out_t [ldt_rows, Mp] = bf16(scale * C)^T zero
-// beyond R and beyond M (Mp >= M).
+// beyond R and beyond M (Mp >= M).  The contraction is cut into
+// lowrank_splits(M, Kc) ranges whose fp32 partial products go to `part`
+// (lowrank_part_bytes(M, Kc, R) bytes of workspace) and are then added in
+// range order, so the result depends on the shape alone.
 struct LowRankArgs {
   const uint16_t *L;
   int64_t ldl, M, Kc;
@@ -146,7 +149,11 @@ struct LowRankArgs {
   int64_t ldb;
   uint16_t *out_t;
   int64_t ldt_rows, Mp;
+  float *part;
+  int splits;   // set by the launcher
 };
+int lowrank_splits(int64_t M, int64_t Kc);
+size_t lowrank_part_bytes(int64_t M, int64_t Kc, int64_t R);
 hipError_t launch_lowrank(const LowRankArgs &a, hipStream_t s);
 // Two independent products with the same rank bucket in one launch (b may be null).
 hipError_t launch_lowrank2(const LowRankArgs &a, const LowRankArgs *b, hipStream_t s);

@@ -225,7 +225,8 @@ size_t qlora_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t r);
  * Requires M >= 1, N % 64 == 0, K % 64 == 0 (whole blocks per row; whole
  * contraction steps of 64 over K in the forward and over N in dX),
  * N*K/2 <= INT32_MAX (the kernels address the codes with 32-bit byte offsets),
- * 1 <= r <= QN_MAX_RANK, finite alpha; workspace 256-byte aligned, H_out 4-byte
+ * K <= 2^23 and N <= 2^23 (a 128-row slab of X or dY is addressed with 32-bit
+ * byte offsets), 1 <= r <= QN_MAX_RANK, finite alpha; workspace 256-byte aligned, H_out 4-byte
  * aligned.  Any other shape returns QN_ERR_SHAPE before anything is launched.
  * M <= 8 runs the streaming decode path (weights read once at HBM rate); larger
  * M runs the MFMA path (tiles dequantised into LDS, bf16 MFMA). */

@@ -145,6 +145,23 @@ def test_linear_rejects_codes_beyond_32bit_offsets():
                               vp(FAKE), 16, vp(0)) == 5
 
 
+def test_linear_rejects_rows_beyond_32bit_slab_offsets():
+    """K and N are each at most 2^23 (the low-rank kernels address 128 rows of X
+    or dY with 32-bit byte offsets): 2^23 passes validation up to the workspace
+    check, 2^23 + 64 is rejected, for K and for N, forward and backward."""
+    L = lib.load()
+    vp = ctypes.c_void_p
+    big = 1 << 40
+    lim = 1 << 23
+    for N, K, want in ((64, lim + 64, 2), (lim + 64, 64, 2), (64, lim, 5), (lim, 64, 5)):
+        w = _w(N=N, K=K)
+        ws = big if want == 2 else 16
+        assert L.qlora_linear_fwd(vp(FAKE), 16, ctypes.byref(w), vp(FAKE), vp(FAKE), 8, 16.0, vp(FAKE), vp(0),
+                                  vp(FAKE), ws, vp(0)) == want
+        assert L.qlora_linear_bwd(vp(FAKE), vp(FAKE), vp(0), 16, ctypes.byref(w), vp(FAKE), vp(FAKE), 8, 16.0,
+                                  vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), ws, vp(0)) == want
+
+
 def test_grouped_forward_rejects_bad_arguments():
     L = lib.load()
     arr = (lib.FwdProblemStruct * 2)()
