@@ -63,11 +63,18 @@ KERNEL_SOURCE = {
     "gemv": "k_linear.hip", "gemm_fwd": "k_qgemm.hip", "gemm_dx": "k_qgemm.hip",
     "lowrank": "k_lowrank.hip", "gemm_db": "k_lowrank.hip", "gemm_da": "k_lowrank.hip",
 }
-# Measured HBM bytes per launch: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per
-# dispatch), each scaled by the ratio of known bytes to counted bytes for a 256 MiB
-# copy in the same run.  Keyed by kernel and workload; `sha256` is that of the
-# kernel's source file and qn_device.h when the counters were taken.
-TRAFFIC = {}
+# Measured memory-side bytes per launch: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# (KiB per dispatch), each scaled by the ratio of known bytes to counted bytes for a
+# 256 MiB copy in the same run, averaged over the step's four launches of the
+# kernel.  The counters see the traffic between the L2 caches and the memory
+# fabric (reads served by the Infinity Cache included), an upper bound on HBM
+# bytes.  Keyed by kernel and workload; `sha256` is that of the kernel's source
+# file and qn_device.h when the counters were taken.
+TRAFFIC = {
+    "gemm_fwd_70b": {"bytes": 2518563017, "sha256": "21ce65109869bd9bcbd14a97a451fbb778b4a12ff13f89d1945f0d88e7626ae3"},
+    "lowrank_70b": {"bytes": 177228525, "sha256": "9fbca7dc2b982463e7e354c07a1d3f79208eec4bd5ac9bc320bfbba9ff1e7ec5"},
+    "gemv_70b": {"bytes": 114272550, "sha256": "5c0de8bafcde596c1510c948dd0b6f7a0dfc6e7ba34d07114dc3322194a9d552"},
+}
 
 # The configurations (N, K) of the linear layers.
 L70B = {"q": (8192, 8192), "k": (1024, 8192), "v": (1024, 8192), "o": (8192, 8192),
@@ -423,7 +430,8 @@ def main():
         lr_bytes = sum(2 * M70_PRE * it["K"] + 2 * R70 * it["K"] + 6 * M70_PRE * R70 for it in L.items)
         a = lr_bytes / (sum(lowr) * 1e-3) / 1e9
         lowrank_roof = {"kernel": "lowrank", "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBPS,
-                        "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4), "launches": len(lowr),
+                        "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
+                        "traffic": traffic("lowrank_70b", "lowrank"), "launches": len(lowr),
                         "launch_ms": [round(x, 5) for x in lowr],
                         "note": "H = X A^T of the prefill step, one launch per dependency group (its finishing "
                                 "launch excluded); bytes = X, A and H per linear"}

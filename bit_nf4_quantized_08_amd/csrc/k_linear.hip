@@ -146,11 +146,15 @@ __device__ __forceinline__ float wave_sum_multi(float (&v)[MM], int lane) {
   int off = 32;
 #pragma unroll
   for (int cnt = MM; cnt > 1; cnt >>= 1, off >>= 1) {
-    const bool upper = (lane & off) != 0;
+    // The choice between the two halves is made on the values' bits: a select
+    // between two array elements would be folded into a lane-dependent index
+    // and push the array out of registers.
+    const uint32_t up = (lane & off) != 0 ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int i = 0; i < cnt / 2; ++i) {
-      const float keep = upper ? v[i + cnt / 2] : v[i];
-      const float send = upper ? v[i] : v[i + cnt / 2];
+      const uint32_t lo = as_u32(v[i]), hi = as_u32(v[i + cnt / 2]);
+      const float keep = as_f32((hi & up) | (lo & ~up));
+      const float send = as_f32((lo & up) | (hi & ~up));
       v[i] = keep + __shfl_xor(send, off, 64);
     }
   }
