@@ -276,8 +276,9 @@ int qlora_linear_fwd_grouped(int n, const qlora_fwd_problem *problems, void *wor
  * is current must be the stream's).  Returns QN_ERR_SCRATCH, before anything is
  * launched, when qlora_workspace_size(QN_OP_FWD, M, N, K, r) exceeds it (16 MiB
  * covers decode, M <= 8, at every configured shape and the MFMA path up to
- * M * r = 8 Mi).  The first call on a device looks the array's address up
- * (hipGetSymbolAddress); no call allocates or frees memory.  Calls that overlap
+ * M = 43690 at r = 64 or M = 104856 at r = 16).  The first call on a device
+ * looks the array's address up (hipGetSymbolAddress); no call allocates or
+ * frees memory.  Calls that overlap
  * in time on one device (different streams, or host threads without ordering)
  * share the array and race: the caller serialises them. */
 #define QN_NOALLOC_SCRATCH_BYTES (16u << 20)
