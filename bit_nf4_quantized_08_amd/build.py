@@ -59,5 +59,53 @@ def build(verbose=False):
     return OUT
 
 
+# Host-side sanitizer build of the C-ABI layer (argument checking, the codebook,
+# the trace log, the device cache): those translation units are compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host side only (device
+# code is never instrumented), then linked with the ordinary kernel objects.
+# The library loads only into a process that preloads the clang ASan runtime
+# (sanitizer_runtime()); the CPU ABI tests run against it in a child process.
+HOST_SOURCES = ["api.cpp", "codebook.cpp", "trace.cpp", "device.cpp"]
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_OUT = os.path.join(BUILD, "asan", "libqlora_nf4_asan.so")
+
+
+def sanitizer_runtime():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    r = subprocess.run([os.path.join(rocm, "llvm", "bin", "clang"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    return path if r.returncode == 0 and os.path.isfile(path) else None
+
+
+def build_sanitized(verbose=False):
+    d = os.path.dirname(SAN_OUT)
+    os.makedirs(d, exist_ok=True)
+
+    def host_obj(src):
+        obj = os.path.join(d, src + ".o")
+        cmd = [hipcc(), *HIPCC_FLAGS, "-O1", "-g", *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        return obj
+
+    kernels = [s for s in SOURCES if s not in HOST_SOURCES]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        hobjs = list(ex.map(host_obj, HOST_SOURCES))
+        kobjs = [os.path.join(BUILD, s + ".o") for s in kernels]
+        missing = [s for s, o in zip(kernels, kobjs) if not os.path.isfile(o)]
+        list(ex.map(_compile, missing))
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *SAN_FLAGS, "-shared-libsan", *hobjs, *kobjs,
+           "-o", SAN_OUT]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + r.stderr)
+    if verbose:
+        print("built", SAN_OUT)
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -17,7 +17,9 @@ from typing import Optional
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqlora_nf4.so")
+# QN_LIBRARY names another build of the same library (the host-sanitizer build
+# that the ABI tests load in a child process); by default the in-tree one.
+LIB_PATH = os.environ.get("QN_LIBRARY") or os.path.join(_PKG, "libqlora_nf4.so")
 
 QN_OK = 0
 QN_F32, QN_BF16 = 0, 1
