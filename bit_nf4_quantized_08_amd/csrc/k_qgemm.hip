@@ -39,9 +39,11 @@
 //      loads 32 codes of one row (16 bytes, one block), the four lanes of a
 //      quad transpose their words with DPP so that each lane holds a 4 x 8
 //      patch (4 rows, 8 columns), and the patch is written transposed.
-// Both stage layouts are XOR-swizzled in 16-byte chunks so that the fragment
-// reads and the weight-stage writes are free of bank conflicts (see kswz and
-// the activation-stage comment below).
+// The activation stages are XOR-swizzled in 16-byte chunks and the forward
+// weight stage has a padded row pitch, so that fragment reads and stage writes
+// are free of bank conflicts; the dX weight stage keeps an XOR layout for its
+// transposed 8-byte writes (see wswz, kswz and the activation-stage comment
+// below).
 
 #include <algorithm>
 #include <atomic>
@@ -105,19 +107,21 @@ __device__ __forceinline__ void tile_coords(int h, int tiles_m, int tiles_n, int
 }
 
 // LDS weight stage: output column `col` (a row of the stage, LD bf16 long)
-// holds contraction positions 0..63.  Position k is stored at k ^ kswz(col):
-// the XOR moves whole 8-element chunks, so every 16-byte fragment stays
-// contiguous.  On gfx950 a 16-byte LDS read serves 16 lanes per cycle, taken
-// as 8-lane blocks 0+3, 1+2, 4+7 and 5+6 of the wave (measured over 256 bank
-// patterns: all agree with this pairing and with no other).  With the row
-// pitch of 36 banks, columns c .. c+7 and c+24 .. c+31 (c = 32j) fall into
-// complementary bank sets, as do c+8 .. c+15 and c+16 .. c+23, so the MMA
-// reads (lane lr reads column 32j + lr) are conflict-free as long as the
-// half-row XOR (32) is the same within each pair: it is keyed on bit 3 XOR
-// bit 4 of the column.  That XOR also separates columns c and c + 16, which
-// the transposed-weight producers write in the same cycle (8-byte writes),
-// and the 8j term staggers the producer waves.
+// holds contraction positions 0..63, 16-byte chunks of 8.  Bank behaviour of
+// gfx950 LDS, measured with a probe of 30 access patterns (timing and the
+// SQ_LDS_BANK_CONFLICT counter): a 16-byte read serves 16 consecutive lanes
+// per cycle over 64 banks of 4 bytes; a 16-byte write serves 8 consecutive
+// lanes per cycle over 32 banks.  With the row pitch of 36 banks, sixteen
+// consecutive columns read at one 16-byte position fall on 16 distinct 4-bank
+// groups, and eight consecutive columns written at one position on 8 distinct
+// groups of the 32: the forward (row-major weight) stages store position k at
+// k, with no XOR (wswz<false>).  The transposed producer of dX writes 8-byte
+// column patches; its stage keeps position k at k ^ kswz(col) (the XOR moves
+// whole 8-element chunks), which separates columns c and c + 16 written in the
+// same cycle; its MMA reads pay about 4 conflict cycles per instruction.
 __device__ __forceinline__ int kswz(int col) { return 32 * (((col >> 3) ^ (col >> 4)) & 1) + 8 * ((col >> 5) & 3); }
+template <bool KN>
+__device__ __forceinline__ int wswz(int col) { return KN ? kswz(col) : 0; }
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t qperm(uint32_t v) {
@@ -267,7 +271,7 @@ struct Producer {
         asm volatile("" : "+v"(o[4 * i]), "+v"(o[4 * i + 1]), "+v"(o[4 * i + 2]), "+v"(o[4 * i + 3]));
       }
       uint16_t *row = Rs + wr_col * LD;
-      const int sw = kswz(wr_col);
+      const int sw = wswz<KN>(wr_col);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4 *>(&row[(wr_k + 8 * i) ^ sw]) = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
@@ -334,6 +338,7 @@ __device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n
 }
 // The 2-byte values are packed only here, at the use, so that the wait for
 // the loads falls at the end of the main loop.
+template <bool KN>
 __device__ __forceinline__ void store_adapter_right(const uint32_t (&h)[32], uint16_t *Rs, int t) {
   const int row = t & (BN - 1), j0 = 32 * (t >> 7);
   uint32_t v[16];
@@ -341,7 +346,7 @@ __device__ __forceinline__ void store_adapter_right(const uint32_t (&h)[32], uin
   for (int i = 0; i < 16; ++i) v[i] = (h[2 * i] & 0xFFFFu) | (h[2 * i + 1] << 16);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<u32x4 *>(&Rs[row * LD + ((j0 + 8 * q) ^ kswz(row))]) = u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    *reinterpret_cast<u32x4 *>(&Rs[row * LD + ((j0 + 8 * q) ^ wswz<KN>(row))]) = u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
 }
 
 // Workgroup barrier that orders the waves' own LDS reads and writes only:
@@ -523,7 +528,7 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
     }
     // Half-step nsteps: the adapter's right operand; its left operand is
     // activation stage nsteps, issued in the last weight half-step.
-    store_adapter_right(adapter, (t & 1) ? ws1 : ws0, tid);
+    store_adapter_right<KN>(adapter, (t & 1) ? ws1 : ws0, tid);
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     lds_barrier();
     lds_barrier();   // the MMA waves' barrier after the adapter step: nothing is in flight
@@ -544,19 +549,19 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
   // Activation stages are filled by the producer waves (see there); this
   // wave only reads them, after the barrier that follows their loads.
   // Fragment offsets: A (activations) tile i, slice c: row 32i + lr, chunk 4lh + c;
-  // B (weights) column 32j + lr, positions 32lh + 8c .. +7, stored at 32(lh ^ g) + 8(c ^ j),
-  // g = bit 3 ^ bit 4 of lr.
+  // B (weights) column 32j + lr, positions 32lh + 8c .. +7, stored there (forward) or at
+  // 32(lh ^ g) + 8(c ^ j), g = bit 3 ^ bit 4 of lr (dX: the kswz layout).
   uint32_t aoff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) aoff[c] = (uint32_t)(wave_u * XW + lr * BK + (((4 * lh + c) ^ ((lr >> 1) & 7)) * 8));
-  const int rb = lr * LD + 32 * (lh ^ (((lr >> 3) ^ (lr >> 4)) & 1));
+  const int rb = lr * LD + 32 * (lh ^ (KN ? (((lr >> 3) ^ (lr >> 4)) & 1) : 0));
   struct Frag {
     bf16x8 a[TM];
     bf16x8 b[TN];
   };
   auto read_b = [&](bf16x8 *b, const uint16_t *wc, int c) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * (c ^ j)]);
+    for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * (KN ? (c ^ j) : c)]);
   };
   auto read_f = [&](Frag &f, const uint16_t *xc, const uint16_t *wc, int c) {
 #pragma unroll
@@ -763,7 +768,7 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   uint32_t aoff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) aoff[c] = (uint32_t)(rg * XW + lr * BK + (((4 * lh + c) ^ ((lr >> 1) & 7)) * 8));
-  const int rb = (128 * cg + lr) * LD + 32 * (lh ^ (((lr >> 3) ^ (lr >> 4)) & 1));
+  const int rb = (128 * cg + lr) * LD + 32 * lh;
   struct Frag {
     bf16x8 a[TM];
     bf16x8 b[TN];
@@ -772,7 +777,7 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(&xc[aoff[c] + i * 32 * BK]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * (c ^ j)]);
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * c]);
   };
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -811,7 +816,7 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   const uint16_t *wrow = nullptr;
   (void)wrow;
   const int wcol = P.wr_col, wk = P.wr_k;
-  const int wsw = kswz(wcol);
+  const int wsw = wswz<false>(wcol);
   auto step = [&](int s, const uint16_t *xc, const uint16_t *wc, uint16_t *xn, uint16_t *wn,
                   typename Producer<false, DQ>::Set &set) {
     issue_x(xn, s + 1);
@@ -926,7 +931,7 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
     for (int i = 0; i < 16; ++i) v[i] = (h[2 * i] & 0xFFFFu) | (h[2 * i + 1] << 16);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4 *>(&wa[col * LD + ((j0 + 8 * q) ^ kswz(col))]) = u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+      *reinterpret_cast<u32x4 *>(&wa[col * LD + ((j0 + 8 * q) ^ wswz<false>(col))]) = u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   lds_barrier();
@@ -1086,7 +1091,7 @@ void qgemm3_kernel(QGemmGroup grp, Code16 cb) {
   RowProducer<DQ> P;
   P.init(a, tid, n0);
   typename RowProducer<DQ>::Set s0, s1;
-  const int wsw = kswz(tid);
+  const int wsw = wswz<false>(tid);
 
   // ---- fragments: A row tile i of the wave is rows 128 rh + 32 i + lr (row
   // block 2 rh + i / 2); B column tile j is column 128 ch + 32 j + lr.
@@ -1094,7 +1099,7 @@ void qgemm3_kernel(QGemmGroup grp, Code16 cb) {
   uint32_t aoff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) aoff[c] = (uint32_t)(2 * rh * XW + lr * BK + (((4 * lh + c) ^ ((lr >> 1) & 7)) * 8));
-  const int rb = (128 * ch + lr) * LD + 32 * (lh ^ (((lr >> 3) ^ (lr >> 4)) & 1));
+  const int rb = (128 * ch + lr) * LD + 32 * lh;
   struct Frag {
     bf16x8 a[TM3];
     bf16x8 b[TN3];
@@ -1103,7 +1108,7 @@ void qgemm3_kernel(QGemmGroup grp, Code16 cb) {
 #pragma unroll
     for (int i = 0; i < TM3; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(&xc[aoff[c] + i * 32 * BK]);
 #pragma unroll
-    for (int j = 0; j < TN3; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * (c ^ j)]);
+    for (int j = 0; j < TN3; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * c]);
   };
   f32x16 acc[TM3][TN3];
 #pragma unroll
