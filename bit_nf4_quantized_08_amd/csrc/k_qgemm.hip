@@ -1293,22 +1293,27 @@ void qgemm3_kernel(QGemmGroup grp, Code16 cb) {
 
 int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-// Tiles, and the row-tile group size of the XCD-aware order: each XCD runs T/8
-// tiles; the group is chosen so that an XCD's share covers about as many
-// activation bytes (rows x Kc x 2) as weight bytes (columns x Kc / 2).
+// Tiles, and the row-tile group size of the XCD-aware order.  Each XCD runs a
+// contiguous run of T/8 logical tiles, and about CUs/8 of them at once (one
+// workgroup per CU); the tiles running together walk the contraction at about
+// the same pace, so the XCD's L2 serves each activation row-panel and weight
+// column-panel they share.  The group size g (row tiles per group) is chosen
+// for that concurrent set: g row panels (bm x 2 bytes per contraction index)
+// plus R/g column panels (bn / 2 bytes) for R = CUs/8 tiles, as few bytes as
+// possible.
 bool plan(QGemmArgs &a, int bm = BM, int bn = BN) {
   // The adapter term is exactly one extra contraction step, and the producer
   // and MMA waves count their barriers on that: reject any other rank here.
   if (a.r < 1 || a.r > BK || a.Kc < BK || a.Kc % BK != 0) return false;
   a.tiles_m = (int)cdiv(a.M, bm);
   a.tiles_n = (int)cdiv(a.Nout, bn);
-  const int T8 = std::max(1, a.tiles_m * a.tiles_n / 8);
+  const int R = std::max(1, std::min(a.tiles_m * a.tiles_n / 8, device_cus() / 8));
   int best = 1;
   double best_cost = 1e300;
   for (int g = 1; g <= a.tiles_m; ++g) {
-    const int cols = std::max(1, std::min(a.tiles_n, T8 / g));
-    const double cost = (double)g * bm * 2 + (double)cols * bn / 2;
-    if (cost < best_cost) { best_cost = cost; best = g; }
+    const int cols = std::max(1, std::min(a.tiles_n, (R + g - 1) / g));
+    const double cost = (double)std::min(g, R) * bm * 2 + (double)cols * bn / 2;
+    if (cost < best_cost * (1.0 - 1e-9)) { best_cost = cost; best = g; }
   }
   a.group_m = best;
   return true;

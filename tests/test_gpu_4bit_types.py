@@ -19,8 +19,10 @@ from tests.gpu_util import REL_FRO_TOL, dev, guarded, guards_intact, host, rel_f
 
 pytestmark = pytest.mark.gpu
 
+# The last size has more groups of 16384 than the fused kernel has resident
+# workgroups (several groups per workgroup), and a partial last group.
 SIZES = [(1, 1), (3, 21), (1, 65), (5, 100), (17, 1000), (64, 4096 + 16), (3, 16384 * 2 + 1000), (256, 2048),
-         (7, 16384 + 64 * 5 + 3)]
+         (7, 16384 + 64 * 5 + 3), (2053, 16484)]
 
 
 def _run(W, qt, bf16, dq):
