@@ -411,8 +411,10 @@ def main():
                 "work_per_launch": gemm_flops // len(gemm),
                 "launch_flops": [sum(2 * M70_PRE * L70B[n][0] * L70B[n][1] + 2 * M70_PRE * R70 * L70B[n][0] for n in part)
                                  for part in dep],
-                "note": "grouped launches q,k,v | o | gate,up | down at M = 4096; work = 2MNK + 2MrN over "
-                        "the linears of each launch (the X A^T product runs in the low-rank kernel)"}
+                "note": "grouped calls q,k,v | o | gate,up | down at M = 4096, one entry per call (the q,k,v "
+                        "call runs q on 256x256 tiles and k, v on 256x128 tiles, two launches traced together); "
+                        "work = 2MNK + 2MrN over the linears of each call (the X A^T product runs in the low-rank "
+                        "kernel)"}
     gemv = kern.get("gemv", [])
     gemv_bytes = sum(nf4_bytes(it["N"], it["K"]) + 2 * it["K"] + 2 * it["N"] + 2 * R70 * it["K"] for it in L.items)
     gemv_roof = None
@@ -545,8 +547,10 @@ def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weig
               "note": "14 calls (A and B of the 7 linears, r = 64); bytes = bf16 parameter read and written, bf16 "
                       "gradient, both 8-bit codes read and written, block steps"}
     del ad_t
+    ctx = context_ceilings(torch, dev, log)
     f, w = flops_pre, weight_bytes
-    return {"prefill_M4096_single_calls_TFLOPs": round(f / pre_single_us / 1e6, 1),
+    return {"context_ceilings": ctx,
+            "prefill_M4096_single_calls_TFLOPs": round(f / pre_single_us / 1e6, 1),
             "prefill_M4096_one_call_all7_TFLOPs": round(f / pre_all7_us / 1e6, 1),
             "prefill_M4096_TFLOPs_by_tiling": {
                 "256x128": round(f / tilings[1] / 1e6, 1), "256x256_8waves": round(f / tilings[2] / 1e6, 1),
@@ -556,6 +560,50 @@ def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weig
             "per_linear": per_linear,
             "merge_export_bf16": merge,
             "adamw8_adapter_step": adamw8}
+
+
+def context_ceilings(torch, dev, log):
+    """What the GPU does without the method: a plain device copy, and the
+    library bf16 GEMM (torch.matmul, hipBLASLt) on the 70B layer's shapes at
+    M = 4096 with ready bf16 weights (no 4-bit storage, no expansion).  Eager
+    calls timed with HIP events on the current stream."""
+    log("context ceilings: device copy, hipBLASLt bf16 GEMM")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    cu = timed(lambda: dst.copy_(src), 10)
+    copy = 2 * src.numel() / cu / 1e3
+    del src, dst
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    per, tot_us, tot_fl = {}, 0.0, 0
+    for name, (N, K) in L70B.items():
+        X = torch.randn((M70_PRE, K), generator=g, device=dev).to(torch.bfloat16)
+        Wt = (torch.randn((K, N), generator=g, device=dev) * 0.015).to(torch.bfloat16)   # [K, N], contiguous
+        Y = torch.empty((M70_PRE, N), dtype=torch.bfloat16, device=dev)
+        us = timed(lambda: torch.matmul(X, Wt, out=Y), 5)
+        fl = 2 * M70_PRE * N * K
+        per[name] = round(fl / us / 1e6, 1)
+        tot_us += us
+        tot_fl += fl
+        del X, Wt, Y
+    torch.cuda.empty_cache()
+    return {"device_copy_GBps": round(copy, 1), "hipblaslt_bf16_layer_M4096_TFLOPs": round(tot_fl / tot_us / 1e6, 1),
+            "hipblaslt_bf16_per_linear_TFLOPs": per,
+            "note": "512 MiB device-to-device copy (read + write counted); torch.matmul on bf16 weights of the same "
+                    "shapes (2MNK, no adapter, no 4-bit storage): the dense GEMM the method's expansion competes with"}
 
 
 def other_stages(torch, lib, dev, cap, log):

@@ -1326,28 +1326,9 @@ bool plan(QGemmArgs &a, int bm = BM, int bn = BN) {
 // round-robin by their global index).
 std::atomic<int> g_variant{0};   // 0 automatic, 1 256 x 128, 2 256 x 256 (8 waves), 3 256 x 256 (4 waves)
 
+// One launch of one tiling over n problems (wide: 256 x 256, forward only).
 template <bool KN, bool EPI_NK>
-hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
-  if (n < 1 || n > QN_MAX_GROUP) return hipErrorInvalidValue;
-  // Tiling: the 256 x 256 one (forward only) when it gives the GPU at least
-  // two rounds of tiles, else the 256 x 128 one.
-  bool wide = false;
-  const int v = g_variant.load(std::memory_order_relaxed);
-  if (!KN) {
-    // Automatic choice: each tiling's time is its rounds of tiles over the
-    // compute units (one workgroup per CU) times the time of one tile; a
-    // 256 x 256 tile measures about 1.74 times a 256 x 128 one on the
-    // configured shapes (the same work per tile costs about 13 % less).
-    int64_t t1 = 0, t2 = 0;
-    for (int i = 0; i < n; ++i) {
-      t1 += cdiv(in[i].M, BM) * cdiv(in[i].Nout, BN);
-      t2 += cdiv(in[i].M, BM2) * cdiv(in[i].Nout, BN2);
-    }
-    const int64_t cus = device_cus();
-    const double c1 = (double)cdiv(t1, cus), c2 = 1.74 * (double)cdiv(t2, cus);
-    wide = v >= 2 || (v == 0 && c2 < c1);
-  }
-  const int wide_kind = v == 3 ? 3 : 2;
+hipError_t launch_tiling(const QGemmArgs *in, int n, bool wide, int wide_kind, hipStream_t st) {
   const int bm = wide ? BM2 : BM, bn = wide ? BN2 : BN;
   QGemmGroup grp{};
   int order[QN_MAX_GROUP];
@@ -1366,7 +1347,6 @@ hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
   for (int k = n; k <= QN_MAX_GROUP; ++k) grp.start[k] = (int)total;
   grp.n = n;
   const dim3 grid((unsigned)total);
-  TraceScope tr(trace_kind, st);
   if constexpr (!KN) {
     if (wide && wide_kind == 3) {
       if (dq) hipLaunchKernelGGL((qgemm3_kernel<true>), grid, dim3(kThreads3), 0, st, grp, code16(in[0].qtype));
@@ -1384,6 +1364,51 @@ hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
   else
     hipLaunchKernelGGL((qgemm_kernel<KN, false, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16(in[0].qtype));
   return hipGetLastError();
+}
+
+// One call over n problems.  Forward tiling, automatic: each tiling's time is
+// its rounds of tiles over the compute units (one workgroup per CU) times the
+// time of one tile; a 256 x 256 tile measures about 1.74 times a 256 x 128 one
+// on the configured shapes (the same work per tile costs about 13 % less).
+// The problems may also be split into a wide launch and a narrow one (say a
+// layer's q projection on 256 x 256 tiles and its short k and v on 256 x 128)
+// when the two launches' rounds cost less than either tiling alone, counting
+// a tenth of a round for the second launch.  The kernel trace brackets the
+// call's launches together.
+template <bool KN, bool EPI_NK>
+hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
+  if (n < 1 || n > QN_MAX_GROUP) return hipErrorInvalidValue;
+  TraceScope tr(trace_kind, st);
+  const int v = g_variant.load(std::memory_order_relaxed);
+  const int wide_kind = v == 3 ? 3 : 2;
+  if (KN) return launch_tiling<KN, EPI_NK>(in, n, false, wide_kind, st);
+  if (v != 0) return launch_tiling<KN, EPI_NK>(in, n, v >= 2, wide_kind, st);
+  const int64_t cus = device_cus();
+  int64_t tw[QN_MAX_GROUP], tn[QN_MAX_GROUP];
+  for (int i = 0; i < n; ++i) {
+    tw[i] = cdiv(in[i].M, BM2) * cdiv(in[i].Nout, BN2);
+    tn[i] = cdiv(in[i].M, BM) * cdiv(in[i].Nout, BN);
+  }
+  // subset = problems on the wide tiling
+  unsigned best = 0;
+  double best_cost = 1e300;
+  for (unsigned sub = 0; sub < (1u << n); ++sub) {
+    int64_t w = 0, nn = 0;
+    for (int i = 0; i < n; ++i) (sub >> i & 1u ? w : nn) += sub >> i & 1u ? tw[i] : tn[i];
+    const double cost = 1.74 * (double)cdiv(w, cus) + (double)cdiv(nn, cus) + (w && nn ? 0.1 : 0.0);
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = sub; }
+  }
+  if (best == 0 || best == (1u << n) - 1)
+    return launch_tiling<KN, EPI_NK>(in, n, best != 0, wide_kind, st);
+  QGemmArgs wa[QN_MAX_GROUP], na[QN_MAX_GROUP];
+  int nw = 0, nnw = 0;
+  for (int i = 0; i < n; ++i) {
+    if (best >> i & 1u) wa[nw++] = in[i];
+    else na[nnw++] = in[i];
+  }
+  const hipError_t e = launch_tiling<KN, EPI_NK>(wa, nw, true, wide_kind, st);
+  if (e != hipSuccess) return e;
+  return launch_tiling<KN, EPI_NK>(na, nnw, false, wide_kind, st);
 }
 
 }  // namespace
