@@ -65,15 +65,15 @@ KERNEL_SOURCE = {
 }
 # Measured memory-side bytes per launch: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
 # (KiB per dispatch), each scaled by the ratio of known bytes to counted bytes for a
-# 256 MiB copy in the same run, averaged over the step's four launches of the
-# kernel.  The counters see the traffic between the L2 caches and the memory
+# 256 MiB copy in the same run, averaged over the step's four calls of the
+# kernel (a call's launches counted together).  The counters see the traffic between the L2 caches and the memory
 # fabric (reads served by the Infinity Cache included), an upper bound on HBM
 # bytes.  Keyed by kernel and workload; `sha256` is that of the kernel's source
 # file and qn_device.h when the counters were taken.
 TRAFFIC = {
-    "gemm_fwd_70b": {"bytes": 2518563017, "sha256": "21ce65109869bd9bcbd14a97a451fbb778b4a12ff13f89d1945f0d88e7626ae3"},
-    "lowrank_70b": {"bytes": 177228525, "sha256": "9fbca7dc2b982463e7e354c07a1d3f79208eec4bd5ac9bc320bfbba9ff1e7ec5"},
-    "gemv_70b": {"bytes": 114272550, "sha256": "5c0de8bafcde596c1510c948dd0b6f7a0dfc6e7ba34d07114dc3322194a9d552"},
+    "gemm_fwd_70b": {"bytes": 1560065844, "sha256": "969c3652d168bad5259a8ea0cb57a0087f0b292906097d3cc2ea7eea2513e74a"},
+    "lowrank_70b": {"bytes": 177342016, "sha256": "9fbca7dc2b982463e7e354c07a1d3f79208eec4bd5ac9bc320bfbba9ff1e7ec5"},
+    "gemv_70b": {"bytes": 114272722, "sha256": "5c0de8bafcde596c1510c948dd0b6f7a0dfc6e7ba34d07114dc3322194a9d552"},
 }
 
 # The configurations (N, K) of the linear layers.
@@ -549,6 +549,7 @@ def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weig
     del ad_t
     ctx = context_ceilings(torch, dev, log)
     f, w = flops_pre, weight_bytes
+    ctx["nf4_prefill_over_dense_bf16"] = round(f / pre_us / 1e6 / ctx["hipblaslt_bf16_layer_M4096_TFLOPs"], 3)
     return {"context_ceilings": ctx,
             "prefill_M4096_single_calls_TFLOPs": round(f / pre_single_us / 1e6, 1),
             "prefill_M4096_one_call_all7_TFLOPs": round(f / pre_all7_us / 1e6, 1),
