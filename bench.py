@@ -520,6 +520,15 @@ def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weig
                                   "prefill_TFLOPs": round(fwd_flops(M70_PRE, it["N"], it["K"], R70) / us / 1e6, 1),
                                   "decode_us": round(dus, 2),
                                   "decode_weight_GBps": round(nf4_bytes(it["N"], it["K"]) / dus / 1e3, 1)}
+    # batched decode (M = 8 activation rows) on the gate projection
+    gate = next(it for it in L.items if it["name"] == "gate")
+    X8 = (torch.randn((8, gate["K"]), device=dev)).to(torch.bfloat16)
+    Y8 = torch.empty((8, gate["N"]), dtype=torch.bfloat16, device=dev)
+    ws8 = lib.workspace(lib.QN_OP_FWD, 8, gate["N"], gate["K"], R70, dev)
+    gate_m8_us = graph_time_us(torch, cap, lambda: [lib.qlora_linear_fwd(X8, gate["w"], gate["A"], gate["B"], L.alpha,
+                                                                         Y=Y8, ws=ws8) for _ in range(10)],
+                               replays=5, calls=10)
+    del X8, Y8, ws8
     # merge/export of the layer's adapters into bf16 weights (one call per linear)
     mo = {it["name"]: torch.empty((it["N"], it["K"]), dtype=torch.bfloat16, device=dev) for it in L.items}
     merge_us = graph_time_us(torch, cap, lambda: [lib.qlora_merge(it["w"], it["A"], it["B"], L.alpha, out=mo[it["name"]])
@@ -559,6 +568,7 @@ def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weig
             "decode_M1_single_calls_weight_GBps": round(w / dec_single_us / 1e3, 1),
             "decode_M1_one_call_all7_weight_GBps": round(w / dec_all7_us / 1e3, 1),
             "per_linear": per_linear,
+            "decode_M8_gate_us": round(gate_m8_us, 2),
             "merge_export_bf16": merge,
             "adamw8_adapter_step": adamw8}
 
@@ -650,6 +660,15 @@ def other_stages(torch, lib, dev, cap, log):
     us["fwd_decode_M1"] = graph_time_us(torch, cap, lambda: [lib.qlora_linear_fwd(Xd, pool[i], A, B, AL, Y=Yd,
                                                                                   ws=ws_d)
                                                              for i in range(64)], calls=64)
+    # batched decode: a few activation rows per call (the decode path runs up to M = 8)
+    for mb in (2, 4, 8):
+        Xm = randn((mb, K), 1.0)
+        Ym = torch.empty((mb, N), dtype=torch.bfloat16, device=dev)
+        wsm = lib.workspace(lib.QN_OP_FWD, mb, N, K, R, dev)
+        us[f"fwd_decode_M{mb}"] = graph_time_us(torch, cap, lambda: [lib.qlora_linear_fwd(Xm, pool[i], A, B, AL,
+                                                                                          Y=Ym, ws=wsm)
+                                                                     for i in range(64)], calls=64)
+        del Xm, Ym, wsm
     us["fwd_prefill_M2048"] = graph_time_us(torch, cap, lambda: [lib.qlora_linear_fwd(Xp, pool[i], A, B, AL, Y=Yp,
                                                                                       ws=ws_p, H=Hp)
                                                                  for i in range(8)], calls=8)
