@@ -10,9 +10,10 @@
 // Work layout.  A workgroup of 4 waves owns 128 rows of L (32 per wave) and one
 // range of the contraction; the ranges (lowrank_splits of them) give the GPU
 // enough workgroups when M is small.  Per 64-deep step each wave loads its own
-// 32 x 64 slab of L straight into registers (a lane: one row, 32 consecutive
-// elements), LR_DEPTH steps ahead, while the R x 64 slab of the factor is
-// loaded once for the workgroup, LR_DEPTH steps ahead as well, and staged in
+// 32 x 64 slab of L into registers with whole-line loads, LR_DEPTH steps ahead,
+// and passes it through its own LDS region into the MFMA layout, while the
+// R x 64 slab of the factor is loaded once for the workgroup, LR_DEPTH steps
+// ahead as well, and staged in
 // LDS (row pitch 144 bytes: sixteen consecutive rows read at one 16-byte
 // column fall on 16 distinct 4-bank groups).  v_mfma_f32_32x32x16_bf16 takes
 // both operands with the same permutation of the step's 64 contraction
@@ -63,6 +64,7 @@ struct LowRankGroup {
 template <int RT>   // 32-column tiles of the factor: R <= 32 * RT
 __global__ __launch_bounds__(LR_THREADS) void lowrank_part_kernel(LowRankGroup grp) {
   __shared__ __attribute__((aligned(16))) uint8_t ps[2][32 * RT * LR_PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[LR_THREADS / 64][32 * 128];   // each wave's L slab
   const LowRankArgs a = grp.p[__builtin_amdgcn_readfirstlane((int)blockIdx.y)];
   const int S = a.splits;
   const int64_t rb = blockIdx.x / S;
@@ -76,10 +78,24 @@ __global__ __launch_bounds__(LR_THREADS) void lowrank_part_kernel(LowRankGroup g
   const int64_t per = (steps + S - 1) / S;
   const int64_t c0 = std::min<int64_t>(steps, (int64_t)s * per), c1 = std::min<int64_t>(steps, c0 + per);
 
-  // L: this lane's row, elements [32 lh, 32 lh + 32) of each step (rows past M
-  // read zeros).  Offsets stay below 2^32: 128 rows of at most 2^31 / 64 bytes.
+  // L: load i of a step brings rows 8i .. 8i + 7 of the wave's 32, eight lanes
+  // per row reading its whole 128-byte line (rows past M read zeros); a wave
+  // whose lanes each read a 16-byte piece of a different row would touch 32
+  // lines per load and fetch each line four times.  The wave writes the slab
+  // to its own LDS region, chunk k of row rho at slot k ^ ((rho >> 1) & 7), and
+  // reads the MFMA fragments back: lane (lr, lh) reads row lr, chunk 4 lh + i in
+  // sub-step i (16 consecutive lanes hit 16 distinct 4-bank groups).  Offsets
+  // stay below 2^32: 128 rows of at most 2^24 elements.
   const rsrc_t rl = make_rsrc(a.L + m0 * a.ldl, (a.M - m0) * a.ldl * 2);
-  const uint32_t lvoff = (uint32_t)((32 * wave + lr) * a.ldl * 2 + 64 * lh);
+  uint32_t lvo[4], xw[4], xrd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rho = 8 * i + (lane >> 3), k = lane & 7;
+    lvo[i] = (uint32_t)((32 * wave + rho) * a.ldl * 2 + 16 * k);
+    xw[i] = (uint32_t)(rho * 128 + 16 * (k ^ ((rho >> 1) & 7)));
+    xrd[i] = (uint32_t)(lr * 128 + 16 * ((4 * lh + i) ^ ((lr >> 1) & 7)));
+  }
+  uint8_t *xslab = xs[wave];
   // P: thread t moves 16-byte unit (t & 7) of rows t / 8 + 32 i, i < RT (rows
   // past R read zeros).
   const rsrc_t rp = make_rsrc(a.P, a.R * a.ldp * 2);
@@ -99,7 +115,7 @@ __global__ __launch_bounds__(LR_THREADS) void lowrank_part_kernel(LowRankGroup g
     const int soff = in ? (int)(c * LR_CK * 2) : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      xr[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rl, in ? lvoff + 16 * i : kOutOfRange, soff, 0);
+      xr[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rl, in ? lvo[i] : kOutOfRange, soff, 0);
 #pragma unroll
     for (int i = 0; i < RT; ++i)
       pr[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rp, in ? pvoff[i] : kOutOfRange, soff, 0);
@@ -131,9 +147,14 @@ __global__ __launch_bounds__(LR_THREADS) void lowrank_part_kernel(LowRankGroup g
 #pragma unroll
       for (int d = 0; d < LR_DEPTH; ++d) {
         const uint8_t *pb = ps[d & 1];
+        // The wave's slab through its LDS region (its own rows only: LDS
+        // operations of one wave complete in order, no barrier needed).
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(xslab + xw[i]) = xr[d][i];
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bf16x8 xa = __builtin_bit_cast(bf16x8, xr[d][i]);
+          const bf16x8 xa = *reinterpret_cast<const bf16x8 *>(xslab + xrd[i]);
 #pragma unroll
           for (int t = 0; t < RT; ++t) {
             const u32x4 pf = *reinterpret_cast<const u32x4 *>(pb + (32 * t + lr) * LR_PITCH + 16 * (4 * lh + i));
