@@ -1,6 +1,7 @@
 // C ABI entry points: argument validation (host only, before any launch) and
 // dispatch to the kernels.  Declared in include/qlora_nf4.h.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -43,6 +44,28 @@ int check_linear_shapes(int64_t M, const qn_nf4_weight *W, int64_t r, float alph
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QN_OK : QN_ERR_HIP; }
+
+int check_adam_tensor(const qn_adamw_tensor &t) {
+  if (!t.param || !t.grad || !t.m_q || !t.m_step || !t.u_q || !t.u_step) return QN_ERR_NULL;
+  if (t.n <= 0 || t.n > kMaxElems) return QN_ERR_SHAPE;
+  if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.m_q, 4) || !aligned(t.u_q, 4) ||
+      !aligned(t.m_step, 4) || !aligned(t.u_step, 4))
+    return QN_ERR_ALIGN;
+  return QN_OK;
+}
+
+// The step's fp32 constants, 1 - beta and 1 - beta^t formed in double.
+int adam_consts(const qn_adamw_config &h, qn::AdamConsts &c) {
+  if (h.step < 1 || !std::isfinite(h.lr) || !std::isfinite(h.eps) || !(h.eps > 0.0f) ||
+      !std::isfinite(h.weight_decay) || !(h.beta1 >= 0.0f && h.beta1 < 1.0f) || !(h.beta2 >= 0.0f && h.beta2 < 1.0f))
+    return QN_ERR_VALUE;
+  c.lr = h.lr; c.b1 = h.beta1; c.b2 = h.beta2; c.eps = h.eps; c.wd = h.weight_decay;
+  c.c1 = (float)(1.0 - (double)h.beta1);
+  c.c2 = (float)(1.0 - (double)h.beta2);
+  c.bc1 = (float)(1.0 - std::pow((double)h.beta1, (double)h.step));
+  c.bc2 = (float)(1.0 - std::pow((double)h.beta2, (double)h.step));
+  return QN_OK;
+}
 
 }  // namespace
 
@@ -116,23 +139,43 @@ int qlora_merge(const qn_nf4_weight *W, const void *A, const void *B, int64_t r,
 
 int qn_adamw8_step(void *param, const void *grad, int64_t n, int8_t *m_q, float *m_step, uint8_t *u_q,
                    float *u_step, const qn_adamw_config *cfg, void *stream) {
-  if (!param || !grad || !m_q || !m_step || !u_q || !u_step || !cfg) return QN_ERR_NULL;
-  if (n <= 0 || n > kMaxElems) return QN_ERR_SHAPE;
-  const qn_adamw_config &h = *cfg;
-  if (h.step < 1 || !std::isfinite(h.lr) || !std::isfinite(h.eps) || !(h.eps > 0.0f) ||
-      !std::isfinite(h.weight_decay) || !(h.beta1 >= 0.0f && h.beta1 < 1.0f) || !(h.beta2 >= 0.0f && h.beta2 < 1.0f))
-    return QN_ERR_VALUE;
-  if (!aligned(param, 16) || !aligned(grad, 16) || !aligned(m_q, 4) || !aligned(u_q, 4) || !aligned(m_step, 4) ||
-      !aligned(u_step, 4))
-    return QN_ERR_ALIGN;
+  if (!cfg) return QN_ERR_NULL;
+  const qn_adamw_tensor t{param, grad, n, m_q, m_step, u_q, u_step};
+  int st = check_adam_tensor(t);
+  if (st != QN_OK) return st;
   qn::AdamConsts c{};
-  c.lr = h.lr; c.b1 = h.beta1; c.b2 = h.beta2; c.eps = h.eps; c.wd = h.weight_decay;
-  c.c1 = (float)(1.0 - (double)h.beta1);
-  c.c2 = (float)(1.0 - (double)h.beta2);
-  c.bc1 = (float)(1.0 - std::pow((double)h.beta1, (double)h.step));
-  c.bc2 = (float)(1.0 - std::pow((double)h.beta2, (double)h.step));
+  st = adam_consts(*cfg, c);
+  if (st != QN_OK) return st;
   return hip_status(qn::launch_adamw8(static_cast<uint16_t *>(param), static_cast<const uint16_t *>(grad), n, m_q,
                                       m_step, u_q, u_step, c, static_cast<hipStream_t>(stream)));
+}
+
+int qn_adamw8_step_multi(int n_tensors, const qn_adamw_tensor *tensors, const qn_adamw_config *cfg, void *stream) {
+  if (!tensors || !cfg) return QN_ERR_NULL;
+  if (n_tensors < 1) return QN_ERR_SHAPE;
+  for (int i = 0; i < n_tensors; ++i) {
+    const int st = check_adam_tensor(tensors[i]);
+    if (st != QN_OK) return st;
+  }
+  qn::AdamConsts c{};
+  const int st = adam_consts(*cfg, c);
+  if (st != QN_OK) return st;
+  for (int b = 0; b < n_tensors; b += QN_ADAMW_MULTI) {
+    qn::AdamMulti mt{};
+    mt.n = std::min(QN_ADAMW_MULTI, n_tensors - b);
+    int64_t spans = 0;
+    for (int i = 0; i < mt.n; ++i) {
+      const qn_adamw_tensor &t = tensors[b + i];
+      mt.t[i] = qn::AdamTensor{static_cast<uint16_t *>(t.param), static_cast<const uint16_t *>(t.grad), t.n, t.m_q,
+                               t.m_step, t.u_q, t.u_step};
+      mt.first[i] = spans;
+      spans += (t.n + 255) / 256;
+    }
+    mt.first[mt.n] = spans;
+    const int e = hip_status(qn::launch_adamw8_multi(mt, c, static_cast<hipStream_t>(stream)));
+    if (e != QN_OK) return e;
+  }
+  return QN_OK;
 }
 
 size_t qlora_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t r) {

@@ -67,6 +67,23 @@ struct AdamConsts {
 };
 hipError_t launch_adamw8(uint16_t *p, const uint16_t *g, int64_t n, int8_t *mq, float *ms, uint8_t *uq, float *us,
                          const AdamConsts &c, hipStream_t s);
+// The same step over up to QN_ADAMW_MULTI tensors in one launch: tensor i owns
+// spans (of 256 parameters) [first[i], first[i + 1]).
+struct AdamTensor {
+  uint16_t *p;
+  const uint16_t *g;
+  int64_t n;
+  int8_t *mq;
+  float *ms;
+  uint8_t *uq;
+  float *us;
+};
+struct AdamMulti {
+  AdamTensor t[QN_ADAMW_MULTI];
+  int64_t first[QN_ADAMW_MULTI + 1];
+  int n;
+};
+hipError_t launch_adamw8_multi(const AdamMulti &mt, const AdamConsts &c, hipStream_t s);
 
 // Adapter merged into the dequantised base (k_merge.hip).  W.K % 64 == 0, 1 <= r <= 64.
 hipError_t launch_merge(const qn_nf4_weight &W, const uint16_t *A, const uint16_t *B, int64_t r, float alpha,

@@ -29,6 +29,7 @@ QN_OP_FWD, QN_OP_BWD = 0, 1
 QN_ERR_SCRATCH = 8
 QN_NOALLOC_SCRATCH_BYTES = 16 << 20
 QN_BLOCK, QN_GROUP, QN_MAX_RANK, QN_MAX_GROUP = 64, 256, 64, 8
+QN_ADAMW_MULTI = 32
 
 _lib = None
 
@@ -76,6 +77,13 @@ class AdamWConfigStruct(ctypes.Structure):
     ]
 
 
+class AdamWTensorStruct(ctypes.Structure):
+    """qn_adamw_tensor: one tensor of a multi-tensor step."""
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("m_q", ctypes.c_void_p), ("m_step", ctypes.c_void_p), ("u_q", ctypes.c_void_p),
+                ("u_step", ctypes.c_void_p)]
+
+
 def load():
     """Load the shared library (once).  Raises if it has not been built."""
     global _lib
@@ -95,6 +103,7 @@ def load():
         "nf4_double_quant": (i32, [vp, i64, vp, vp, vp]),
         "nf4_dequant": (i32, [ctypes.POINTER(NF4WeightStruct), vp, i32, vp]),
         "qn_adamw8_step": (i32, [vp, vp, i64, vp, vp, vp, vp, ctypes.POINTER(AdamWConfigStruct), vp]),
+        "qn_adamw8_step_multi": (i32, [i32, ctypes.POINTER(AdamWTensorStruct), ctypes.POINTER(AdamWConfigStruct), vp]),
         "qlora_merge": (i32, [ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, i32, vp]),
         "qlora_workspace_size": (ctypes.c_size_t, [i32, i64, i64, i64, i64]),
         "qlora_linear_fwd": (i32, [vp, i64, ctypes.POINTER(NF4WeightStruct), vp, vp, i64, f32, vp, vp, vp,
@@ -119,7 +128,8 @@ def load():
 
 
 def exported_symbols():
-    return ["qn_codebook", "qn_table", "qn_quantize_4bit", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_merge", "qn_adamw8_step", "qlora_workspace_size",
+    return ["qn_codebook", "qn_table", "qn_quantize_4bit", "nf4_quantize", "nf4_double_quant", "nf4_dequant", "qlora_merge", "qn_adamw8_step", "qn_adamw8_step_multi",
+            "qlora_workspace_size",
             "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_workspace_size_grouped",
             "qlora_linear_fwd_grouped", "qlora_linear_bwd", "qn_status_string", "qn_version", "qn_set_gemm_variant", "qn_trace_enable",
             "qn_trace_read"]
@@ -327,6 +337,31 @@ def adamw8_step(param, grad, state: AdamW8State, lr=1e-4, beta1=0.9, beta2=0.999
         _ptr(param), _ptr(grad), state.n, _ptr(state.m_q), _ptr(state.m_step), _ptr(state.u_q), _ptr(state.u_step),
         ctypes.byref(cfg), _stream()))
     return param
+
+
+def adamw8_step_multi(params, grads, states, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                      step=None):
+    """One qn_adamw8_step_multi over several bf16 tensors in place (one launch
+    per QN_ADAMW_MULTI tensors); all states advance to the same step unless an
+    explicit step number is given."""
+    torch = _torch()
+    if not (len(params) == len(grads) == len(states)) or not params:
+        raise ValueError("params, grads and states must be non-empty lists of one length")
+    arr = (AdamWTensorStruct * len(params))()
+    for i, (p, g, st) in enumerate(zip(params, grads, states)):
+        _need(p, "param", torch.bfloat16)
+        _need(g, "grad", torch.bfloat16)
+        if p.numel() != st.n or g.numel() != st.n:
+            raise ValueError("param, grad and state sizes differ")
+        arr[i] = AdamWTensorStruct(_ptr(p), _ptr(g), st.n, _ptr(st.m_q), _ptr(st.m_step), _ptr(st.u_q),
+                                   _ptr(st.u_step))
+    if step is None:
+        step = states[0].step + 1
+    for st in states:
+        st.step = int(step)
+    cfg = AdamWConfigStruct(lr, beta1, beta2, eps, weight_decay, int(step))
+    _check("qn_adamw8_step_multi", load().qn_adamw8_step_multi(len(params), arr, ctypes.byref(cfg), _stream()))
+    return params
 
 
 def workspace_size(op, M, N, K, r):

@@ -207,6 +207,27 @@ typedef struct {
 int qn_adamw8_step(void *param, const void *grad, int64_t n, int8_t *m_q, float *m_step,
                    uint8_t *u_q, float *u_step, const qn_adamw_config *cfg, void *stream);
 
+/* The same step over several tensors (the A and B of every adapted linear of
+ * a layer or a model: [QE] "Turn a LoRA script into a QLoRA script with one
+ * config object", the adapter on every linear) in as few launches as possible:
+ * one per QN_ADAMW_MULTI tensors.  Each tensor's arguments, layout and
+ * alignment as in qn_adamw8_step; all share cfg.  Results are bit-identical to
+ * qn_adamw8_step on each tensor in turn.  QN_ERR_SHAPE for n_tensors < 1 or a
+ * tensor with n <= 0; QN_ERR_NULL, QN_ERR_ALIGN and QN_ERR_VALUE as there;
+ * nothing is launched unless every tensor passes. */
+typedef struct {
+  void *param;
+  const void *grad;
+  int64_t n;
+  int8_t *m_q;
+  float *m_step;
+  uint8_t *u_q;
+  float *u_step;
+} qn_adamw_tensor;
+#define QN_ADAMW_MULTI 32
+int qn_adamw8_step_multi(int n_tensors, const qn_adamw_tensor *tensors, const qn_adamw_config *cfg,
+                         void *stream);
+
 /* Workspace size in bytes for op = QN_OP_FWD or QN_OP_BWD at the given shape.
  * Returns 0 for an invalid op or shape. */
 #define QN_OP_FWD 0
@@ -323,7 +344,7 @@ int qlora_linear_bwd(const void *dY, const void *X, const float *H, int64_t M,
 #define QN_TRACE_GEMM_DA 8       /* reserved (dA shares the launch of kind 7)    */
 #define QN_TRACE_LOWRANK 9       /* X A^T or dY B low-rank product               */
 #define QN_TRACE_MERGE 10        /* qlora_merge kernel                           */
-#define QN_TRACE_ADAMW8 11       /* qn_adamw8_step kernel                        */
+#define QN_TRACE_ADAMW8 11       /* qn_adamw8_step(_multi) kernel                */
 int qn_trace_enable(int on);
 int qn_trace_read(int *kinds, float *ms, int cap);
 

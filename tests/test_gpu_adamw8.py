@@ -47,3 +47,35 @@ def test_adamw8_bit_exact_over_steps(n):
     assert guards_intact(pf, 2 * n), "param guard band overwritten"
     for k, nbytes in (("m_q", n), ("m_step", 4 * nb), ("u_q", n), ("u_step", 4 * nb)):
         assert guards_intact(bufs[k][0], nbytes), f"{k} guard band overwritten"
+
+
+def test_adamw8_multi_equals_single_calls():
+    """qn_adamw8_step_multi over 40 tensors of ragged sizes (two launches of at
+    most QN_ADAMW_MULTI tensors) equals qn_adamw8_step on each tensor, bit for
+    bit, over three consecutive steps; the tensors' buffers are guard-banded."""
+    sizes = [1, 3, 63, 64, 65, 255, 256, 257, 1000, 4096 + 5] * 4
+    assert len(sizes) > lib.QN_ADAMW_MULTI
+    say(f"adamw8 multi over {len(sizes)} tensors")
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.99, eps=1e-6, weight_decay=0.02)
+    rng = np.random.default_rng(77)
+    multi, single, guards = [], [], []
+    for n in sizes:
+        p0 = torch.from_numpy(synth.bf16_values(synth.to_bf16((rng.standard_normal(n) * 0.02).astype(np.float32))))
+        pf, pd = guarded(2 * n, torch.bfloat16)
+        pd.copy_(p0.to(torch.bfloat16).to(dev()))
+        guards.append((pf, 2 * n))
+        multi.append((pd, lib.AdamW8State(n, dev())))
+        single.append((p0.to(torch.bfloat16).to(dev()), lib.AdamW8State(n, dev())))
+    for t in range(1, 4):
+        grads = [torch.from_numpy(synth.bf16_values(synth.to_bf16(
+            (rng.standard_normal(n) * 0.05).astype(np.float32)))).to(torch.bfloat16).to(dev()) for n in sizes]
+        lib.adamw8_step_multi([p for p, _ in multi], grads, [s for _, s in multi], step=t, **hp)
+        for (p, s), g in zip(single, grads):
+            lib.adamw8_step(p, g, s, step=t, **hp)
+        torch.cuda.synchronize()
+        for i, ((pm, sm), (ps, ss)) in enumerate(zip(multi, single)):
+            np.testing.assert_array_equal(host(pm).view(np.uint16), host(ps).view(np.uint16), err_msg=f"param {i} step {t}")
+            for k in ("m_q", "u_q", "m_step", "u_step"):
+                np.testing.assert_array_equal(host(getattr(sm, k)), host(getattr(ss, k)), err_msg=f"{k} {i} step {t}")
+    for pf, nbytes in guards:
+        assert guards_intact(pf, nbytes), "param guard band overwritten"

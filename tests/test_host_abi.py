@@ -220,3 +220,28 @@ def test_adamw8_rejects_bad_arguments():
     assert call(lr=float("inf")) == 7
     assert call(p=FAKE + 2) == 4
     assert call(aq=FAKE + 1) == 4
+
+
+def test_adamw8_multi_rejects_bad_arguments():
+    """Every tensor is checked before anything is launched: a bad tensor
+    anywhere in the list (here the last of 40) is reported with the same code
+    as the single-tensor call gives it."""
+    L = lib.load()
+    vp = ctypes.c_void_p
+    good = lib.AdamWTensorStruct(FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE)
+    ok = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1)
+
+    def call(last=None, count=40, **kw):
+        arr = (lib.AdamWTensorStruct * 40)(*([good] * 40))
+        if last is not None:
+            arr[39] = last
+        cfg = lib.AdamWConfigStruct(**dict(ok, **kw))
+        return L.qn_adamw8_step_multi(count, arr, ctypes.byref(cfg), vp(0))
+    assert L.qn_adamw8_step_multi(1, None, ctypes.byref(lib.AdamWConfigStruct(**ok)), vp(0)) == 1
+    assert call(count=0) == 2
+    assert call(last=lib.AdamWTensorStruct(0, FAKE, 64, FAKE, FAKE, FAKE, FAKE)) == 1
+    assert call(last=lib.AdamWTensorStruct(FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE)) == 2
+    assert call(last=lib.AdamWTensorStruct(FAKE + 2, FAKE, 64, FAKE, FAKE, FAKE, FAKE)) == 4
+    assert call(last=lib.AdamWTensorStruct(FAKE, FAKE, 64, FAKE + 1, FAKE, FAKE, FAKE)) == 4
+    assert call(step=0) == 7
+    assert call(eps=-1.0) == 7
