@@ -71,9 +71,9 @@ KERNEL_SOURCE = {
 # bytes.  Keyed by kernel and workload; `sha256` is that of the kernel's source
 # file and qn_device.h when the counters were taken.
 TRAFFIC = {
-    "gemm_fwd_70b": {"bytes": 1560065844, "sha256": "969c3652d168bad5259a8ea0cb57a0087f0b292906097d3cc2ea7eea2513e74a"},
-    "lowrank_70b": {"bytes": 177342016, "sha256": "9fbca7dc2b982463e7e354c07a1d3f79208eec4bd5ac9bc320bfbba9ff1e7ec5"},
-    "gemv_70b": {"bytes": 114272722, "sha256": "5c0de8bafcde596c1510c948dd0b6f7a0dfc6e7ba34d07114dc3322194a9d552"},
+    "gemm_fwd_70b": {"bytes": 1555335864, "sha256": "969c3652d168bad5259a8ea0cb57a0087f0b292906097d3cc2ea7eea2513e74a"},
+    "lowrank_70b": {"bytes": 176672545, "sha256": "a57c50ee535319b8bbe9d0dfabf389574080cf28428456f786f074f90eb225a9"},
+    "gemv_70b": {"bytes": 114272651, "sha256": "5c0de8bafcde596c1510c948dd0b6f7a0dfc6e7ba34d07114dc3322194a9d552"},
 }
 
 # The configurations (N, K) of the linear layers.
@@ -441,7 +441,8 @@ def main():
     weight_bytes = L.weight_bytes()
     layer_stage = {}
     if not args.no_stages:
-        layer_stage = layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weight_bytes, pre_us)
+        layer_stage = layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weight_bytes, pre_us,
+                                   dec_us)
     quality = L.quality
     del L
     torch.cuda.empty_cache()
@@ -496,7 +497,7 @@ def main():
 
 
 
-def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weight_bytes, pre_us):
+def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weight_bytes, pre_us, dec_us):
     """The 70B layer's other timings: the forward as 7 single calls and as one
     call over all 7 linears, each forward tiling, each linear alone, the merge
     of all adapters into bf16 weights and one 8-bit AdamW step over them."""
@@ -565,6 +566,7 @@ def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weig
     ctx = context_ceilings(torch, dev, log)
     f, w = flops_pre, weight_bytes
     ctx["nf4_prefill_over_dense_bf16"] = round(f / pre_us / 1e6 / ctx["hipblaslt_bf16_layer_M4096_TFLOPs"], 3)
+    ctx["nf4_decode_speedup_over_dense_bf16"] = round(ctx["dense_bf16_decode_M1_layer_us"] / dec_us, 2)
     return {"context_ceilings": ctx,
             "prefill_M4096_single_calls_TFLOPs": round(f / pre_single_us / 1e6, 1),
             "prefill_M4096_one_call_all7_TFLOPs": round(f / pre_all7_us / 1e6, 1),
@@ -606,6 +608,7 @@ def context_ceilings(torch, dev, log):
     g = torch.Generator(device=dev)
     g.manual_seed(7)
     per, tot_us, tot_fl = {}, 0.0, 0
+    dec_us, dec_bytes = 0.0, 0
     for name, (N, K) in L70B.items():
         X = torch.randn((M70_PRE, K), generator=g, device=dev).to(torch.bfloat16)
         Wt = (torch.randn((K, N), generator=g, device=dev) * 0.015).to(torch.bfloat16)   # [K, N], contiguous
@@ -615,12 +618,19 @@ def context_ceilings(torch, dev, log):
         per[name] = round(fl / us / 1e6, 1)
         tot_us += us
         tot_fl += fl
-        del X, Wt, Y
+        X1, Y1 = X[:1].contiguous(), Y[:1].contiguous()
+        dec_us += timed(lambda: torch.matmul(X1, Wt, out=Y1), 20)
+        dec_bytes += 2 * N * K
+        del X, Wt, Y, X1, Y1
     torch.cuda.empty_cache()
     return {"device_copy_GBps": round(copy, 1), "hipblaslt_bf16_layer_M4096_TFLOPs": round(tot_fl / tot_us / 1e6, 1),
             "hipblaslt_bf16_per_linear_TFLOPs": per,
+            "dense_bf16_decode_M1_layer_us": round(dec_us, 1),
+            "dense_bf16_decode_M1_weight_GBps": round(dec_bytes / dec_us / 1e3, 1),
             "note": "512 MiB device-to-device copy (read + write counted); torch.matmul on bf16 weights of the same "
-                    "shapes (2MNK, no adapter, no 4-bit storage): the dense GEMM the method's expansion competes with"}
+                    "shapes (2MNK, no adapter, no 4-bit storage): the dense GEMM the method's expansion competes with; "
+                    "dense decode: torch.matmul of one activation row by each linear's bf16 weight (1.7 GB for the "
+                    "layer), the seven eager calls summed"}
 
 
 def other_stages(torch, lib, dev, cap, log):
