@@ -554,15 +554,25 @@ def layer_extras(torch, lib, dev, cap, L, pre_groups, all7, log, flops_pre, weig
                                                                             [gr for _, gr, _ in ad_t],
                                                                             [stt for _, _, stt in ad_t],
                                                                             lr=1e-4, step=2), replays=10)
+    ad_host = [lib.AdamW8State(t.numel(), dev, host=True) for t, _, _ in ad_t]
+    lib.adamw8_step_multi([t for t, _, _ in ad_t], [gr for _, gr, _ in ad_t], ad_host, lr=1e-4, step=1)
+    adam_host_us = graph_time_us(torch, cap, lambda: lib.adamw8_step_multi([t for t, _, _ in ad_t],
+                                                                           [gr for _, gr, _ in ad_t], ad_host,
+                                                                           lr=1e-4, step=2), replays=5)
     adam_bytes = ad_n * (2 + 2 + 2 + 2 + 1 + 1) + 2 * 2 * 4 * ((ad_n + 63) // 64)
+    state_bytes = 2 * (2 * ad_n + 2 * 4 * ((ad_n + 63) // 64))   # both codes and steps, read and written
     adamw8 = {"us": round(adam_multi_us, 2), "params": ad_n, "GBps": round(adam_bytes / adam_multi_us / 1e3, 1),
               "hbm_frac": round(adam_bytes / adam_multi_us / 1e3 / PEAK_HBM_GBPS, 4),
               "per_tensor_calls_us": round(adam_us, 2),
+              "host_state_us": round(adam_host_us, 1),
+              "host_state_link_GBps": round(state_bytes / adam_host_us / 1e3, 1),
               "state_bytes_per_param": 2.125,
               "note": "one qn_adamw8_step_multi over the 14 tensors (A and B of the 7 linears, r = 64); "
                       "per_tensor_calls_us: 14 qn_adamw8_step calls; bytes = bf16 parameter read and written, bf16 "
-                      "gradient, both 8-bit codes read and written, block steps"}
-    del ad_t
+                      "gradient, both 8-bit codes read and written, block steps; host_state: the same step with "
+                      "the 8-bit state in pinned host memory (the paged placement), its state bytes crossing the "
+                      "host link"}
+    del ad_t, ad_host
     ctx = context_ceilings(torch, dev, log)
     f, w = flops_pre, weight_bytes
     ctx["nf4_prefill_over_dense_bf16"] = round(f / pre_us / 1e6 / ctx["hipblaslt_bf16_layer_M4096_TFLOPs"], 3)

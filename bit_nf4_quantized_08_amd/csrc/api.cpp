@@ -2,6 +2,7 @@
 // dispatch to the kernels.  Declared in include/qlora_nf4.h.
 
 #include <algorithm>
+#include <vector>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -45,12 +46,44 @@ int check_linear_shapes(int64_t M, const qn_nf4_weight *W, int64_t r, float alph
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QN_OK : QN_ERR_HIP; }
 
+// The address a kernel uses for a buffer the caller placed in device memory,
+// managed memory, or pinned host memory mapped for the device (the optimizer
+// state's host placement); nullptr for anything else, pageable host memory
+// included, which a kernel could not reach.
+template <typename T>
+T *device_view(T *p) {
+  void *vp = const_cast<void *>(static_cast<const void *>(p));
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, vp) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) return p;
+  if (at.type != hipMemoryTypeHost) return nullptr;
+  void *dp = nullptr;
+  if (hipHostGetDevicePointer(&dp, vp, 0) != hipSuccess || !dp) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return static_cast<T *>(dp);
+}
+
 int check_adam_tensor(const qn_adamw_tensor &t) {
   if (!t.param || !t.grad || !t.m_q || !t.m_step || !t.u_q || !t.u_step) return QN_ERR_NULL;
   if (t.n <= 0 || t.n > kMaxElems) return QN_ERR_SHAPE;
   if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.m_q, 4) || !aligned(t.u_q, 4) ||
       !aligned(t.m_step, 4) || !aligned(t.u_step, 4))
     return QN_ERR_ALIGN;
+  return QN_OK;
+}
+
+// Replaces each of a validated tensor's pointers by the address the kernel
+// uses (the last check before a launch: it asks the HIP runtime).
+int place_adam_tensor(qn_adamw_tensor &t) {
+  qn_adamw_tensor d{device_view(t.param), device_view(t.grad), t.n, device_view(t.m_q), device_view(t.m_step),
+                    device_view(t.u_q), device_view(t.u_step)};
+  if (!d.param || !d.grad || !d.m_q || !d.m_step || !d.u_q || !d.u_step) return QN_ERR_MEMORY;
+  t = d;
   return QN_OK;
 }
 
@@ -140,14 +173,16 @@ int qlora_merge(const qn_nf4_weight *W, const void *A, const void *B, int64_t r,
 int qn_adamw8_step(void *param, const void *grad, int64_t n, int8_t *m_q, float *m_step, uint8_t *u_q,
                    float *u_step, const qn_adamw_config *cfg, void *stream) {
   if (!cfg) return QN_ERR_NULL;
-  const qn_adamw_tensor t{param, grad, n, m_q, m_step, u_q, u_step};
+  qn_adamw_tensor t{param, grad, n, m_q, m_step, u_q, u_step};
   int st = check_adam_tensor(t);
   if (st != QN_OK) return st;
   qn::AdamConsts c{};
   st = adam_consts(*cfg, c);
   if (st != QN_OK) return st;
-  return hip_status(qn::launch_adamw8(static_cast<uint16_t *>(param), static_cast<const uint16_t *>(grad), n, m_q,
-                                      m_step, u_q, u_step, c, static_cast<hipStream_t>(stream)));
+  st = place_adam_tensor(t);
+  if (st != QN_OK) return st;
+  return hip_status(qn::launch_adamw8(static_cast<uint16_t *>(t.param), static_cast<const uint16_t *>(t.grad), n,
+                                      t.m_q, t.m_step, t.u_q, t.u_step, c, static_cast<hipStream_t>(stream)));
 }
 
 int qn_adamw8_step_multi(int n_tensors, const qn_adamw_tensor *tensors, const qn_adamw_config *cfg, void *stream) {
@@ -160,12 +195,17 @@ int qn_adamw8_step_multi(int n_tensors, const qn_adamw_tensor *tensors, const qn
   qn::AdamConsts c{};
   const int st = adam_consts(*cfg, c);
   if (st != QN_OK) return st;
+  std::vector<qn_adamw_tensor> dev(tensors, tensors + n_tensors);   // the kernel's addresses
+  for (auto &t : dev) {
+    const int sp = place_adam_tensor(t);
+    if (sp != QN_OK) return sp;
+  }
   for (int b = 0; b < n_tensors; b += QN_ADAMW_MULTI) {
     qn::AdamMulti mt{};
     mt.n = std::min(QN_ADAMW_MULTI, n_tensors - b);
     int64_t spans = 0;
     for (int i = 0; i < mt.n; ++i) {
-      const qn_adamw_tensor &t = tensors[b + i];
+      const qn_adamw_tensor &t = dev[b + i];
       mt.t[i] = qn::AdamTensor{static_cast<uint16_t *>(t.param), static_cast<const uint16_t *>(t.grad), t.n, t.m_q,
                                t.m_step, t.u_q, t.u_step};
       mt.first[i] = spans;
@@ -333,6 +373,7 @@ const char *qn_status_string(int status) {
     case QN_ERR_HIP: return "HIP launch error";
     case QN_ERR_VALUE: return "invalid scalar value";
     case QN_ERR_SCRATCH: return "problem needs more scratch than the static buffer holds";
+    case QN_ERR_MEMORY: return "buffer is neither device memory nor pinned host memory mapped for the device";
     default: return "unknown status";
   }
 }

@@ -27,6 +27,7 @@ QN_NF4, QN_FP4 = 0, 1
 QUANT_TYPES = {"nf4": QN_NF4, "fp4": QN_FP4}
 QN_OP_FWD, QN_OP_BWD = 0, 1
 QN_ERR_SCRATCH = 8
+QN_ERR_MEMORY = 9
 QN_NOALLOC_SCRATCH_BYTES = 16 << 20
 QN_BLOCK, QN_GROUP, QN_MAX_RANK, QN_MAX_GROUP = 64, 256, 64, 8
 QN_ADAMW_MULTI = 32
@@ -307,16 +308,22 @@ def qlora_merge(w: NF4Weight, A, B, alpha, out_dtype="bf16", use_double_quant=Tr
 
 
 class AdamW8State:
-    """8-bit block-wise AdamW state of one bf16 tensor (zeros: before the first step)."""
+    """8-bit block-wise AdamW state of one bf16 tensor (zeros: before the first step).
 
-    def __init__(self, n, device="cuda"):
+    host=True places the state in pinned host memory mapped for the device
+    (the "paged" placement: none of its bytes occupy device memory, and the
+    step reads and writes it across the host link)."""
+
+    def __init__(self, n, device="cuda", host=False):
         torch = _torch()
         nb = (n + 63) // 64
         self.n = n
-        self.m_q = torch.zeros(n, dtype=torch.int8, device=device)
-        self.m_step = torch.zeros(nb, dtype=torch.float32, device=device)
-        self.u_q = torch.zeros(n, dtype=torch.uint8, device=device)
-        self.u_step = torch.zeros(nb, dtype=torch.float32, device=device)
+        self.host = bool(host)
+        kw = dict(device="cpu", pin_memory=True) if self.host else dict(device=device)
+        self.m_q = torch.zeros(n, dtype=torch.int8, **kw)
+        self.m_step = torch.zeros(nb, dtype=torch.float32, **kw)
+        self.u_q = torch.zeros(n, dtype=torch.uint8, **kw)
+        self.u_step = torch.zeros(nb, dtype=torch.float32, **kw)
         self.step = 0
 
 

@@ -52,8 +52,10 @@ typedef enum {
   QN_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than qlora_workspace_size() */
   QN_ERR_HIP = 6,        /* the HIP runtime reported an error on launch           */
   QN_ERR_VALUE = 7,      /* a scalar argument is not finite                       */
-  QN_ERR_SCRATCH = 8     /* the no-allocation entry point's static scratch is too */
+  QN_ERR_SCRATCH = 8,    /* the no-allocation entry point's static scratch is too */
                          /* small for this problem                                */
+  QN_ERR_MEMORY = 9      /* a buffer is neither device memory nor pinned host     */
+                         /* memory mapped for the device                          */
 } qn_status;
 
 typedef enum { QN_F32 = 0, QN_BF16 = 1 } qn_dtype;
@@ -191,15 +193,23 @@ int qlora_merge(const qn_nf4_weight *W, const void *A, const void *B, int64_t r,
  * -127, 127); the second through its square root u' = sqrt(v'), step_u =
  * max u'/255, k_u = clamp(ceil(u'/step_u - 1/2), 0, 255); a zero block has step
  * 0 and codes 0.  2.125 bytes of state per parameter.
- *   param  device bf16 [n], updated in place;  grad device bf16 [n].
- *   m_q    device int8 [n];  m_step device fp32 [ceil(n/64)];
- *   u_q    device uint8 [n]; u_step device fp32 [ceil(n/64)]: read and rewritten;
+ *   param  bf16 [n], updated in place;  grad bf16 [n].
+ *   m_q    int8 [n];  m_step fp32 [ceil(n/64)];
+ *   u_q    uint8 [n]; u_step fp32 [ceil(n/64)]: read and rewritten;
  *          all zero before the first step.
  * param, grad 16-byte aligned; m_q, u_q, m_step, u_step 4-byte aligned.
+ * Placement ([QE] "Turn a memory spike into a slowdown with a paged
+ * optimizer": optimizer state that does not fit next to the model can live
+ * in host memory, at the price of a slower step).  Each of the six buffers
+ * may be device memory (or managed memory), or pinned host memory mapped for
+ * the device (hipHostMalloc; torch's pin_memory=True): the kernel then reads
+ * and writes it across the host link, the state's bytes never occupying
+ * device memory.  Host memory that is not pinned and mapped (pageable
+ * memory, an unknown pointer) returns QN_ERR_MEMORY, checked with
+ * hipPointerGetAttributes and hipHostGetDevicePointer before any launch.  The
+ * library allocates none of it.
  * QN_ERR_VALUE for step < 1, lr, eps or weight_decay not finite, a beta
- * outside [0, 1) or eps <= 0.  (The pages' "paged" placement of this state in
- * host memory is a property of where the caller puts the buffers; the
- * library allocates none.) */
+ * outside [0, 1) or eps <= 0. */
 typedef struct {
   float lr, beta1, beta2, eps, weight_decay;
   int64_t step;
@@ -213,8 +223,8 @@ int qn_adamw8_step(void *param, const void *grad, int64_t n, int8_t *m_q, float 
  * one per QN_ADAMW_MULTI tensors.  Each tensor's arguments, layout and
  * alignment as in qn_adamw8_step; all share cfg.  Results are bit-identical to
  * qn_adamw8_step on each tensor in turn.  QN_ERR_SHAPE for n_tensors < 1 or a
- * tensor with n <= 0; QN_ERR_NULL, QN_ERR_ALIGN and QN_ERR_VALUE as there;
- * nothing is launched unless every tensor passes. */
+ * tensor with n <= 0; QN_ERR_NULL, QN_ERR_ALIGN, QN_ERR_MEMORY and
+ * QN_ERR_VALUE as there; nothing is launched unless every tensor passes. */
 typedef struct {
   void *param;
   const void *grad;

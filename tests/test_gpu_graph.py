@@ -60,3 +60,40 @@ def test_graph_replays_match_eager(M):
         assert torch.equal(Y, Y_ref), f"replay {rep}: Y"
         assert torch.equal(dX, dX_ref) and torch.equal(dA, dA_ref) and torch.equal(dB, dB_ref), f"replay {rep}: grads"
         assert not torch.equal(other, Y_ref)
+
+
+@pytest.mark.parametrize("host_state", [False, True])
+def test_graph_replays_adamw8_match_eager(host_state):
+    """A captured multi-tensor 8-bit AdamW step (its state in device memory, or
+    in pinned host memory) replayed three times equals the same step called
+    eagerly on copies, bit for bit after every replay; the placement check runs
+    at capture time and the replays reuse its addresses."""
+    say(f"graph capture of the multi-tensor AdamW step, host_state={host_state}")
+    sizes = [1000, 64, 4096 + 5]
+    rng = np.random.default_rng(5)
+    pa = [torch.from_numpy((rng.standard_normal(n) * 0.02).astype(np.float32)).to(torch.bfloat16).to(dev())
+          for n in sizes]
+    pb = [p.clone() for p in pa]
+    gs = [torch.from_numpy((rng.standard_normal(n) * 0.05).astype(np.float32)).to(torch.bfloat16).to(dev())
+          for n in sizes]
+    sa = [lib.AdamW8State(n, dev()) for n in sizes]
+    sb = [lib.AdamW8State(n, dev(), host=host_state) for n in sizes]
+    hp = dict(lr=1e-3, weight_decay=0.01, step=3)
+    lib.adamw8_step_multi(pb, gs, sb, **hp)   # one eager call outside capture on each side
+    lib.adamw8_step_multi(pa, gs, sa, **hp)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        lib.adamw8_step_multi(pb, gs, sb, **hp)
+    for rep in range(3):
+        g.replay()
+        lib.adamw8_step_multi(pa, gs, sa, **hp)
+        other = torch.ones(1024, device=dev()).sum()   # eager work of the program
+        torch.cuda.synchronize()
+        assert float(other) == 1024.0
+        for i in range(len(sizes)):
+            assert torch.equal(pa[i].view(torch.int16), pb[i].view(torch.int16)), f"replay {rep}: param {i}"
+            for k in ("m_q", "m_step", "u_q", "u_step"):
+                a, b = getattr(sa[i], k).cpu(), getattr(sb[i], k).cpu()
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: {k} of tensor {i}"

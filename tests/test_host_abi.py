@@ -49,6 +49,7 @@ def test_status_strings():
     assert lib.status_string(0) == "ok"
     assert "null" in lib.status_string(1)
     assert lib.status_string(99) == "unknown status"
+    assert "pinned host memory" in lib.status_string(lib.QN_ERR_MEMORY)
 
 
 def _w(N=64, K=64, codes=FAKE, absmax=FAKE, absmax_q=0, scale2=0, quant_type=0):
@@ -220,6 +221,9 @@ def test_adamw8_rejects_bad_arguments():
     assert call(lr=float("inf")) == 7
     assert call(p=FAKE + 2) == 4
     assert call(aq=FAKE + 1) == 4
+    # well-formed arguments at an address that is neither device memory nor
+    # mapped host memory: rejected before any launch
+    assert call() == lib.QN_ERR_MEMORY
 
 
 def test_adamw8_multi_rejects_bad_arguments():
@@ -245,3 +249,4 @@ def test_adamw8_multi_rejects_bad_arguments():
     assert call(last=lib.AdamWTensorStruct(FAKE, FAKE, 64, FAKE + 1, FAKE, FAKE, FAKE)) == 4
     assert call(step=0) == 7
     assert call(eps=-1.0) == 7
+    assert call() == lib.QN_ERR_MEMORY
