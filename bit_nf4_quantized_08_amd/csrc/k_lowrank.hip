@@ -184,32 +184,45 @@ __global__ __launch_bounds__(LR_THREADS) void lowrank_part_kernel(LowRankGroup g
 }
 
 // Adds the ranges' partial products in range order and writes the outputs.  A
-// workgroup owns FIN_ROWS rows x 64 columns (a thread: one column of four
-// rows, every range's partial loaded before the in-order sum), staged in LDS
-// so that both the row-major and the transposed outputs are written along
+// workgroup owns FIN_ROWS rows x RW columns (RW: the launch's largest rank
+// rounded up to 16, 32 or 64); thread t owns elements t, t + 256, ... of that
+// tile, and every range's partial of all of them is loaded before the first
+// sum, so that the workgroup waits for memory once.  The sums are staged in
+// LDS so that both the row-major and the transposed outputs are written along
 // their rows.
+template <int RW>
 __global__ __launch_bounds__(256) void lowrank_finish_kernel(LowRankGroup grp) {
+  constexpr int E = FIN_ROWS * RW / 256;   // elements per thread
+  static_assert(E >= 1 && FIN_ROWS * RW == 256 * E && RW <= 64, "finish tile");
   __shared__ float tile[FIN_ROWS][65];
   const LowRankArgs a = grp.p[__builtin_amdgcn_readfirstlane((int)blockIdx.y)];
   const int64_t m0 = (int64_t)blockIdx.x * FIN_ROWS;
   if (m0 >= lowrank_rows(a)) return;
-  const int tid = threadIdx.x, j = tid & 63, rq = tid >> 6;
+  const int tid = threadIdx.x;
   const int64_t Rp = align32(a.R), plane = a.M * Rp;
   const int S = a.splits;
+  // The loads carry no condition, so that they all issue before the first
+  // wait: lanes outside the problem read the first element of each range, and
+  // slots past the last range re-read the last one; both are discarded.
+  float pv[E][LR_MAX_SPLITS];
+  bool in[E];
 #pragma unroll
-  for (int q = 0; q < FIN_ROWS / 4; ++q) {
-    const int r = rq + 4 * q;
+  for (int i = 0; i < E; ++i) {
+    const int e = tid + 256 * i, r = e / RW, j = e % RW;
     const int64_t m = m0 + r;
-    const bool in = m < a.M && j < a.R;
-    const float *p = a.part + (in ? m * Rp + j : 0);
-    float pv[LR_MAX_SPLITS];
+    in[i] = m < a.M && j < a.R;
+    const float *p = a.part + (in[i] ? m * Rp + j : 0);
 #pragma unroll
-    for (int s = 0; s < LR_MAX_SPLITS; ++s) pv[s] = (in && s < S) ? p[s * plane] : 0.0f;
+    for (int s = 0; s < LR_MAX_SPLITS; ++s) pv[i][s] = p[(int64_t)min(s, S - 1) * plane];
+  }
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = tid + 256 * i, r = e / RW, j = e % RW;
     float v = 0.0f;
 #pragma unroll
     for (int s = 0; s < LR_MAX_SPLITS; ++s)
-      if (s < S) v += pv[s];
-    tile[r][j] = v;
+      if (s < S) v += pv[i][s];
+    tile[r][j] = in[i] ? v : 0.0f;
   }
   __syncthreads();
   for (int idx = tid; idx < FIN_ROWS * 64; idx += 256) {
@@ -262,7 +275,10 @@ hipError_t launch_lowrank_n(const LowRankArgs *a, int n, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lowrank_finish_kernel, dim3((unsigned)fin, (unsigned)n), dim3(256), 0, st, grp);
+  const dim3 fgrid((unsigned)fin, (unsigned)n);
+  if (R <= 16) hipLaunchKernelGGL(lowrank_finish_kernel<16>, fgrid, dim3(256), 0, st, grp);
+  else if (R <= 32) hipLaunchKernelGGL(lowrank_finish_kernel<32>, fgrid, dim3(256), 0, st, grp);
+  else hipLaunchKernelGGL(lowrank_finish_kernel<64>, fgrid, dim3(256), 0, st, grp);
   return hipGetLastError();
 }
 
