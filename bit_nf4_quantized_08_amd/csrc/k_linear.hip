@@ -398,34 +398,64 @@ __global__ __launch_bounds__(kThreads) void gemv_epilogue_kernel(EpiGroup g) {
   float *H_out = ea.H_out;
   const int eblock = (int)blockIdx.x - g.start[gi];
   const int64_t n0 = (int64_t)eblock * EPI_ROWS;
-  // The split sums of this thread's outputs first, so that their loads
-  // overlap those of H and B.
-  float ysum[(8 * EPI_ROWS + kThreads - 1) / kThreads];
-#pragma unroll
-  for (int u = 0; u < (8 * EPI_ROWS + kThreads - 1) / kThreads; ++u) {
-    const int idx = threadIdx.x + u * kThreads;
-    ysum[u] = 0.0f;
-    if (idx < M * EPI_ROWS) {
-      const int64_t m = idx / EPI_ROWS, i = idx % EPI_ROWS;
-      for (int s = 0; s < splits; ++s) ysum[u] += y_part[((int64_t)s * M + m) * N + n0 + i];
-    }
-  }
-  for (int idx = threadIdx.x; idx < M * 64; idx += kThreads) {
-    const int m = idx / 64, j = idx % 64;
-    float v = 0.0f;
-    if (j < r) {
-#pragma unroll 8
-      for (int s = 0; s < hsplits; ++s) v += h_part[((int64_t)s * M + m) * 64 + j];
-    }
-    Hs[idx] = v;
-    if (H_out && eblock == 0 && j < r) H_out[m * r + j] = v;
-  }
   const int t = threadIdx.x, row = t >> 3, j0 = 8 * (t & 7);
   const int64_t n = n0 + row;  // N % EPI_ROWS == 0
+  // This thread's slice of B's row n first, so that its load overlaps those
+  // of the partial sums below.  The load has no condition: a thread without
+  // a 16-byte slice (r not a multiple of 8, or j0 >= r) reads B's first 16
+  // bytes (B is 16-byte aligned and holds at least EPI_ROWS rows) and
+  // discards them.
+  const bool b16 = r % 8 == 0, bin = b16 && j0 < r;
+  const u32x4 bw = *reinterpret_cast<const u32x4 *>(B + (bin ? n * r + j0 : 0));
+  // Thread t sums output (t / EPI_ROWS, n0 + t % EPI_ROWS) over the K-segments
+  // (8 EPI_ROWS == kThreads: at most one output each) and H entries t and
+  // t + kThreads over the H ranges, in range order.  The loads of a batch of
+  // ranges carry no condition (threads without an element read the first
+  // element, slots past the last range re-read the last one; both are
+  // discarded), so that each batch waits for memory once.
+  static_assert(8 * EPI_ROWS == kThreads && 8 * 64 <= 2 * kThreads, "epilogue thread map");
+  const bool yo = t < M * EPI_ROWS;
+  const float *yp = y_part + (yo ? (int64_t)(t / EPI_ROWS) * N + n0 + t % EPI_ROWS : 0);
+  const int64_t ys = M * N, hs = M * 64;
+  bool ho[2];
+  const float *hp[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = t + u * kThreads;
+    ho[u] = idx < M * 64 && idx % 64 < r;
+    hp[u] = h_part + (ho[u] ? idx : 0);
+  }
+  float ysum = 0.0f, hsum[2] = {0.0f, 0.0f};
+  constexpr int BATCH = 8;
+  const int nr = max(splits, hsplits);
+  for (int s0 = 0; s0 < nr; s0 += BATCH) {
+    float yv[BATCH], hv[2][BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      yv[q] = yp[(int64_t)min(s0 + q, splits - 1) * ys];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) hv[u][q] = hp[u][(int64_t)min(s0 + q, hsplits - 1) * hs];
+    }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      if (s0 + q < splits) ysum += yv[q];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (s0 + q < hsplits) hsum[u] += hv[u][q];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = t + u * kThreads;
+    if (idx < 8 * 64) {
+      const float v = ho[u] ? hsum[u] : 0.0f;
+      Hs[idx] = v;
+      if (H_out && eblock == 0 && ho[u]) H_out[(idx / 64) * r + idx % 64] = v;
+    }
+  }
   float b[8];
-  if (r % 8 == 0) {
-    const u32x4 v = j0 < r ? *reinterpret_cast<const u32x4 *>(B + n * r + j0) : u32x4{0, 0, 0, 0};
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if (b16) {
+    const uint32_t w[4] = {bin ? bw.x : 0u, bin ? bw.y : 0u, bin ? bw.z : 0u, bin ? bw.w : 0u};
 #pragma unroll
     for (int q = 0; q < 4; ++q) { b[2 * q] = bf16_lo(w[q]); b[2 * q + 1] = bf16_hi(w[q]); }
   } else {
@@ -445,14 +475,7 @@ __global__ __launch_bounds__(kThreads) void gemv_epilogue_kernel(EpiGroup g) {
     if (j0 == 0) Ls[m * EPI_ROWS + row] = l;
   }
   __syncthreads();
-#pragma unroll
-  for (int u = 0; u < (8 * EPI_ROWS + kThreads - 1) / kThreads; ++u) {
-    const int idx = t + u * kThreads;
-    if (idx < M * EPI_ROWS) {
-      const int64_t m = idx / EPI_ROWS, i = idx % EPI_ROWS;
-      Y[m * N + n0 + i] = f32_to_bf16(__builtin_fmaf(s_lora, Ls[idx], ysum[u]));
-    }
-  }
+  if (yo) Y[(int64_t)(t / EPI_ROWS) * N + n0 + t % EPI_ROWS] = f32_to_bf16(__builtin_fmaf(s_lora, Ls[t], ysum));
 }
 
 // ================================================================ host side
