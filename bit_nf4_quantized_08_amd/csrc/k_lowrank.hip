@@ -325,29 +325,40 @@ __global__ __launch_bounds__(CR_THREADS) void colred_kernel(ColRedArgs a0, ColRe
   const int split = blockIdx.y;
   const int64_t mb = (int64_t)split * CR_RB;
 
-  // Activation loads first (all of this wave's row pairs), so their latency
-  // overlaps the factor preload below.
+  // The factor slice (rows j < R, columns [mb, mb + RB) of Lt) is loaded
+  // first and the activations (all of this wave's row pairs) after it, so
+  // that waiting for the slice leaves the activation loads in flight.  The
+  // slice loads have no condition (an index outside Lt is clamped into it and
+  // its value replaced by zero), so they all issue before the first wait.
+  constexpr int LTN = CR_PAIRS * R / CR_THREADS;
+  static_assert(LTN * CR_THREADS == CR_PAIRS * R, "factor slice thread map");
+  uint32_t ltv[LTN];
+#pragma unroll
+  for (int i = 0; i < LTN; ++i) {
+    const int idx = tid + i * CR_THREADS, j = idx / CR_PAIRS, p = idx % CR_PAIRS;
+    const int64_t m = mb + 2 * p;
+    const int64_t jc = j < a.R ? j : a.R - 1, mc = m < a.Mp ? m : a.Mp - 2;
+    ltv[i] = *reinterpret_cast<const uint32_t *>(a.Lt + jc * a.Mp + mc);
+  }
   const rsrc_t rq = make_rsrc(a.Q + mb * a.ldq, (a.M - mb) * a.ldq * 2);
   const int64_t c = c0 + 2 * lane;
   const bool cin = c < a.Ncols;
-  const uint32_t qoff = cin ? (uint32_t)(c * 2) : kOutOfRange;
   constexpr int U = CR_PAIRS / 4;
   uint32_t q[U][2];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    // Columns past the end read zero through the out-of-range offset (the
+    // offset is selected, not the load, so that no load sits in a branch).
     const int p = wave + 4 * u;
-    const uint32_t r0 = (uint32_t)(2 * p) * (uint32_t)(a.ldq * 2);
-    q[u][0] = cin ? __builtin_amdgcn_raw_buffer_load_b32(rq, qoff + r0, 0, 0) : 0u;
-    q[u][1] = cin ? __builtin_amdgcn_raw_buffer_load_b32(rq, qoff + r0 + (uint32_t)(a.ldq * 2), 0, 0) : 0u;
+    const uint32_t r0 = (uint32_t)(2 * p) * (uint32_t)(a.ldq * 2) + (uint32_t)(c * 2);
+    q[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, cin ? r0 : kOutOfRange, 0, 0);
+    q[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rq, cin ? r0 + (uint32_t)(a.ldq * 2) : kOutOfRange, 0, 0);
   }
 
-  // Factor slice: rows j < R, columns [mb, mb + RB) of Lt (always inside Mp).
-  for (int idx = tid; idx < CR_PAIRS * R; idx += CR_THREADS) {
-    const int j = idx / CR_PAIRS, p = idx % CR_PAIRS;
-    const int64_t m = mb + 2 * p;
-    uint32_t v = 0;
-    if (j < a.R && m < a.Mp) v = *reinterpret_cast<const uint32_t *>(a.Lt + (int64_t)j * a.Mp + m);
-    lt[p * R + j] = v;
+#pragma unroll
+  for (int i = 0; i < LTN; ++i) {
+    const int idx = tid + i * CR_THREADS, j = idx / CR_PAIRS, p = idx % CR_PAIRS;
+    lt[p * R + j] = (j < a.R && mb + 2 * p < a.Mp) ? ltv[i] : 0u;
   }
   __syncthreads();
 
@@ -409,16 +420,18 @@ __global__ __launch_bounds__(256) void colred_reduce_kernel(ColRedArgs a0, ColRe
   const int64_t j = idx / a.Ncols, col = idx % a.Ncols;
   const int64_t stride = a.R * a.Ncols;
   const float *p = a.part + idx;
+  // Batches of splits loaded with no condition (slots past the last split
+  // re-read it and are discarded), so that each batch waits for memory once.
+  constexpr int BATCH = 16;
   float v = 0.0f;
-  int s = 0;
-  for (; s + 4 <= splits; s += 4) {
-    const float x0 = p[(s + 0) * stride], x1 = p[(s + 1) * stride], x2 = p[(s + 2) * stride], x3 = p[(s + 3) * stride];
-    v += x0;
-    v += x1;
-    v += x2;
-    v += x3;
+  for (int s0 = 0; s0 < splits; s0 += BATCH) {
+    float x[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) x[q] = p[(int64_t)min(s0 + q, splits - 1) * stride];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q)
+      if (s0 + q < splits) v += x[q];
   }
-  for (; s < splits; ++s) v += p[s * stride];
   a.out[a.transpose ? col * a.R + j : idx] = f32_to_bf16(v);
 }
 
