@@ -131,16 +131,41 @@ __device__ __forceinline__ void load_x_chunk(const GemvArgs &a, int64_t k, uint3
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
+// Sum over each group of G consecutive lanes (G = 8, 16, 32 or 64), returned
+// in every lane of the group, with no LDS traffic: DPP within a row of 16
+// lanes (quad swaps, then half-row and row mirrors, which pair lanes holding
+// equal partial sums), then the rows' sums read out with readlane.  (A
+// butterfly of lane shuffles costs one LDS round trip per step, and the
+// decode kernel pays it once per weight row.)
+template <int G>
+__device__ __forceinline__ float group_sum(float t, int lane) {
+  static_assert(G == 8 || G == 16 || G == 32 || G == 64, "group size");
+  t += dpp_f32<0xB1>(t);    // quad: lanes i ^ 1
+  t += dpp_f32<0x4E>(t);    // quad: lanes i ^ 2
+  t += dpp_f32<0x141>(t);   // half-row mirror: quad sums of the two quads of 8
+  if constexpr (G >= 16) t += dpp_f32<0x140>(t);   // row mirror: the two halves of 16
+  if constexpr (G == 32) {
+    const float a = lane_f32(t, 0) + lane_f32(t, 16), b = lane_f32(t, 32) + lane_f32(t, 48);
+    t = lane < 32 ? a : b;
+  }
+  if constexpr (G == 64) t = (lane_f32(t, 0) + lane_f32(t, 16)) + (lane_f32(t, 32) + lane_f32(t, 48));
+  return t;
+}
+
+__device__ __forceinline__ float wave_sum(float v, int lane) { return group_sum<64>(v, lane); }
+
 // Wave sums of MM values at once (MM a power of two <= 8): each exchange step
-// halves the values a lane carries, so MM sums cost MM - 1 + 6 - log2(MM)
-// shuffles instead of 6 MM.  Returns, in every lane, the full sum of value
-// m = lane >> (6 - log2(MM)).
+// halves the values a lane carries (MM - 1 shuffles), and one group sum over
+// the remaining 64 / MM lanes finishes.  Returns, in every lane, the full sum
+// of value m = lane >> (6 - log2(MM)).
 template <int MM>
 __device__ __forceinline__ float wave_sum_multi(float (&v)[MM], int lane) {
   int off = 32;
@@ -158,9 +183,7 @@ __device__ __forceinline__ float wave_sum_multi(float (&v)[MM], int lane) {
       v[i] = keep + __shfl_xor(send, off, 64);
     }
   }
-  float t = v[0];
-  for (; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
-  return t;
+  return group_sum<64 / MM>(v[0], lane);
 }
 
 // Several decode problems in one launch: workgroups [start[g], start[g+1])
@@ -222,7 +245,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, int block, const ui
       }
 #pragma unroll
       for (int m = 0; m < MM; ++m) {
-        const float t = wave_sum(hm[m]);
+        const float t = wave_sum(hm[m], lane);
         if (lane == 0 && m < a.M) a.h_part[((int64_t)hb * a.M + m) * 64 + j] = t;
       }
     }
