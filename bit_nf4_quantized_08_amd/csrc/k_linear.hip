@@ -14,7 +14,7 @@
 //   gemv_kernel           decode path (M <= 8): streams codes at HBM rate,
 //                         expands byte pairs through an LDS table and
 //                         accumulates with v_dot2_f32_bf16; per-block scale
-//                         applied to partial sums.  Its first blocks compute
+//                         applied to partial sums.  Its waves also compute
 //                         the adapter's H partials.
 //   gemv_epilogue_kernel  adds the split partials and the adapter term.
 //   bwd_prep_kernel       B^T for the backward's dH = dY B, and (s H)^T from a
@@ -82,11 +82,10 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t *__re
 // one contiguous read of KW KB of codes (rows of neighbouring waves are
 // neighbours in memory), and the next row is requested before the current one
 // is multiplied.
-// The first h_blocks blocks instead compute H partials,
-// h_part[split][m][j] = sum over the split's K-range of x[m][k] * A[j][k]:
-// block b takes K-range b % hsplits and adapter rows 4 (b / hsplits) .. +3,
-// one per wave, so that every wave makes a single pass and H is spread over
-// many short blocks that start first.
+// After its weight rows a wave computes the adapter's H partials for its
+// K-segment (one adapter row j at a time, against the activations it already
+// holds): h_part[split][m][j] = sum over the segment of x[m][k] * A[j][k].
+// There are no separate H workgroups, so every workgroup slot serves rows.
 // 2048-wide chunks per wave segment (KW): the activations of a segment take
 // 16 * KW * MM registers per lane, at most 64 (128 for MM = 8, KW = 1), and a
 // segment is no longer than the row needs.
@@ -105,31 +104,11 @@ struct GemvArgs {
   const uint16_t *A;  // [r, K]
   int64_t r;
   float *y_part;      // [splits][M][N]
-  float *h_part;      // [hsplits][M][64]
+  float *h_part;      // [splits][M][64]
   int64_t k_per_split;   // KW * 2048: the K-segment of one wave
   int splits;            // K-segments
   int64_t row_waves;     // waves per K-segment; wave v takes rows v, v + row_waves, ...
-  int h_blocks;       // hsplits * ceil(r / 4)
-  int hsplits;
-  int64_t hk_per_split;  // H partial K-range per block (multiple of 2048 or K)
 };
-
-// 32 activations of each row m at column k (k must be in range).  Rows m >= M
-// read row M - 1 instead, so that every load is unconditional; their results
-// are never stored.
-template <int MM>
-__device__ __forceinline__ void load_x_chunk(const GemvArgs &a, int64_t k, uint32_t (&x)[MM][16]) {
-#pragma unroll
-  for (int m = 0; m < MM; ++m) {
-    const int64_t mr = min((int64_t)m, a.M - 1);
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(a.X + mr * a.K + k);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 v = p[c];
-      x[m][4 * c] = v.x; x[m][4 * c + 1] = v.y; x[m][4 * c + 2] = v.z; x[m][4 * c + 3] = v.w;
-    }
-  }
-}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
@@ -217,43 +196,8 @@ template <int MM, bool DQ, int KW>
 __device__ __forceinline__ void gemv_body(const GemvArgs &a, int block, const uint32_t *pairs) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  if (block < a.h_blocks) {
-    // ---- H partials (see above).
-    const int hb = block % a.hsplits;
-    const int64_t kb = (int64_t)hb * a.hk_per_split;
-    const int64_t ke = min(a.K, kb + a.hk_per_split);
-    const int j = 4 * (block / a.hsplits) + wave;
-    if (j < a.r) {
-      float hm[MM];
-#pragma unroll
-      for (int m = 0; m < MM; ++m) hm[m] = 0.0f;
-      for (int64_t k = kb + lane * 32; k < ke; k += 2048) {
-        uint32_t x[MM][16];
-        load_x_chunk<MM>(a, k, x);
-        const u32x4 *pa = reinterpret_cast<const u32x4 *>(a.A + j * a.K + k);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 av = pa[c];
-          const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int m = 0; m < MM; ++m)
-              hm[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
-                                                      __builtin_bit_cast(bf16x2, x[m][4 * c + q]), hm[m], false);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MM; ++m) {
-        const float t = wave_sum(hm[m], lane);
-        if (lane == 0 && m < a.M) a.h_part[((int64_t)hb * a.M + m) * 64 + j] = t;
-      }
-    }
-    return;
-  }
-
   static_assert(KW * MM <= 4 || KW == 1, "activation registers");
-  const int64_t v = (int64_t)(block - a.h_blocks) * (kThreads / 64) + wave;
+  const int64_t v = (int64_t)block * (kThreads / 64) + wave;
   const int split = (int)(v % a.splits);
   const int64_t n_first = v / a.splits;
   if (n_first >= a.row_waves) return;
@@ -375,6 +319,49 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, int block, const ui
     n += a.row_waves;
   }
   if (rows & 1) row_dot(r0, n);
+
+  // The adapter's H partials for this wave's K-segment, h_part[split][m][j] =
+  // sum over the segment of x[m][k] A[j][k], with the activations already in
+  // registers (zero past the segment's end).  Adapter row j goes to the wave
+  // with n_first = (N mod W + j) mod W (W = row_waves), so the first adapter
+  // rows go to the waves with one weight row fewer.  The loads of A's row
+  // carry no condition: past the segment's end (or of A) they re-read the
+  // segment's first chunk, and the zero activations cancel them.
+  const int64_t W = a.row_waves;
+  int64_t j = n_first - a.N % W;
+  if (j < 0) j += W;
+  for (; j < a.r; j += W) {
+    float hm[MM];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) hm[m] = 0.0f;
+    u32x4 av[KW][4];
+#pragma unroll
+    for (int c = 0; c < KW; ++c) {
+      const int64_t k = kb + c * 2048 + lane * 32;
+      const u32x4 *pa = reinterpret_cast<const u32x4 *>(a.A + j * a.K + (k < ke ? k : kb + lane * 32));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) av[c][q] = pa[q];
+    }
+#pragma unroll
+    for (int c = 0; c < KW; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t aw[4] = {av[c][q].x, av[c][q].y, av[c][q].z, av[c][q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int m = 0; m < MM; ++m)
+            hm[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[e]),
+                                                    __builtin_bit_cast(bf16x2, x[c][m][4 * q + e]), hm[m], false);
+      }
+    constexpr int kLog2MM = MM == 1 ? 0 : (MM == 2 ? 1 : (MM == 4 ? 2 : 3));
+    float hs[MM];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) hs[m] = hm[m];
+    const float t = wave_sum_multi<MM>(hs, lane);
+    const int m = lane >> (6 - kLog2MM);
+    if ((lane & ((64 >> kLog2MM) - 1)) == 0 && m < a.M) a.h_part[((int64_t)split * a.M + m) * 64 + j] = t;
+  }
 }
 
 // y[m][n] = sum_s y_part[s][m][n] + s_lora * sum_j H[m][j] * B[n][j], H summed
@@ -526,10 +513,6 @@ constexpr int64_t GEMV_MAX_M = 8;
 struct GemvPlan {
   int splits;          // K-segments of gemv_kw(mm) chunks
   int64_t kps;         // K per segment
-  int64_t row_waves;   // waves per segment
-  int row_wgs;         // workgroups for the rows
-  int hsplits;         // K-ranges of the H partials
-  int64_t hkps;
 };
 
 int gemv_mm(int64_t M) { return M == 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
@@ -540,10 +523,6 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t kw = gemv_kw(gemv_mm(M), chunks);
   p.kps = kw * 2048;
   p.splits = (int)cdiv(chunks, kw);
-  p.row_waves = 0;
-  p.row_wgs = 0;
-  p.hkps = 2048 * cdiv(chunks, std::min<int64_t>(chunks, 64));
-  p.hsplits = (int)cdiv(K, p.hkps);
   return p;
 }
 
@@ -577,14 +556,6 @@ int gemv_resident(const void *fn) {
   return nb;
 }
 
-// Rows are dealt to as many waves as fit on the GPU at once (each wave then
-// walks its rows to the end with no second round of workgroups), but to no
-// more than half the rows, so that every wave has a next row to prefetch.
-void gemv_rows(GemvPlan &p, int64_t N, const void *fn) {
-  const int64_t waves = (int64_t)gemv_resident(fn) * num_cus() * (kThreads / 64);
-  p.row_waves = std::min<int64_t>(cdiv(N, 2), std::max<int64_t>(1, waves / p.splits));
-  p.row_wgs = (int)cdiv(p.row_waves * p.splits, kThreads / 64);
-}
 
 #define QN_TRY(x)                      \
   do {                                 \
@@ -600,7 +571,7 @@ size_t fwd_workspace(int64_t M, int64_t N, int64_t K, int64_t r) {
   if (M <= GEMV_MAX_M) {
     const GemvPlan p = gemv_plan(M, N, K);
     c.take<float>((int64_t)p.splits * M * N);
-    c.take<float>((int64_t)p.hsplits * M * 64);
+    c.take<float>((int64_t)p.splits * M * 64);
   } else {
     c.take<uint16_t>(M * align_up(r, 8));
     c.take<char>((int64_t)lowrank_part_bytes(M, K, r));
@@ -643,21 +614,40 @@ static DecodePlan decode_plan(const FwdArgs &a) {
   GemvPlan p = gemv_plan(a.M, a.N, a.K);
   const int64_t kw = p.kps / 2048;
   d.fn = a.sc.absmax_q ? gemv_fn<true>(a.M, kw) : gemv_fn<false>(a.M, kw);
-  gemv_rows(p, a.N, d.fn);
   float *y_part = c.take<float>((int64_t)p.splits * a.M * a.N);
-  float *h_part = c.take<float>((int64_t)p.hsplits * a.M * 64);
-  const int h_blocks = p.hsplits * (int)cdiv(a.r, 4);
-  d.ga = GemvArgs{a.X, a.M, a.N, a.K, a.codes, a.sc, a.A, a.r, y_part, h_part, p.kps, p.splits, p.row_waves,
-                  h_blocks, p.hsplits, p.hkps};
-  d.ea = EpiArgs{y_part, p.splits, h_part, p.hsplits, a.M, a.N, a.r, a.B, a.s, a.Y, a.H_out};
-  d.blocks = h_blocks + p.row_wgs;
+  float *h_part = c.take<float>((int64_t)p.splits * a.M * 64);
+  d.ga = GemvArgs{a.X, a.M, a.N, a.K, a.codes, a.sc, a.A, a.r, y_part, h_part, p.kps, p.splits, 0};
+  d.ea = EpiArgs{y_part, p.splits, h_part, p.splits, a.M, a.N, a.r, a.B, a.s, a.Y, a.H_out};
+  d.blocks = 0;   // set by share_row_waves
   d.qtype = a.sc.qtype;
   return d;
 }
 
+// Row waves of the problems of one decode launch.  Every wave walks its rows
+// to the end, so the row workgroups are sized to what fits on the GPU at once
+// (a workgroup that waits for a free slot finishes late by the whole wait),
+// and those waves are shared among the problems in proportion to their
+// weights' bytes, so that the problems run side by side and end together.
+// Which wave computes a row does not change the row's arithmetic.
+static void share_row_waves(DecodePlan *d, int n) {
+  const int64_t slots = (int64_t)gemv_resident(d[0].fn) * num_cus();
+  double bytes = 0.0;
+  for (int i = 0; i < n; ++i) bytes += (double)d[i].ga.N * (double)d[i].ga.K;
+  const int64_t waves = slots * (kThreads / 64);
+  for (int i = 0; i < n; ++i) {
+    GemvArgs &ga = d[i].ga;
+    const int64_t share = (int64_t)((double)waves * ((double)ga.N * (double)ga.K / bytes));
+    ga.row_waves = std::min<int64_t>(cdiv(ga.N, 2), std::max<int64_t>(1, share / ga.splits));
+    d[i].blocks = (int)cdiv(ga.row_waves * ga.splits, kThreads / 64);
+  }
+}
+
 // One streaming launch and one epilogue launch over n decode problems that
 // share the kernel instance and the 4-bit type.
-static hipError_t launch_decode(const DecodePlan *d, int n, hipStream_t st) {
+static hipError_t launch_decode(const DecodePlan *dp, int n, hipStream_t st) {
+  DecodePlan d[QN_MAX_GROUP];
+  for (int i = 0; i < n; ++i) d[i] = dp[i];
+  share_row_waves(d, n);
   GemvGroup gg{};
   EpiGroup eg{};
   int64_t gb = 0, eb = 0;
