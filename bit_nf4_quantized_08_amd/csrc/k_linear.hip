@@ -88,9 +88,10 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t *__re
 // There are no separate H workgroups, so every workgroup slot serves rows.
 // 2048-wide chunks per wave segment (KW): the activations of a segment take
 // 16 * KW * MM registers per lane, at most 64 (128 for MM = 8, KW = 1), and a
-// segment is no longer than the row needs.
+// segment is no longer than the row needs.  Two chunks at most, so that three
+// rows' registers fit beside them at three or more waves per SIMD.
 int gemv_kw(int mm, int64_t chunks) {
-  const int cap = mm == 1 ? 4 : (mm == 2 ? 2 : 1);
+  const int cap = mm <= 2 ? 2 : 1;
   int kw = 1;
   while (kw < cap && kw < chunks) kw *= 2;
   return kw;
@@ -301,24 +302,31 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, int block, const ui
     if ((lane & ((64 >> kLog2MM) - 1)) == 0 && m < a.M) a.y_part[((int64_t)split * a.M + m) * a.N + n] = t;
   };
 
-  // Rows in pairs with two register sets (no copies between them, so that
-  // a set's loads stay in flight while the other set is multiplied), then
-  // the odd row out.  (Two rows ahead costs occupancy and was slower.)
+  // Rows in threes with three register sets (no copies between them): two
+  // rows' loads stay in flight while the third is multiplied.
   const int64_t rows = cdiv_d(a.N - n_first, a.row_waves);
-  Row r0, r1;
+  const int64_t rw = a.row_waves;
+  Row r0, r1, r2;
   load_row(r0, n_first);
+  load_row(r1, n_first + rw);
   int64_t n = n_first;
-  for (int64_t t = 0; t + 2 <= rows; t += 2) {
+  int64_t t = 0;
+  for (; t + 3 <= rows; t += 3) {
     __builtin_amdgcn_sched_barrier(0);
-    load_row(r1, n + a.row_waves);
+    load_row(r2, n + 2 * rw);
     row_dot(r0, n);
-    n += a.row_waves;
+    n += rw;
     __builtin_amdgcn_sched_barrier(0);
-    load_row(r0, n + a.row_waves);
+    load_row(r0, n + 2 * rw);
     row_dot(r1, n);
-    n += a.row_waves;
+    n += rw;
+    __builtin_amdgcn_sched_barrier(0);
+    load_row(r1, n + 2 * rw);
+    row_dot(r2, n);
+    n += rw;
   }
-  if (rows & 1) row_dot(r0, n);
+  if (t < rows) row_dot(r0, n);
+  if (t + 1 < rows) row_dot(r1, n + rw);
 
   // The adapter's H partials for this wave's K-segment, h_part[split][m][j] =
   // sum over the segment of x[m][k] A[j][k], with the activations already in
@@ -532,8 +540,7 @@ template <bool DQ>
 const void *gemv_fn(int64_t M, int64_t kw) {
   switch (gemv_mm(M)) {
     case 1:
-      return kw == 4 ? reinterpret_cast<const void *>(&gemv_kernel<1, DQ, 4>)
-           : kw == 2 ? reinterpret_cast<const void *>(&gemv_kernel<1, DQ, 2>)
+      return kw == 2 ? reinterpret_cast<const void *>(&gemv_kernel<1, DQ, 2>)
                      : reinterpret_cast<const void *>(&gemv_kernel<1, DQ, 1>);
     case 2:
       return kw == 2 ? reinterpret_cast<const void *>(&gemv_kernel<2, DQ, 2>)
