@@ -424,7 +424,7 @@ def main():
                      "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4), "traffic": traffic("gemv_70b", "gemv"),
                      "launches": len(gemv), "avg_ms": round(sum(gemv) / len(gemv), 5),
                      "note": "the streaming kernel alone (its epilogue launch excluded); bytes = NF4 weights + "
-                             "x + y + A read by the H blocks"}
+                             "x + y + A (read for the H partials)"}
     lowr = kern.get("lowrank", [])
     lowrank_roof = None
     if lowr:
