@@ -41,8 +41,10 @@
 //      patch (4 rows, 8 columns), and the patch is written transposed.
 // The activation stages are XOR-swizzled in 16-byte chunks and the forward
 // weight stage has a padded row pitch, so that fragment reads and stage writes
-// are free of bank conflicts; the dX weight stage keeps an XOR layout for its
-// transposed 8-byte writes (see wswz, kswz and the activation-stage comment
+// are free of bank conflicts; the dX weight stage permutes its output columns
+// over stage rows and XORs positions per group of 16 rows, so that its
+// transposed 8-byte writes spread over the banks while the fragment reads stay
+// conflict-free (see wswz, kswz, kn_row and the activation-stage comment
 // below).
 
 #include <algorithm>
@@ -116,10 +118,23 @@ __device__ __forceinline__ void tile_coords(int h, int tiles_m, int tiles_n, int
 // groups, and eight consecutive columns written at one position on 8 distinct
 // groups of the 32: the forward (row-major weight) stages store position k at
 // k, with no XOR (wswz<false>).  The transposed producer of dX writes 8-byte
-// column patches; its stage keeps position k at k ^ kswz(col) (the XOR moves
-// whole 8-element chunks), which separates columns c and c + 16 written in the
-// same cycle; its MMA reads pay about 4 conflict cycles per instruction.
-__device__ __forceinline__ int kswz(int col) { return 32 * (((col >> 3) ^ (col >> 4)) & 1) + 8 * ((col >> 5) & 3); }
+// column patches, the four lanes of a quad to output columns 8 apart at the
+// same positions, and 8-byte writes are served 16 lanes per cycle over 32
+// banks: with the pitch alone those four columns fall on the same banks.  So
+// dX stores output column n in stage row kn_row(n), which puts the four
+// columns of a write cycle into four different aligned groups of 16 rows, and
+// keeps position k of stage row s at k ^ kswz(s), kswz = 16 * (group of 16 rows
+// mod 4): the writes of a cycle fall on four disjoint spans of 8 banks, while
+// the MMA reads (16 consecutive stage rows at one position) see one XOR per
+// read and stay conflict-free.  kn_row keeps 8-column chunks whole, so the
+// output is still stored in 16-byte row chunks (output column kn_col(s)).
+__device__ __forceinline__ int kswz(int row) { return 16 * ((row >> 4) & 3); }
+__device__ __forceinline__ int kn_row(int n) {
+  return 64 * (n >> 6) + 16 * ((n >> 3) & 3) + 8 * ((n >> 5) & 1) + (n & 7);
+}
+__device__ __forceinline__ int kn_col(int row) {
+  return 64 * (row >> 6) + 32 * ((row >> 3) & 1) + 8 * ((row >> 4) & 3) + (row & 7);
+}
 template <bool KN>
 __device__ __forceinline__ int wswz(int col) { return KN ? kswz(col) : 0; }
 
@@ -181,7 +196,7 @@ struct Producer {
       qvoff = in ? 0u : kOutOfRange;
       if constexpr (DQ) rq = make_rsrc(a.absmax_q, a.Kc * a.Nout / 64);
       else rq = make_rsrc(a.absmax, a.Kc * a.Nout / 64 * 4);
-      wr_col = cb + 8 * j;
+      wr_col = kn_row(cb + 8 * j);   // stage row of output column cb + 8j (+c for c < 8)
       wr_k = 4 * (q & 15);
     }
     if constexpr (DQ) rs = make_rsrc(a.scale2, (a.Nout * a.Kc / 64 + 255) / 256 * 4);
@@ -340,7 +355,7 @@ __device__ __forceinline__ void load_adapter_right(const QGemmArgs &a, int64_t n
 // the loads falls at the end of the main loop.
 template <bool KN>
 __device__ __forceinline__ void store_adapter_right(const uint32_t (&h)[32], uint16_t *Rs, int t) {
-  const int row = t & (BN - 1), j0 = 32 * (t >> 7);
+  const int row = KN ? kn_row(t & (BN - 1)) : (t & (BN - 1)), j0 = 32 * (t >> 7);
   uint32_t v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = (h[2 * i] & 0xFFFFu) | (h[2 * i + 1] << 16);
@@ -549,19 +564,23 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
   // Activation stages are filled by the producer waves (see there); this
   // wave only reads them, after the barrier that follows their loads.
   // Fragment offsets: A (activations) tile i, slice c: row 32i + lr, chunk 4lh + c;
-  // B (weights) column 32j + lr, positions 32lh + 8c .. +7, stored there (forward) or at
-  // 32(lh ^ g) + 8(c ^ j), g = bit 3 ^ bit 4 of lr (dX: the kswz layout).
+  // B (weights) stage row 32j + lr, positions 32lh + 8c .. +7, stored there (forward) or
+  // at (32lh + 8c) ^ kswz(32j + lr) (dX).
   uint32_t aoff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) aoff[c] = (uint32_t)(wave_u * XW + lr * BK + (((4 * lh + c) ^ ((lr >> 1) & 7)) * 8));
-  const int rb = lr * LD + 32 * (lh ^ (KN ? (((lr >> 3) ^ (lr >> 4)) & 1) : 0));
+  const int rb = lr * LD + (KN ? 0 : 32 * lh);
+  int bpos[TN];   // dX: position base of tile j, before the slice's 8c
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bpos[j] = KN ? ((32 * lh) ^ kswz(32 * j + lr)) : 0;
   struct Frag {
     bf16x8 a[TM];
     bf16x8 b[TN];
   };
   auto read_b = [&](bf16x8 *b, const uint16_t *wc, int c) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * (KN ? (c ^ j) : c)]);
+    for (int j = 0; j < TN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + (KN ? (bpos[j] ^ (8 * c)) : 8 * c)]);
   };
   auto read_f = [&](Frag &f, const uint16_t *xc, const uint16_t *wc, int c) {
 #pragma unroll
@@ -662,7 +681,7 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
     for (int q = 0; q < 8; ++q) {
       const int row = 4 * q + (lane >> 4), c8 = 8 * (lane & 15);
       const u32x4 v = *reinterpret_cast<const u32x4 *>(&blk[row * kOutPitch + c8]);
-      const int64_t lrow = (int64_t)wave_u * WM + i * 32 + row, gn = n0 + c8;
+      const int64_t lrow = (int64_t)wave_u * WM + i * 32 + row, gn = n0 + (KN ? kn_col(c8) : c8);
       if (vec_ok && gn + 8 <= a.Nout) {
         __builtin_amdgcn_raw_buffer_store_b128(v, rout, (uint32_t)((lrow * a.ldo + gn) * 2), 0, 0);
       } else if (m0 + lrow < a.M) {
