@@ -49,6 +49,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "qn_device.h"
 #include "qn_internal.h"
@@ -151,7 +152,7 @@ __device__ __forceinline__ uint32_t qperm(uint32_t v) {
 // one block), then the four lanes of a quad transpose their 4-byte words so
 // that lane j holds columns 32*(q>>4) + 8j .. +7 of all four rows: each column
 // then has 4 consecutive contraction positions, written as one 8-byte store.
-template <bool KN, bool DQ>
+template <bool KN, bool DQ, bool Q4 = false>
 struct Producer {
   struct Set {
     uint32_t code[4];
@@ -208,7 +209,9 @@ struct Producer {
     t.code[0] = c4.x; t.code[1] = c4.y; t.code[2] = c4.z; t.code[3] = c4.w;
     const int64_t b = blk_base + (int64_t)s * blk_step;
     if constexpr (!KN) {
-      if constexpr (DQ) {
+      if constexpr (Q4) {
+        (void)b;   // the scales come from Scale4
+      } else if constexpr (DQ) {
         t.q = __builtin_amdgcn_raw_buffer_load_b8(rq, qvoff, s, 0);
         t.st = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
             rs, qvoff == kOutOfRange ? kOutOfRange : (uint32_t)((b >> 8) * 4), 0, 0));
@@ -237,8 +240,13 @@ struct Producer {
   template <typename Hook>
   __device__ __forceinline__ void store(const Set &t, uint16_t *Rs, const float2 *pair, const float *cv,
                                         int lane, Hook &&hook) const {
+    store_scaled(t, scale(t), Rs, pair, cv, lane, hook);
+  }
+  // The same with the block scale A given.
+  template <typename Hook>
+  __device__ __forceinline__ void store_scaled(const Set &t, float A, uint16_t *Rs, const float2 *pair,
+                                               const float *cv, int lane, Hook &&hook) const {
     const int copy = lane & (kPairCopies - 1);
-    const float A = scale(t);
     if constexpr (!KN) {
       // All 32 codes share one block scale: build the block's sixteen bf16
       // products bf16(fl32(c[q] * A)) once, split into a low-byte and a
@@ -329,6 +337,40 @@ struct Producer {
         *reinterpret_cast<u32x2 *>(&Rs[(wr_col + c) * LD + k]) =
             u32x2{pack_bf16x2(v[0][c], v[1][c]), pack_bf16x2(v[2][c], v[3][c])};
     }
+  }
+};
+
+// Double-quantised block scales of row-major weights four steps at a time,
+// for rows of a multiple of four blocks (K % 256 == 0): blocks 4k .. 4k + 3 of
+// a row are then one aligned dword of absmax_q and fall in one group of 256
+// (a row starts at a multiple of four blocks, a group at a multiple of 256),
+// so a thread loads one dword and one group scale per four steps instead of a
+// byte and a scale per step (each of those loads touches a cache line per row
+// of the tile).  Row mapping as the row-major producer's.  `nxt` holds dword
+// k + 1 while `cur` holds dword k.
+struct Scale4 {
+  rsrc_t rq, rs;
+  uint32_t qoff;
+  int64_t b0;   // first block of the thread's row
+  uint32_t cur, nxt;
+  float cur_s, nxt_s;
+
+  __device__ void init(const QGemmArgs &a, int tid, int64_t n0) {
+    const int row = ((tid >> 5) << 4) | (tid & 15);
+    const int64_t nbr = a.Kc / 64;
+    rq = make_rsrc(a.absmax_q + n0 * nbr, (a.Nout - n0) * nbr);
+    rs = make_rsrc(a.scale2, (a.Nout * nbr + 255) / 256 * 4);
+    qoff = n0 + row < a.Nout ? (uint32_t)(row * nbr) : kOutOfRange;
+    b0 = (n0 + row) * nbr;
+  }
+  // Loads dword k (wave-uniform) into nxt.
+  __device__ __forceinline__ void issue(int k) {
+    nxt = __builtin_amdgcn_raw_buffer_load_b32(rq, qoff, 4 * k, 0);
+    nxt_s = as_f32(__builtin_amdgcn_raw_buffer_load_b32(
+        rs, qoff == kOutOfRange ? kOutOfRange : (uint32_t)(((b0 + 4 * k) >> 8) * 4), 0, 0));
+  }
+  __device__ __forceinline__ static float scale(uint32_t w, float st, int byte) {
+    return (float)((w >> (8 * byte)) & 0xFFu) * st;
   }
 };
 
@@ -722,7 +764,7 @@ constexpr int BM2 = 256, BN2 = 256;
 constexpr int R_TILE2 = BN2 * LD;
 constexpr int XSTAGE2 = BM2 * BK;
 
-template <bool DQ>
+template <bool DQ, bool Q4>
 __global__ __launch_bounds__(kThreads2, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   int gi = 0;
@@ -778,9 +820,11 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   };
 
   // ---- weight stages: the producer of the tiling above, over 256 rows.
-  Producer<false, DQ> P;
+  Producer<false, DQ, Q4> P;
   P.init(a, tid, n0);
-  typename Producer<false, DQ>::Set s0, s1;
+  typename Producer<false, DQ, Q4>::Set s0, s1;
+  Scale4 q4;
+  if constexpr (Q4) q4.init(a, tid, n0);
 
   // ---- fragments
   const int lr = lane & 31, lh = lane >> 5;
@@ -812,12 +856,15 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
       for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
-  // ---- prologue: code sets of steps 0 and 1, activation stage 0, weight stage 0.
-  constexpr int kReload = DQ ? 3 : 2;
+  // ---- prologue: code sets of steps 0 and 1, activation stage 0, weight stage 0
+  // (with Scale4: its dword 0 first, in nxt).
+  constexpr int kReload = Q4 ? 1 : (DQ ? 3 : 2);   // loads per code-set reload
+  if constexpr (Q4) q4.issue(0);
   P.issue(s0, 0);
   issue_x(xs0, 0);
   P.issue(s1, __builtin_amdgcn_readfirstlane(min(1, last)));
-  P.store(s0, ws0, nullptr, cb.v, lane, [&](int) {});
+  if constexpr (Q4) P.store_scaled(s0, Scale4::scale(q4.nxt, q4.nxt_s, 0), ws0, nullptr, cb.v, lane, [&](int) {});
+  else P.store(s0, ws0, nullptr, cb.v, lane, [&](int) {});
   P.issue(s0, __builtin_amdgcn_readfirstlane(min(2, last)));
   __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kReload));
   lds_barrier();
@@ -834,18 +881,31 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   // every step together, so they cannot cover for each other).
   const uint16_t *wrow = nullptr;
   (void)wrow;
+  // With Scale4 the loop runs four steps per iteration (nsteps is then a
+  // multiple of 4): step 4k + p writes the stage of block 4k + p + 1, whose
+  // scale is byte p + 1 of dword k (cur) for p < 3 and byte 0 of dword k + 1
+  // (nxt, loaded at step 4k) for p = 3.
   const int wcol = P.wr_col, wk = P.wr_k;
   const int wsw = wswz<false>(wcol);
-  auto step = [&](int s, const uint16_t *xc, const uint16_t *wc, uint16_t *xn, uint16_t *wn,
-                  typename Producer<false, DQ>::Set &set) {
+  const int last4 = last >> 2;
+  auto step = [&](auto phase, int s, const uint16_t *xc, const uint16_t *wc, uint16_t *xn, uint16_t *wn,
+                  typename Producer<false, DQ, Q4>::Set &set) {
+    constexpr int ph = decltype(phase)::value;
     issue_x(xn, s + 1);
+    if constexpr (Q4 && ph == 0) {
+      q4.cur = q4.nxt;
+      q4.cur_s = q4.nxt_s;
+      q4.issue(__builtin_amdgcn_readfirstlane(min((s >> 2) + 1, last4)));
+    }
     Frag f0, f1;
     read_f(f0, xc, wc, 0);
     read_f(f1, xc, wc, 1);
     uint32_t LO[4], HI[4];
     // slice 0 + the block's products
     {
-      const float A = P.scale(set);
+      float A;
+      if constexpr (Q4) A = ph == 3 ? Scale4::scale(q4.nxt, q4.nxt_s, 0) : Scale4::scale(q4.cur, q4.cur_s, ph + 1);
+      else A = P.scale(set);
       uint32_t Pp[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) Pp[k] = pack_bf16x2(cb.v[2 * k] * A, cb.v[2 * k + 1] * A);
@@ -921,14 +981,27 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
     __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload));
     lds_barrier();
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   int s = 0;
-  for (; s + 2 <= nsteps; s += 2) {
-    step(s, xs0, ws0, xs1, ws1, s1);
-    step(s + 1, xs1, ws1, xs0, ws0, s0);
-  }
-  if (s < nsteps) {
-    step(s, xs0, ws0, xs1, ws1, s1);
-    ++s;
+  if constexpr (Q4) {
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    for (; s + 4 <= nsteps; s += 4) {
+      step(P0{}, s, xs0, ws0, xs1, ws1, s1);
+      step(P1{}, s + 1, xs1, ws1, xs0, ws0, s0);
+      step(P2{}, s + 2, xs0, ws0, xs1, ws1, s1);
+      step(P3{}, s + 3, xs1, ws1, xs0, ws0, s0);
+    }
+  } else {
+    for (; s + 2 <= nsteps; s += 2) {
+      step(P0{}, s, xs0, ws0, xs1, ws1, s1);
+      step(P1{}, s + 1, xs1, ws1, xs0, ws0, s0);
+    }
+    if (s < nsteps) {
+      step(P0{}, s, xs0, ws0, xs1, ws1, s1);
+      ++s;
+    }
   }
   // ---- adapter step: left operand in activation stage nsteps & 1 (loaded by
   // the last step); right operand B (zero beyond r) into weight stage nsteps & 1.
@@ -1373,8 +1446,11 @@ hipError_t launch_tiling(const QGemmArgs *in, int n, bool wide, int wide_kind, h
       return hipGetLastError();
     }
     if (wide) {
-      if (dq) hipLaunchKernelGGL((qgemm2_kernel<true>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
-      else hipLaunchKernelGGL((qgemm2_kernel<false>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      bool q4 = dq;   // Scale4 needs rows of a multiple of four blocks
+      for (int k = 0; k < n; ++k) q4 = q4 && in[k].Kc % 256 == 0;
+      if (q4) hipLaunchKernelGGL((qgemm2_kernel<true, true>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      else if (dq) hipLaunchKernelGGL((qgemm2_kernel<true, false>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      else hipLaunchKernelGGL((qgemm2_kernel<false, false>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
       return hipGetLastError();
     }
   }
