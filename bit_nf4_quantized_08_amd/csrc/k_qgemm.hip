@@ -430,7 +430,7 @@ __device__ __forceinline__ void lds_barrier() {
 // Exactly one workgroup (2 waves per SIMD) fits a CU, so tell the compiler
 // that higher occupancy is not reachable: it may then keep a whole step's
 // operands in registers instead of re-reading them one by one.
-template <bool KN, bool DQ, bool EPI_NK>
+template <bool KN, bool DQ, bool EPI_NK, bool Q4>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qgemm_kernel(QGemmGroup grp, Code16 cb) {
   // The problem this workgroup belongs to (a grouped launch runs several
@@ -470,9 +470,11 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
 
   if (producer) {
     const int tid = threadIdx.x - kProducers;
-    Producer<KN, DQ> P;
+    Producer<KN, DQ, Q4> P;
     P.init(a, tid, n0);
-    typename Producer<KN, DQ>::Set s0, s1;
+    typename Producer<KN, DQ, Q4>::Set s0, s1;
+    Scale4 q4;
+    if constexpr (Q4) q4.init(a, tid, n0);
     const int nsteps = __builtin_amdgcn_readfirstlane((int)steps), last = nsteps - 1;   // nsteps >= 1
     const int ntotal = nsteps + 1;   // contraction steps including the adapter step
 
@@ -538,6 +540,7 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
     uint32_t adapter[32];
     load_adapter_right<EPI_NK>(a, n0, tid, adapter);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (Q4) q4.issue(0);   // Scale4 dword 0, in nxt
     P.issue(s0, 0);
     __builtin_amdgcn_sched_barrier(0);
     {
@@ -560,13 +563,31 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
     // load instead of dequantising.
     // A half-step's reload is the code set plus its block scale: the
     // quantised scale and the group step, or one fp32 scale.
-    constexpr int kReload = DQ ? 3 : 2;
-    auto half = [&](int t, typename Producer<KN, DQ>::Set &set, uint16_t *wdst) {   // t < nsteps
-      P.store(set, wdst, pair, cb.v, lane, [&](int q) { issue_x(t + 1, q); });
+    // With Scale4 (a code set reload is then the code load alone) the loop
+    // runs four half-steps per iteration (nsteps is a multiple of 4): half-step
+    // 4k + p takes byte p of dword k, and half-step 4k first moves dword k from
+    // nxt to cur and loads dword k + 1 (two more loads before its stage t + 1,
+    // counted in its wait).
+    constexpr int kReload = Q4 ? 1 : (DQ ? 3 : 2);
+    const int last4 = last >> 2;
+    auto half = [&](auto phase, int t, typename Producer<KN, DQ, Q4>::Set &set, uint16_t *wdst) {   // t < nsteps
+      constexpr int ph = decltype(phase)::value;
+      constexpr int kScale = Q4 && ph == 0 ? 2 : 0;
+      if constexpr (kScale) {
+        q4.cur = q4.nxt;
+        q4.cur_s = q4.nxt_s;
+        q4.issue(__builtin_amdgcn_readfirstlane(min((t >> 2) + 1, last4)));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (Q4)
+        P.store_scaled(set, Scale4::scale(q4.cur, q4.cur_s, ph), wdst, pair, cb.v, lane,
+                       [&](int q) { issue_x(t + 1, q); });
+      else
+        P.store(set, wdst, pair, cb.v, lane, [&](int q) { issue_x(t + 1, q); });
       __builtin_amdgcn_sched_barrier(0);
       P.issue(set, min(t + 2, last));
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload + 8 + kReload));
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload + 8 + kScale + kReload));
       lds_barrier();
     };
     // Weight half-steps in pairs, then the odd one out.  Neither an exit from
@@ -574,14 +595,27 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
     // load: the compiler gives such control flow a path that skips the loads
     // (or leaves the loop body early), and its wait counts then assume that
     // path and wait for loads that are still a half-step early.
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
     int t = 0;
-    for (; t + 2 <= nsteps; t += 2) {
-      half(t, s0, ws0);
-      half(t + 1, s1, ws1);
-    }
-    if (t < nsteps) {
-      half(t, s0, ws0);
-      ++t;
+    if constexpr (Q4) {
+      using P2 = std::integral_constant<int, 2>;
+      using P3 = std::integral_constant<int, 3>;
+      for (; t + 4 <= nsteps; t += 4) {
+        half(P0{}, t, s0, ws0);
+        half(P1{}, t + 1, s1, ws1);
+        half(P2{}, t + 2, s0, ws0);
+        half(P3{}, t + 3, s1, ws1);
+      }
+    } else {
+      for (; t + 2 <= nsteps; t += 2) {
+        half(P0{}, t, s0, ws0);
+        half(P1{}, t + 1, s1, ws1);
+      }
+      if (t < nsteps) {
+        half(P0{}, t, s0, ws0);
+        ++t;
+      }
     }
     // Half-step nsteps: the adapter's right operand; its left operand is
     // activation stage nsteps, issued in the last weight half-step.
@@ -1454,10 +1488,14 @@ hipError_t launch_tiling(const QGemmArgs *in, int n, bool wide, int wide_kind, h
       return hipGetLastError();
     }
   }
-  if (dq)
-    hipLaunchKernelGGL((qgemm_kernel<KN, true, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16(in[0].qtype));
+  bool q4 = !KN && dq;   // Scale4 needs row-major weights with rows of a multiple of four blocks
+  for (int k = 0; k < n; ++k) q4 = q4 && in[k].Kc % 256 == 0;
+  if (q4)
+    hipLaunchKernelGGL((qgemm_kernel<KN, true, EPI_NK, !KN>), grid, dim3(kThreads), 0, st, grp, code16(in[0].qtype));
+  else if (dq)
+    hipLaunchKernelGGL((qgemm_kernel<KN, true, EPI_NK, false>), grid, dim3(kThreads), 0, st, grp, code16(in[0].qtype));
   else
-    hipLaunchKernelGGL((qgemm_kernel<KN, false, EPI_NK>), grid, dim3(kThreads), 0, st, grp, code16(in[0].qtype));
+    hipLaunchKernelGGL((qgemm_kernel<KN, false, EPI_NK, false>), grid, dim3(kThreads), 0, st, grp, code16(in[0].qtype));
   return hipGetLastError();
 }
 
