@@ -798,9 +798,10 @@ constexpr int BM2 = 256, BN2 = 256;
 constexpr int R_TILE2 = BN2 * LD;
 constexpr int XSTAGE2 = BM2 * BK;
 
-template <bool DQ, bool Q4>
+template <bool DQ, bool Q4, bool KN>
 __global__ __launch_bounds__(kThreads2, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
+  static_assert(!(KN && Q4), "four-step scales are for row-major weights");
   int gi = 0;
 #pragma unroll
   for (int i = 1; i < QN_MAX_GROUP; ++i) gi += (i < grp.n && (int)blockIdx.x >= grp.start[i]) ? 1 : 0;
@@ -813,6 +814,15 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   __shared__ __attribute__((aligned(16))) uint16_t xs1[XSTAGE2];
   __shared__ __attribute__((aligned(16))) uint16_t ws0[R_TILE2];
   __shared__ __attribute__((aligned(16))) uint16_t ws1[R_TILE2];
+  // Byte -> (row lo, row hi) table of the transposed-weight expansion (dX).
+  __shared__ __attribute__((aligned(16))) float2 pair[KN ? 256 * kPairCopies : 1];
+  if constexpr (KN) {
+    for (int i = threadIdx.x; i < 256 * kPairCopies; i += kThreads2) {
+      const int e = i / kPairCopies;
+      pair[i] = make_float2(cb.v[e & 15], cb.v[e >> 4]);
+    }
+    lds_barrier();
+  }
 
   int tm, tn;
   tile_coords(tile, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
@@ -854,9 +864,9 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   };
 
   // ---- weight stages: the producer of the tiling above, over 256 rows.
-  Producer<false, DQ, Q4> P;
+  Producer<KN, DQ, Q4> P;
   P.init(a, tid, n0);
-  typename Producer<false, DQ, Q4>::Set s0, s1;
+  typename Producer<KN, DQ, Q4>::Set s0, s1;
   Scale4 q4;
   if constexpr (Q4) q4.init(a, tid, n0);
 
@@ -865,7 +875,13 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   uint32_t aoff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) aoff[c] = (uint32_t)(rg * XW + lr * BK + (((4 * lh + c) ^ ((lr >> 1) & 7)) * 8));
-  const int rb = (128 * cg + lr) * LD + 32 * lh;
+  // Weights: stage row 128 cg + 32 j + lr, positions 32 lh + 8 c .. +7, stored
+  // there (row-major) or at (32 lh + 8 c) ^ kswz(32 j + lr) (dX: kswz depends
+  // on bits 4 and 5 of the stage row only).
+  const int rb = (128 * cg + lr) * LD + (KN ? 0 : 32 * lh);
+  int bpos[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bpos[j] = KN ? ((32 * lh) ^ kswz(32 * j + lr)) : 0;
   struct Frag {
     bf16x8 a[TM];
     bf16x8 b[TN];
@@ -874,7 +890,8 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(&xc[aoff[c] + i * 32 * BK]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + 8 * c]);
+    for (int j = 0; j < TN; ++j)
+      f.b[j] = *reinterpret_cast<const bf16x8 *>(&wc[rb + j * 32 * LD + (KN ? (bpos[j] ^ (8 * c)) : 8 * c)]);
   };
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -892,13 +909,21 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
 
   // ---- prologue: code sets of steps 0 and 1, activation stage 0, weight stage 0
   // (with Scale4: its dword 0 first, in nxt).
+  // The scheduling fences keep the loads in this order, which the wait before
+  // the barrier counts on: only the two code-set reloads issued after stage 0
+  // may still be in flight there (unfenced, the compiler had moved the second
+  // reload between stage 0's loads, and the barrier could pass before that
+  // stage had landed).
   constexpr int kReload = Q4 ? 1 : (DQ ? 3 : 2);   // loads per code-set reload
   if constexpr (Q4) q4.issue(0);
   P.issue(s0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   issue_x(xs0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   P.issue(s1, __builtin_amdgcn_readfirstlane(min(1, last)));
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (Q4) P.store_scaled(s0, Scale4::scale(q4.nxt, q4.nxt_s, 0), ws0, nullptr, cb.v, lane, [&](int) {});
-  else P.store(s0, ws0, nullptr, cb.v, lane, [&](int) {});
+  else P.store(s0, ws0, KN ? pair : nullptr, cb.v, lane, [&](int) {});
   P.issue(s0, __builtin_amdgcn_readfirstlane(min(2, last)));
   __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kReload));
   lds_barrier();
@@ -923,13 +948,101 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   const int wsw = wswz<false>(wcol);
   const int last4 = last >> 2;
   auto step = [&](auto phase, int s, const uint16_t *xc, const uint16_t *wc, uint16_t *xn, uint16_t *wn,
-                  typename Producer<false, DQ, Q4>::Set &set) {
+                  typename Producer<KN, DQ, Q4>::Set &set) {
     constexpr int ph = decltype(phase)::value;
     issue_x(xn, s + 1);
     if constexpr (Q4 && ph == 0) {
       q4.cur = q4.nxt;
       q4.cur_s = q4.nxt_s;
       q4.issue(__builtin_amdgcn_readfirstlane(min((s >> 2) + 1, last4)));
+    }
+    if constexpr (KN) {
+      // Transposed weights (dX): the producer of the 256 x 128 tiling, its
+      // work spread over the four k-slices.  Slice 0 goes with the quad
+      // transpose of the code words and the four rows' scales, slices 1 to 3
+      // with the table lookups of the patch's rows, and the patch is written
+      // transposed after the last slice.
+      Frag f0, f1;
+      read_f(f0, xc, wc, 0);
+      read_f(f1, xc, wc, 1);
+      uint32_t w0 = set.code[0], w1 = set.code[1], w2 = set.code[2], w3 = set.code[3];
+      const bool odd = lane & 1, hi2 = lane & 2;
+      {
+        uint32_t x = odd ? w0 : w1, y = odd ? w2 : w3;
+        x = qperm<0xB1>(x);
+        y = qperm<0xB1>(y);
+        if (odd) { w0 = x; w2 = y; } else { w1 = x; w3 = y; }
+      }
+      {
+        uint32_t x = hi2 ? w0 : w2, y = hi2 ? w1 : w3;
+        x = qperm<0x4E>(x);
+        y = qperm<0x4E>(y);
+        if (hi2) { w0 = x; w1 = y; } else { w2 = x; w3 = y; }
+      }
+      const uint32_t au = as_u32(P.scale(set));
+      const float S[4] = {as_f32(qperm<0x00>(au)), as_f32(qperm<0x55>(au)), as_f32(qperm<0xAA>(au)),
+                          as_f32(qperm<0xFF>(au))};
+      const uint32_t wv[4] = {w0, w1, w2, w3};
+      mma(f0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      read_f(f0, xc, wc, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int copy = lane & (kPairCopies - 1);
+      float v[4][8];
+      auto lookrow = [&](int i) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float2 pv = pair[((wv[i] >> (8 * m)) & 0xFF) * kPairCopies + copy];
+          v[i][2 * m] = pv.x * S[i];
+          v[i][2 * m + 1] = pv.y * S[i];
+        }
+      };
+      // slice 1 + rows 0 and 1
+      mma(f1);
+      lookrow(0);
+      lookrow(1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      read_f(f1, xc, wc, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 2 + rows 0 and 1 packed, row 2
+      mma(f0);
+      uint32_t pk01[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) pk01[c] = pack_bf16x2(v[0][c], v[1][c]);
+      lookrow(2);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 3 + row 3
+      mma(f1);
+      lookrow(3);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int kk = P.wr_k ^ kswz(P.wr_col);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<u32x2 *>(&wn[(P.wr_col + c) * LD + kk]) = u32x2{pk01[c], pack_bf16x2(v[2][c], v[3][c])};
+      __builtin_amdgcn_sched_barrier(0);
+      P.issue(set, __builtin_amdgcn_readfirstlane(min(s + 3, last)));
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload));
+      lds_barrier();
+      return;
     }
     Frag f0, f1;
     read_f(f0, xc, wc, 0);
@@ -1044,20 +1157,23 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
   {
     const int col = tid & (BN2 - 1), j0 = 32 * (tid >> 8);
     const int64_t gn = n0 + col;
-    const rsrc_t rr = make_rsrc(a.R2, a.Nout * a.ldr2 * 2);
+    // B is [Nout, r]; for dX the operand is A, [r, Nout], into stage row kn_row(col).
+    const rsrc_t rr = make_rsrc(a.R2, KN ? a.r * a.ldr2 * 2 : a.Nout * a.ldr2 * 2);
     uint32_t h[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int64_t j = j0 + i;
       const bool in = j < a.r && gn < a.Nout;
-      h[i] = __builtin_amdgcn_raw_buffer_load_b16(rr, in ? (uint32_t)((gn * a.ldr2 + j) * 2) : kOutOfRange, 0, 0);
+      const int64_t e = KN ? j * a.ldr2 + gn : gn * a.ldr2 + j;
+      h[i] = __builtin_amdgcn_raw_buffer_load_b16(rr, in ? (uint32_t)(e * 2) : kOutOfRange, 0, 0);
     }
     uint32_t v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = (h[2 * i] & 0xFFFFu) | (h[2 * i + 1] << 16);
+    const int srow = KN ? kn_row(col) : col;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4 *>(&wa[col * LD + ((j0 + 8 * q) ^ wswz<false>(col))]) = u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+      *reinterpret_cast<u32x4 *>(&wa[srow * LD + ((j0 + 8 * q) ^ wswz<KN>(srow))]) = u32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   lds_barrier();
@@ -1089,7 +1205,7 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
     for (int q = 0; q < 8; ++q) {
       const int row = 4 * q + (lane >> 4), c8 = 8 * (lane & 15);
       const u32x4 v = *reinterpret_cast<const u32x4 *>(&blk[row * kOutPitch + c8]);
-      const int64_t lrow = (int64_t)rg * WM + i * 32 + row, gn = n0 + 128 * cg + c8;
+      const int64_t lrow = (int64_t)rg * WM + i * 32 + row, gn = n0 + (KN ? kn_col(128 * cg + c8) : 128 * cg + c8);
       if (vec_ok && gn + 8 <= a.Nout) {
         __builtin_amdgcn_raw_buffer_store_b128(v, rout, (uint32_t)((lrow * a.ldo + gn) * 2), 0, 0);
       } else if (m0 + lrow < a.M) {
@@ -1290,10 +1406,15 @@ void qgemm3_kernel(QGemmGroup grp, Code16 cb) {
   };
 
   // ---- prologue
+  // Fenced so that the wait before the barrier covers stage 0 (see the
+  // 8-wave tiling's prologue).
   constexpr int kReload3 = DQ ? 4 : 3;
   P.issue(s0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   issue_x(xs0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   P.issue(s1, __builtin_amdgcn_readfirstlane(min(1, last)));
+  __builtin_amdgcn_sched_barrier(0);
   prep(s0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) word(s0, i, ws0);
@@ -1452,7 +1573,7 @@ bool plan(QGemmArgs &a, int bm = BM, int bn = BN) {
 // round-robin by their global index).
 std::atomic<int> g_variant{0};   // 0 automatic, 1 256 x 128, 2 256 x 256 (8 waves), 3 256 x 256 (4 waves)
 
-// One launch of one tiling over n problems (wide: 256 x 256, forward only).
+// One launch of one tiling over n problems (wide: 256 x 256; dX has only the 8-wave one).
 template <bool KN, bool EPI_NK>
 hipError_t launch_tiling(const QGemmArgs *in, int n, bool wide, int wide_kind, hipStream_t st) {
   const int bm = wide ? BM2 : BM, bn = wide ? BN2 : BN;
@@ -1473,7 +1594,13 @@ hipError_t launch_tiling(const QGemmArgs *in, int n, bool wide, int wide_kind, h
   for (int k = n; k <= QN_MAX_GROUP; ++k) grp.start[k] = (int)total;
   grp.n = n;
   const dim3 grid((unsigned)total);
-  if constexpr (!KN) {
+  if constexpr (KN) {
+    if (wide) {   // dX: the 8-wave 256 x 256 tiling
+      if (dq) hipLaunchKernelGGL((qgemm2_kernel<true, false, true>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      else hipLaunchKernelGGL((qgemm2_kernel<false, false, true>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      return hipGetLastError();
+    }
+  } else {
     if (wide && wide_kind == 3) {
       if (dq) hipLaunchKernelGGL((qgemm3_kernel<true>), grid, dim3(kThreads3), 0, st, grp, code16(in[0].qtype));
       else hipLaunchKernelGGL((qgemm3_kernel<false>), grid, dim3(kThreads3), 0, st, grp, code16(in[0].qtype));
@@ -1482,9 +1609,9 @@ hipError_t launch_tiling(const QGemmArgs *in, int n, bool wide, int wide_kind, h
     if (wide) {
       bool q4 = dq;   // Scale4 needs rows of a multiple of four blocks
       for (int k = 0; k < n; ++k) q4 = q4 && in[k].Kc % 256 == 0;
-      if (q4) hipLaunchKernelGGL((qgemm2_kernel<true, true>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
-      else if (dq) hipLaunchKernelGGL((qgemm2_kernel<true, false>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
-      else hipLaunchKernelGGL((qgemm2_kernel<false, false>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      if (q4) hipLaunchKernelGGL((qgemm2_kernel<true, true, false>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      else if (dq) hipLaunchKernelGGL((qgemm2_kernel<true, false, false>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
+      else hipLaunchKernelGGL((qgemm2_kernel<false, false, false>), grid, dim3(kThreads2), 0, st, grp, code16(in[0].qtype));
       return hipGetLastError();
     }
   }
@@ -1507,14 +1634,15 @@ hipError_t launch_tiling(const QGemmArgs *in, int n, bool wide, int wide_kind, h
 // layer's q projection on 256 x 256 tiles and its short k and v on 256 x 128)
 // when the two launches' rounds cost less than either tiling alone, counting
 // a tenth of a round for the second launch.  The kernel trace brackets the
-// call's launches together.
+// call's launches together.  dX takes the same choice between its two tilings
+// (the 8-wave 256 x 256 one and 256 x 128; a forced variant 3 means the
+// 8-wave one there): its wide tile measures about 1.8 times a narrow one.
 template <bool KN, bool EPI_NK>
 hipError_t launch(const QGemmArgs *in, int n, hipStream_t st, int trace_kind) {
   if (n < 1 || n > QN_MAX_GROUP) return hipErrorInvalidValue;
   TraceScope tr(trace_kind, st);
   const int v = g_variant.load(std::memory_order_relaxed);
   const int wide_kind = v == 3 ? 3 : 2;
-  if (KN) return launch_tiling<KN, EPI_NK>(in, n, false, wide_kind, st);
   if (v != 0) return launch_tiling<KN, EPI_NK>(in, n, v >= 2, wide_kind, st);
   const int64_t cus = device_cus();
   int64_t tw[QN_MAX_GROUP], tn[QN_MAX_GROUP];

@@ -136,7 +136,7 @@ hipError_t launch_qgemm_dx(const QGemmArgs &a, hipStream_t s);
 // problems must agree on the scale source (all double-quantised or none) and
 // on the 4-bit type.
 hipError_t launch_qgemm_fwd_group(const QGemmArgs *a, int n, hipStream_t s);
-// Forward tiling choice for all later launches: 0 automatic, 1 256 x 128, 2 256 x 256.
+// Tiling choice of the dequant-GEMMs (forward and dX) for all later launches: 0 automatic, 1 256 x 128, 2 256 x 256.
 void set_gemm_variant(int v);
 
 // Problems of one grouped launch, passed by value in the kernel arguments.

@@ -358,9 +358,10 @@ int qlora_linear_bwd(const void *dY, const void *X, const float *H, int64_t M,
 int qn_trace_enable(int on);
 int qn_trace_read(int *kinds, float *ms, int cap);
 
-/* Tiling of the forward dequant-GEMM for the calls that follow, process-wide
- * (for measurement and tests; results are the same either way up to the order
- * of fp32 accumulation within a tile, which both tilings share):
+/* Tiling of the dequant-GEMMs (forward and the backward's dX) for the calls
+ * that follow, process-wide (for measurement and tests; results are the same
+ * either way up to the order of fp32 accumulation within a tile, which the
+ * tilings share; dX has tilings 1 and 2 only, and 3 selects 2 there):
  *   0  automatic (the default): per launch, the tiling whose rounds of tiles
  *      over the compute units, weighted by the measured time of one tile,
  *      finish first (256 x 256 tiles for large launches, 256 x 128 for small

@@ -103,3 +103,78 @@ def test_grouped_launch_equals_single_calls(variant):
         torch.cuda.synchronize()
         assert torch.equal(Y, Y1) and torch.equal(H, H1)
         _check(host(Y), host(H), Xh, Ah, Bh, Wh, alpha)
+
+
+@pytest.mark.parametrize("M,N,K,r,qt,dq", [
+    (300, 320, 512, 16, "nf4", True),    # ragged M; five contraction steps over N
+    (77, 64, 192, 8, "nf4", True),       # one step; a partial 256-wide column tile
+    (513, 576, 320, 24, "nf4", False),   # fp32 scales; nine steps
+    (256, 128, 256, 1, "nf4", True),     # rank 1
+    (200, 256, 512, 16, "fp4", True),
+    (1024, 1024, 2048, 64, "nf4", True),
+])
+def test_dx_tilings_match_the_oracle(M, N, K, r, qt, dq):
+    """The backward's dX = dY W_hat + dH A on both tilings (256 x 128 and
+    256 x 256, forced) against the fp64 oracle: relative Frobenius <= 5e-3 and
+    the elementwise bound |err| <= 2^-7 (|dY| |W_hat| + |dH| |A|), dX
+    guard-banded; dA and dB do not depend on the tiling."""
+    w, X, A, B, Wh = _case(M, N, K, r, seed=M + 3 * N + K, qt=qt, dq=dq)
+    dY = synth.to_bf16(synth.gaussian((M, N), 1.0, synth.SEED_X + 77 + M))
+    Xv, Av, Bv, Gv = (synth.bf16_values(t) for t in (X, A, B, dY))
+    alpha = 2.0 * r
+    dXr, _, _ = oracle.backward(Gv, Xv, Wh, Av, Bv, alpha)
+    dH = (alpha / r) * (Gv.astype(np.float64) @ Bv.astype(np.float64))
+    bound = np.abs(Gv.astype(np.float64)) @ np.abs(Wh.astype(np.float64)) + np.abs(dH) @ np.abs(Av.astype(np.float64))
+    out = {}
+    for v in (1, 2):
+        say(f"dX tiling {v}: M={M} N={N} K={K} r={r} {qt} dq={dq}")
+        lib.set_gemm_variant(v)
+        full, dX = guarded(M * K * 2, torch.bfloat16)
+        dX = dX.view(M, K)
+        dA = torch.empty((r, K), dtype=torch.bfloat16, device=dev())
+        dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev())
+        lib.qlora_linear_bwd(dY.to(dev()), X.to(dev()), w, A.to(dev()), B.to(dev()), alpha, use_double_quant=dq,
+                             out=(dX, dA, dB))
+        torch.cuda.synchronize()
+        assert guards_intact(full, M * K * 2), "dX guard band overwritten"
+        got = host(dX)
+        assert rel_fro(got, dXr) <= REL_FRO_TOL
+        assert np.all(np.abs(got - dXr) <= 2 * 2.0 ** -8 * bound + 1e-30)
+        out[v] = got
+    assert np.all(np.abs(out[1] - out[2]) <= 2 * 2.0 ** -8 * bound + 1e-30)
+
+
+@pytest.mark.parametrize("variant", [2, 3])
+def test_wide_tiling_repeats_exactly(variant):
+    """Four repetitions of a forward over 1184 wide tiles (and, on the 8-wave
+    tiling, of a backward whose dX covers 512 wide tiles) give identical bits.
+    Each tile's prologue stages its first activation slab with direct-to-LDS
+    loads that the barrier after it must wait for; a tile that read the slab
+    early would show up as differing rows in some repetition."""
+    lib.set_gemm_variant(variant)
+    say(f"wide tiling {variant}: repeated forward 4096 x 18944 x 512")
+    M, N, K, r = 4096, 18944, 512, 16
+    W = synth.gaussian((N, K), 0.02, synth.SEED_W + 91)
+    w = lib.quantize_weight(to_dev(W))
+    X = synth.to_bf16(synth.gaussian((M, K), 1.0, synth.SEED_X + 91)).to(dev())
+    A = synth.to_bf16(synth.gaussian((r, K), 0.01, synth.SEED_A + 91)).to(dev())
+    B = synth.to_bf16(synth.gaussian((N, r), 0.02, synth.SEED_B + 91)).to(dev())
+    ys = [lib.qlora_linear_fwd(X, w, A, B, 2.0 * r) for _ in range(4)]
+    torch.cuda.synchronize()
+    for i in range(1, 4):
+        assert torch.equal(ys[i], ys[0]), f"forward repetition {i} differs"
+    del ys, w, X, A, B
+    if variant != 2:
+        return
+    say("wide tiling 2: repeated backward, dX 4096 x 8192 from N = 512")
+    M, N, K, r = 4096, 512, 8192, 16
+    W = synth.gaussian((N, K), 0.02, synth.SEED_W + 92)
+    w = lib.quantize_weight(to_dev(W))
+    X = synth.to_bf16(synth.gaussian((M, K), 1.0, synth.SEED_X + 92)).to(dev())
+    dY = synth.to_bf16(synth.gaussian((M, N), 1.0, synth.SEED_X + 93)).to(dev())
+    A = synth.to_bf16(synth.gaussian((r, K), 0.01, synth.SEED_A + 92)).to(dev())
+    B = synth.to_bf16(synth.gaussian((N, r), 0.02, synth.SEED_B + 92)).to(dev())
+    gs = [lib.qlora_linear_bwd(dY, X, w, A, B, 2.0 * r) for _ in range(4)]
+    torch.cuda.synchronize()
+    for i in range(1, 4):
+        assert all(torch.equal(a, b) for a, b in zip(gs[i], gs[0])), f"backward repetition {i} differs"
