@@ -570,7 +570,12 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
     // counted in its wait).
     constexpr int kReload = Q4 ? 1 : (DQ ? 3 : 2);
     const int last4 = last >> 2;
-    auto half = [&](auto phase, int t, typename Producer<KN, DQ, Q4>::Set &set, uint16_t *wdst) {   // t < nsteps
+    // The last half-step of an odd count (tail) reloads a set that nothing
+    // reads again, and the compiler drops that load; its wait then counts only
+    // the loads that remain after stage t (the previous reload and stage t + 1),
+    // which is right whether or not the dead load survives.
+    auto half = [&](auto phase, int t, typename Producer<KN, DQ, Q4>::Set &set, uint16_t *wdst,
+                    bool tail = false) {   // t < nsteps
       constexpr int ph = decltype(phase)::value;
       constexpr int kScale = Q4 && ph == 0 ? 2 : 0;
       if constexpr (kScale) {
@@ -587,7 +592,8 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
       __builtin_amdgcn_sched_barrier(0);
       P.issue(set, min(t + 2, last));
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload + 8 + kScale + kReload));
+      if (tail) __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload + 8 + kScale));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload + 8 + kScale + kReload));
       lds_barrier();
     };
     // Weight half-steps in pairs, then the odd one out.  Neither an exit from
@@ -613,7 +619,7 @@ void qgemm_kernel(QGemmGroup grp, Code16 cb) {
         half(P1{}, t + 1, s1, ws1);
       }
       if (t < nsteps) {
-        half(P0{}, t, s0, ws0);
+        half(P0{}, t, s0, ws0, true);
         ++t;
       }
     }
