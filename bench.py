@@ -71,9 +71,9 @@ KERNEL_SOURCE = {
 # bytes.  Keyed by kernel and workload; `sha256` is that of the kernel's source
 # file and qn_device.h when the counters were taken.
 TRAFFIC = {
-    "gemm_fwd_70b": {"bytes": 1562702578, "sha256": "b665b11f8e06270717bb1f377ec7b678eaff6c5eeec30c13b44fbcbea94bad38"},
-    "lowrank_70b": {"bytes": 176663967, "sha256": "a9720ed64701ca58a3adf8b5f53627d51383e3fd25feb52c5caef37c5c1ca6bb"},
-    "gemv_70b": {"bytes": 114969572, "sha256": "a5da0adfb8a87a342062662a46fde1812682acb87b6815a04b93989080b3022b"},
+    "gemm_fwd_70b": {"bytes": 1567300477, "sha256": "d1003fb40c72094218af7a896d0e3965071ff2ab4f8090b27a6d9a2a456b4c4a"},
+    "lowrank_70b": {"bytes": 176664427, "sha256": "a9720ed64701ca58a3adf8b5f53627d51383e3fd25feb52c5caef37c5c1ca6bb"},
+    "gemv_70b": {"bytes": 114969786, "sha256": "a5da0adfb8a87a342062662a46fde1812682acb87b6815a04b93989080b3022b"},
 }
 
 # The configurations (N, K) of the linear layers.
