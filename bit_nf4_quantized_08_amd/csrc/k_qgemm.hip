@@ -299,44 +299,71 @@ struct Producer {
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4 *>(&row[(wr_k + 8 * i) ^ sw]) = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
     } else {
-      // 4 x 4 transpose of words within the quad: w[i] of lane j <- word j of lane i.
-      uint32_t w0 = t.code[0], w1 = t.code[1], w2 = t.code[2], w3 = t.code[3];
-      const bool odd = lane & 1, hi = lane & 2;
-      {
-        uint32_t x = odd ? w0 : w1, y = odd ? w2 : w3;
-        x = qperm<0xB1>(x);
-        y = qperm<0xB1>(y);
-        if (odd) { w0 = x; w2 = y; } else { w1 = x; w3 = y; }
-      }
-      {
-        uint32_t x = hi ? w0 : w2, y = hi ? w1 : w3;
-        x = qperm<0x4E>(x);
-        y = qperm<0x4E>(y);
-        if (hi) { w0 = x; w1 = y; } else { w2 = x; w3 = y; }
-      }
-      const uint32_t au = as_u32(A);
-      const float S[4] = {as_f32(qperm<0x00>(au)), as_f32(qperm<0x55>(au)), as_f32(qperm<0xAA>(au)),
-                          as_f32(qperm<0xFF>(au))};
-      const uint32_t wv[4] = {w0, w1, w2, w3};
+      uint32_t wv[4];
+      float S[4];
+      patch_prep(t, A, lane, wv, S);
       float v[4][8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_barrier(0);
         hook(i);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float2 p = pair[((wv[i] >> (8 * m)) & 0xFF) * kPairCopies + copy];
-          v[i][2 * m] = p.x * S[i];
-          v[i][2 * m + 1] = p.y * S[i];
-        }
+        patch_row(wv, S, i, pair, copy, v[i]);
       }
-      const int k = wr_k ^ kswz(wr_col);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<u32x2 *>(&Rs[(wr_col + c) * LD + k]) =
-            u32x2{pack_bf16x2(v[0][c], v[1][c]), pack_bf16x2(v[2][c], v[3][c])};
+      write_patch(Rs, v[0], v[1], v[2], v[3]);
     }
+  }
+
+  // Transposed weights, in parts that a caller can spread over its own work:
+  // patch_prep transposes the quad's 4 x 4 code words (w[i] of lane j <- word
+  // j of lane i) and broadcasts the four rows' block scales within the quad;
+  // patch_row expands row i of the lane's 4 x 8 patch through the byte-pair
+  // table; write_patch stores the patch transposed (8-byte column pieces).
+  __device__ __forceinline__ void patch_prep(const Set &t, float A, int lane, uint32_t (&wv)[4], float (&S)[4]) const {
+    uint32_t w0 = t.code[0], w1 = t.code[1], w2 = t.code[2], w3 = t.code[3];
+    const bool odd = lane & 1, hi = lane & 2;
+    {
+      uint32_t x = odd ? w0 : w1, y = odd ? w2 : w3;
+      x = qperm<0xB1>(x);
+      y = qperm<0xB1>(y);
+      if (odd) { w0 = x; w2 = y; } else { w1 = x; w3 = y; }
+    }
+    {
+      uint32_t x = hi ? w0 : w2, y = hi ? w1 : w3;
+      x = qperm<0x4E>(x);
+      y = qperm<0x4E>(y);
+      if (hi) { w0 = x; w1 = y; } else { w2 = x; w3 = y; }
+    }
+    const uint32_t au = as_u32(A);
+    S[0] = as_f32(qperm<0x00>(au));
+    S[1] = as_f32(qperm<0x55>(au));
+    S[2] = as_f32(qperm<0xAA>(au));
+    S[3] = as_f32(qperm<0xFF>(au));
+    wv[0] = w0; wv[1] = w1; wv[2] = w2; wv[3] = w3;
+  }
+  __device__ __forceinline__ static void patch_row(const uint32_t (&wv)[4], const float (&S)[4], int i,
+                                                   const float2 *pair, int copy, float (&v)[8]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float2 p = pair[((wv[i] >> (8 * m)) & 0xFF) * kPairCopies + copy];
+      v[2 * m] = p.x * S[i];
+      v[2 * m + 1] = p.y * S[i];
+    }
+  }
+  // Rows 0 and 1 may come packed already (pk01[c] = bf16 pair of rows 0, 1).
+  __device__ __forceinline__ void write_patch(uint16_t *Rs, const uint32_t (&pk01)[8], const float (&v2)[8],
+                                              const float (&v3)[8]) const {
+    const int k = wr_k ^ kswz(wr_col);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<u32x2 *>(&Rs[(wr_col + c) * LD + k]) = u32x2{pk01[c], pack_bf16x2(v2[c], v3[c])};
+  }
+  __device__ __forceinline__ void write_patch(uint16_t *Rs, const float (&v0)[8], const float (&v1)[8],
+                                              const float (&v2)[8], const float (&v3)[8]) const {
+    uint32_t pk01[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) pk01[c] = pack_bf16x2(v0[c], v1[c]);
+    write_patch(Rs, pk01, v2, v3);
   }
 };
 
@@ -971,24 +998,9 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
       Frag f0, f1;
       read_f(f0, xc, wc, 0);
       read_f(f1, xc, wc, 1);
-      uint32_t w0 = set.code[0], w1 = set.code[1], w2 = set.code[2], w3 = set.code[3];
-      const bool odd = lane & 1, hi2 = lane & 2;
-      {
-        uint32_t x = odd ? w0 : w1, y = odd ? w2 : w3;
-        x = qperm<0xB1>(x);
-        y = qperm<0xB1>(y);
-        if (odd) { w0 = x; w2 = y; } else { w1 = x; w3 = y; }
-      }
-      {
-        uint32_t x = hi2 ? w0 : w2, y = hi2 ? w1 : w3;
-        x = qperm<0x4E>(x);
-        y = qperm<0x4E>(y);
-        if (hi2) { w0 = x; w1 = y; } else { w2 = x; w3 = y; }
-      }
-      const uint32_t au = as_u32(P.scale(set));
-      const float S[4] = {as_f32(qperm<0x00>(au)), as_f32(qperm<0x55>(au)), as_f32(qperm<0xAA>(au)),
-                          as_f32(qperm<0xFF>(au))};
-      const uint32_t wv[4] = {w0, w1, w2, w3};
+      uint32_t wv[4];
+      float S[4];
+      P.patch_prep(set, P.scale(set), lane, wv, S);
       mma(f0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -999,14 +1011,7 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
       __builtin_amdgcn_sched_barrier(0);
       const int copy = lane & (kPairCopies - 1);
       float v[4][8];
-      auto lookrow = [&](int i) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float2 pv = pair[((wv[i] >> (8 * m)) & 0xFF) * kPairCopies + copy];
-          v[i][2 * m] = pv.x * S[i];
-          v[i][2 * m + 1] = pv.y * S[i];
-        }
-      };
+      auto lookrow = [&](int i) { P.patch_row(wv, S, i, pair, copy, v[i]); };
       // slice 1 + rows 0 and 1
       mma(f1);
       lookrow(0);
@@ -1040,10 +1045,7 @@ void qgemm2_kernel(QGemmGroup grp, Code16 cb) {
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const int kk = P.wr_k ^ kswz(P.wr_col);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<u32x2 *>(&wn[(P.wr_col + c) * LD + kk]) = u32x2{pk01[c], pack_bf16x2(v[2][c], v[3][c])};
+      P.write_patch(wn, pk01, v[2], v[3]);
       __builtin_amdgcn_sched_barrier(0);
       P.issue(set, __builtin_amdgcn_readfirstlane(min(s + 3, last)));
       __builtin_amdgcn_s_waitcnt(vmcnt_only(kReload));
