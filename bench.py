@@ -71,9 +71,9 @@ KERNEL_SOURCE = {
 # bytes.  Keyed by kernel and workload; `sha256` is that of the kernel's source
 # file and qn_device.h when the counters were taken.
 TRAFFIC = {
-    "gemm_fwd_70b": {"bytes": 1567300477, "sha256": "d1003fb40c72094218af7a896d0e3965071ff2ab4f8090b27a6d9a2a456b4c4a"},
-    "lowrank_70b": {"bytes": 176664427, "sha256": "a9720ed64701ca58a3adf8b5f53627d51383e3fd25feb52c5caef37c5c1ca6bb"},
-    "gemv_70b": {"bytes": 114969786, "sha256": "a5da0adfb8a87a342062662a46fde1812682acb87b6815a04b93989080b3022b"},
+    "gemm_fwd_70b": {"bytes": 1565569317, "sha256": "eeece9299dab90e57c0d8c85d8c243062b22dc01db76f699f6f807421ae217ea"},
+    "lowrank_70b": {"bytes": 176664927, "sha256": "a9720ed64701ca58a3adf8b5f53627d51383e3fd25feb52c5caef37c5c1ca6bb"},
+    "gemv_70b": {"bytes": 114969601, "sha256": "a5da0adfb8a87a342062662a46fde1812682acb87b6815a04b93989080b3022b"},
 }
 
 # The configurations (N, K) of the linear layers.
