@@ -144,16 +144,19 @@ def test_dx_tilings_match_the_oracle(M, N, K, r, qt, dq):
     assert np.all(np.abs(out[1] - out[2]) <= 2 * 2.0 ** -8 * bound + 1e-30)
 
 
-@pytest.mark.parametrize("variant", [2, 3])
-def test_wide_tiling_repeats_exactly(variant):
-    """Four repetitions of a forward over 1184 wide tiles (and, on the 8-wave
-    tiling, of a backward whose dX covers 512 wide tiles) give identical bits.
-    Each tile's prologue stages its first activation slab with direct-to-LDS
-    loads that the barrier after it must wait for; a tile that read the slab
-    early would show up as differing rows in some repetition."""
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_tilings_repeat_exactly(variant):
+    """Four repetitions of a forward over more than a thousand tiles (and, on
+    the tilings dX has, of a backward whose dX covers hundreds of tiles) give
+    identical bits.  Each tile stages activation slabs with direct-to-LDS loads
+    that a barrier must wait for (in the prologue, and on the 256 x 128 tiling
+    in the last half-step of an odd step count, which K = 320 gives); a tile
+    that read a slab early would show up as differing rows in some
+    repetition."""
     lib.set_gemm_variant(variant)
-    say(f"wide tiling {variant}: repeated forward 4096 x 18944 x 512")
-    M, N, K, r = 4096, 18944, 512, 16
+    K = 320 if variant == 1 else 512
+    say(f"tiling {variant}: repeated forward 4096 x 18944 x {K}")
+    M, N, r = 4096, 18944, 16
     W = synth.gaussian((N, K), 0.02, synth.SEED_W + 91)
     w = lib.quantize_weight(to_dev(W))
     X = synth.to_bf16(synth.gaussian((M, K), 1.0, synth.SEED_X + 91)).to(dev())
@@ -164,10 +167,11 @@ def test_wide_tiling_repeats_exactly(variant):
     for i in range(1, 4):
         assert torch.equal(ys[i], ys[0]), f"forward repetition {i} differs"
     del ys, w, X, A, B
-    if variant != 2:
+    if variant == 3:
         return
-    say("wide tiling 2: repeated backward, dX 4096 x 8192 from N = 512")
-    M, N, K, r = 4096, 512, 8192, 16
+    N = 320 if variant == 1 else 512
+    say(f"tiling {variant}: repeated backward, dX 4096 x 8192 from N = {N}")
+    M, K, r = 4096, 8192, 16
     W = synth.gaussian((N, K), 0.02, synth.SEED_W + 92)
     w = lib.quantize_weight(to_dev(W))
     X = synth.to_bf16(synth.gaussian((M, K), 1.0, synth.SEED_X + 92)).to(dev())
