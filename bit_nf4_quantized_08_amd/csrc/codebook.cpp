@@ -81,12 +81,13 @@ double fp4_value(int c) {
 // ascending (a repeated value keeps its smaller code); threshold i is the
 // smallest fp32 strictly above the exact midpoint of levels i and i+1, so an
 // fp32 value equal to a representable midpoint stays with the lower level.
-// Buckets of width 1/16 over [-1, 1] each hold at most one threshold:
+// Buckets of width 1/16 over [-1, 1 + 1/16) each hold at most one threshold:
 // base[b] = levels below the bucket, thr[b] = its threshold (or +inf),
 // lohi[b] = code of level base[b] | code of level base[b] + 1 << 8.  The
-// kernel's bucket index floor(16 n + 16) can only come out one too high, for an
-// n within a few 1e-8 below a bucket edge, so no threshold may lie just below
-// an edge (checked).
+// kernel takes the bucket from the fp32 sum n + 5 (rounded once, in [4, 8)),
+// whose edges 5 + b/16 - 1 are representable, so the bucket can only come
+// out one too high, for an n within 2^-22 below an edge; no threshold may lie
+// that close below an edge (checked, with a margin of 1e-6).
 void build_decisions(CodecTables &t) {
   int order[16];
   for (int i = 0; i < 16; ++i) order[i] = i;
@@ -105,7 +106,7 @@ void build_decisions(CodecTables &t) {
   }
   float T[15];
   for (int i = 0; i + 1 < L; ++i) T[i] = next_f32_above(((double)lev[i] + (double)lev[i + 1]) / 2.0);
-  for (int b = 0; b < 32; ++b) {
+  for (int b = 0; b < kBuckets; ++b) {
     const double lo = b / 16.0 - 1.0, hi = (b + 1) / 16.0 - 1.0;
     uint32_t below = 0;
     float inside = INFINITY;
@@ -147,7 +148,7 @@ void build() {
   build_decisions(g_tables[QN_FP4]);
   // The NF4 rows are distinct and ascending: the code of a level is its rank,
   // which the quantiser's NF4 path relies on.
-  for (int b = 0; b < 32; ++b) {
+  for (int b = 0; b < kBuckets; ++b) {
     const uint32_t lo = g_tables[QN_NF4].lohi[b] & 0xFF;
     if (lo != g_tables[QN_NF4].base[b]) g_ok = false;
   }

@@ -16,6 +16,8 @@
 #pragma clang fp contract(off)
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "qn_device.h"
 #include "qn_internal.h"
@@ -25,21 +27,21 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Code of one normalised value: bucket lookup plus one compare.  lut[b] holds
-// the bucket's threshold and, for NF4, the level below it (whose code is the
-// level itself), for FP4 the two candidate codes (low byte below the
-// threshold, second byte at or above it).
+// Code of one normalised value n: bucket lookup plus one compare.  t5 is the
+// fp32 value of n + 5 rounded once (in [4, 8) for n in [-1, 1 + 2^-23]):
+// its mantissa's top six bits are the bucket floor(16 n + 16), 0 .. 32.
+// lut[b] holds the bucket's threshold and, for NF4, the level below it (whose
+// code is the level itself), for FP4 the two candidate codes (low byte below
+// the threshold, second byte at or above it).
 template <int QT>
-__device__ __forceinline__ uint32_t nearest_row(float nrm, const float2 *lut) {
-  int b = (int)__builtin_fmaf(nrm, 16.0f, 16.0f);
-  b = min(max(b, 0), 31);
-  const float2 e = lut[b];
+__device__ __forceinline__ uint32_t nearest_row(float nrm, float t5, const float2 *lut) {
+  const float2 e = lut[(as_u32(t5) >> 17) & 63u];
   if constexpr (QT == QN_NF4) return as_u32(e.y) + (nrm >= e.x ? 1u : 0u);
   else return (as_u32(e.y) >> (nrm >= e.x ? 8 : 0)) & 0xFu;
 }
 
 __device__ __forceinline__ void load_lut(float2 *lut, const CodecTables &tab, int qt) {
-  if (threadIdx.x < 32)
+  if (threadIdx.x < kBuckets)
     lut[threadIdx.x] = make_float2(tab.thr[threadIdx.x],
                                    __builtin_bit_cast(float, qt == QN_NF4 ? tab.base[threadIdx.x] : tab.lohi[threadIdx.x]));
 }
@@ -61,6 +63,10 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
 
 // Codes of `cnt` normalised values x[i] * rho (or x[i] / a when 1/a overflows),
 // packed low nibble first.
@@ -71,11 +77,15 @@ __device__ __forceinline__ uint32_t encode(const float *x, float am, const float
   uint32_t w = 0;
   if (!__builtin_isinf(rho)) {
 #pragma unroll
-    for (int i = 0; i < CNT; ++i) w |= nearest_row<QT>(x[i] * rho, lut) << (4 * i);
+    for (int i = 0; i < CNT; ++i)
+      w |= nearest_row<QT>(x[i] * rho, __builtin_fmaf(x[i], rho, 5.0f), lut) << (4 * i);
   } else {
     // 1/a overflows fp32 (a < 2^-128): divide each weight by a instead.
 #pragma unroll
-    for (int i = 0; i < CNT; ++i) w |= nearest_row<QT>(x[i] / am, lut) << (4 * i);
+    for (int i = 0; i < CNT; ++i) {
+      const float nrm = x[i] / am;
+      w |= nearest_row<QT>(nrm, nrm + 5.0f, lut) << (4 * i);
+    }
   }
   return w;
 }
@@ -120,14 +130,28 @@ __device__ void quantize_tail(const void *__restrict__ W, int64_t n, int64_t sta
   }
 }
 
-// One full 1024-element span starting at `base`, in two halves so that a
-// caller can have several spans' loads in flight before it encodes the first:
-// span_load issues the wave's coalesced loads (fp32: 4 x 16 bytes per lane,
-// bf16: 2 x 16 bytes), span_encode reduces the block absmaxes (written to
-// absmax and, when am_lds is given, to am_lds[block - blk0]) and stores the codes.
+// One full 1024-element span starting at `base`, in three parts so that a
+// caller can have several spans' loads in flight and encode them in one
+// straight-line stretch of code: span_load issues the wave's coalesced loads
+// (fp32: 4 x 16 bytes per lane, bf16: 2 x 16 bytes), span_codes reduces the
+// block absmaxes and encodes every element with the block's reciprocal,
+// span_store writes codes and absmaxes (and, when am_lds is given, the
+// absmaxes to am_lds[block - blk0]).  A block whose reciprocal overflows is
+// re-encoded by span_codes_div, behind one wave-uniform test per group of
+// spans, so the common path has no branch and its table lookups can overlap.
 template <bool BF16>
 struct SpanRaw {
   u32x4 v[BF16 ? 2 : 4];
+};
+
+// Per load instruction i of a span: the lane's packed codes, its block's
+// absmax and reciprocal.
+template <bool BF16>
+struct SpanEnc {
+  static constexpr int kI = BF16 ? 2 : 4;
+  uint32_t w[kI];
+  float am[kI];
+  float rho[kI];
 };
 
 template <bool BF16>
@@ -145,80 +169,169 @@ __device__ __forceinline__ void span_load(const void *__restrict__ W, int64_t ba
   }
 }
 
-template <bool BF16, int QT>
-__device__ __forceinline__ void span_encode(const SpanRaw<BF16> &raw, int64_t base, uint8_t *__restrict__ codes,
-                                            float *__restrict__ absmax, const float2 *lut, int lane, float *am_lds,
-                                            int64_t blk0) {
-  if constexpr (!BF16) {
+// The lane's elements of load instruction i as fp32.
+template <bool BF16>
+__device__ __forceinline__ void span_values(const SpanRaw<BF16> &raw, int i, float (&v)[BF16 ? 8 : 4]) {
+  // Copy components to scalars before reinterpreting them: a bit_cast
+  // applied directly to a vector component reads the wrong element.
+  const uint32_t u[4] = {raw.v[i].x, raw.v[i].y, raw.v[i].z, raw.v[i].w};
+  if constexpr (BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // Copy components to scalars before reinterpreting them: a bit_cast
-      // applied directly to a vector component reads the wrong element.
-      const uint32_t u[4] = {raw.v[i].x, raw.v[i].y, raw.v[i].z, raw.v[i].w};
-      float v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = as_f32(u[j]);
-      float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-      am = fmaxf(am, dpp_f32<0xB1>(am));    // quad xor 1
-      am = fmaxf(am, dpp_f32<0x4E>(am));    // quad xor 2
-      am = fmaxf(am, dpp_f32<0x124>(am));   // row rotate by 4
-      am = fmaxf(am, dpp_f32<0x128>(am));   // row rotate by 8
-      if ((lane & 15) == 0) {
-        const int64_t b = base / QN_BLOCK + 4 * i + (lane >> 4);
-        absmax[b] = am;
-        if (am_lds) am_lds[b - blk0] = am;
-      }
-      const uint32_t w = encode<4, QT>(v, am, lut);
-      *reinterpret_cast<uint16_t *>(codes + base / 2 + 2 * (64 * i + lane)) = (uint16_t)w;
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_lo(u[j]);
+      v[2 * j + 1] = bf16_hi(u[j]);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t u[4] = {raw.v[i].x, raw.v[i].y, raw.v[i].z, raw.v[i].w};
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = bf16_lo(u[j]);
-        v[2 * j + 1] = bf16_hi(u[j]);
-      }
-      float am = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
-      am = fmaxf(am, dpp_f32<0xB1>(am));    // quad xor 1
-      am = fmaxf(am, dpp_f32<0x4E>(am));    // quad xor 2
-      am = fmaxf(am, dpp_f32<0x141>(am));   // half-row mirror: the other quad of 8
-      if ((lane & 7) == 0) {
-        const int64_t b = base / QN_BLOCK + 8 * i + (lane >> 3);
-        absmax[b] = am;
-        if (am_lds) am_lds[b - blk0] = am;
-      }
-      const uint32_t w = encode<8, QT>(v, am, lut);
-      *reinterpret_cast<uint32_t *>(codes + base / 2 + 4 * (64 * i + lane)) = w;
-    }
+    for (int j = 0; j < 4; ++j) v[j] = as_f32(u[j]);
   }
 }
 
+// Block absmaxes (every lane of a block ends with its block's value: DPP quad
+// permutes, then a half-row mirror for the 8 lanes of a bf16 block or two row
+// rotations for the 16 lanes of an fp32 block), correctly rounded reciprocals,
+// codes by multiplying with the reciprocal.  Returns true in a lane whose
+// reciprocal overflowed (its codes are then redone by span_codes_div).
 template <bool BF16, int QT>
-__device__ __forceinline__ void quantize_span(const void *__restrict__ W, int64_t base, uint8_t *__restrict__ codes,
-                                              float *__restrict__ absmax, const float2 *lut, int lane) {
-  SpanRaw<BF16> raw;
-  span_load<BF16>(W, base, lane, raw);
-  span_encode<BF16, QT>(raw, base, codes, absmax, lut, lane, nullptr, 0);
+__device__ __forceinline__ bool span_codes(const SpanRaw<BF16> &raw, const float2 *lut, SpanEnc<BF16> &e) {
+  constexpr int C = BF16 ? 8 : 4;
+  bool slow = false;
+#pragma unroll
+  for (int i = 0; i < SpanEnc<BF16>::kI; ++i) {
+    float v[C];
+    span_values<BF16>(raw, i, v);
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) am = fmaxf(am, fabsf(v[j]));
+    // Across the block's lanes the maxima of magnitudes are taken on their
+    // bit patterns (for non-negative fp32 the integer order is the value
+    // order), which lets each DPP exchange fold into an integer max.
+    uint32_t ab = as_u32(am);
+    ab = max(ab, dpp_u32<0xB1>(ab));    // quad xor 1
+    ab = max(ab, dpp_u32<0x4E>(ab));    // quad xor 2
+    if constexpr (BF16) {
+      ab = max(ab, dpp_u32<0x141>(ab));   // half-row mirror: the other quad of 8
+    } else {
+      ab = max(ab, dpp_u32<0x124>(ab));   // row rotate by 4
+      ab = max(ab, dpp_u32<0x128>(ab));   // row rotate by 8
+    }
+    e.am[i] = as_f32(ab);
+  }
+  // Correctly rounded reciprocals of the lane's kI block maxima (infinite when
+  // 1/a overflows) with one division: lane l divides for instruction l mod kI
+  // (the kI lanes of an aligned group share their blocks) and takes the
+  // others' results by DPP.
+  constexpr int kI = SpanEnc<BF16>::kI;
+  const int lane = threadIdx.x & 63;
+  float mine = e.am[0];
+#pragma unroll
+  for (int i = 1; i < kI; ++i) mine = (lane & (kI - 1)) == i ? e.am[i] : mine;
+  const float r = mine > 0.0f ? 1.0f / mine : 0.0f;
+  if constexpr (kI == 2) {
+    const float o = dpp_f32<0xB1>(r);   // lane ^ 1
+    e.rho[0] = (lane & 1) ? o : r;
+    e.rho[1] = (lane & 1) ? r : o;
+  } else {
+    e.rho[0] = dpp_f32<0x00>(r);   // quad broadcast of lane 0
+    e.rho[1] = dpp_f32<0x55>(r);   // lane 1
+    e.rho[2] = dpp_f32<0xAA>(r);   // lane 2
+    e.rho[3] = dpp_f32<0xFF>(r);   // lane 3
+  }
+#pragma unroll
+  for (int i = 0; i < kI; ++i) {
+    float v[C];
+    span_values<BF16>(raw, i, v);
+    const float rho = e.rho[i];
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) w |= nearest_row<QT>(v[j] * rho, __builtin_fmaf(v[j], rho, 5.0f), lut) << (4 * j);
+    e.w[i] = w;
+    slow |= __builtin_isinf(rho);
+  }
+  return slow;
 }
 
+// 1/a overflows fp32 (a < 2^-128): divide each weight of such a block by a.
+// Run for the whole wave (behind a wave-uniform test) and selected per lane,
+// so that none of it is folded into the common path.
 template <bool BF16, int QT>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restrict__ W, int64_t n,
+__device__ void span_codes_div(const SpanRaw<BF16> &raw, const float2 *lut, SpanEnc<BF16> &e) {
+  constexpr int C = BF16 ? 8 : 4;
+#pragma unroll
+  for (int i = 0; i < SpanEnc<BF16>::kI; ++i) {
+    float v[C];
+    span_values<BF16>(raw, i, v);
+    // The divisor passes through an empty asm statement (a side effect the
+    // compiler cannot move), so that the divisions stay behind the test
+    // instead of being speculated into the common path.
+    float a = e.am[i];
+    asm volatile("" : "+v"(a));
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const float nrm = v[j] / a;
+      w |= nearest_row<QT>(nrm, nrm + 5.0f, lut) << (4 * j);
+    }
+    e.w[i] = __builtin_isinf(e.rho[i]) ? w : e.w[i];
+  }
+}
+
+// Codes from registers (2 or 4 bytes per lane per instruction, contiguous over
+// the wave); each block's absmax is stored by all lanes of the block, same
+// value to the same address, so no lane needs a branch.
+template <bool BF16>
+__device__ __forceinline__ void span_store(const SpanEnc<BF16> &e, int64_t base, uint8_t *__restrict__ codes,
+                                           float *__restrict__ absmax, int lane, float *am_lds, int64_t blk0) {
+#pragma unroll
+  for (int i = 0; i < SpanEnc<BF16>::kI; ++i) {
+    const int64_t b = BF16 ? base / QN_BLOCK + 8 * i + (lane >> 3) : base / QN_BLOCK + 4 * i + (lane >> 4);
+    absmax[b] = e.am[i];
+    if (am_lds) am_lds[b - blk0] = e.am[i];
+    if constexpr (BF16) *reinterpret_cast<uint32_t *>(codes + base / 2 + 4 * (64 * i + lane)) = e.w[i];
+    else *reinterpret_cast<uint16_t *>(codes + base / 2 + 2 * (64 * i + lane)) = (uint16_t)e.w[i];
+  }
+}
+
+// U consecutive full spans from span index ch0: all loads first, then each
+// span's codes (one straight-line stretch, the rare division path behind a
+// wave-uniform test) and stores.
+template <bool BF16, int QT, int U>
+__device__ __forceinline__ void quantize_spans(const void *__restrict__ W, int64_t ch0, uint8_t *__restrict__ codes,
+                                               float *__restrict__ absmax, const float2 *lut, int lane,
+                                               float *am_lds, int64_t blk0) {
+  SpanRaw<BF16> raw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) span_load<BF16>(W, (ch0 + u) * kQChunk, lane, raw[u]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    SpanEnc<BF16> e;
+    if (__builtin_amdgcn_ballot_w64(span_codes<BF16, QT>(raw[u], lut, e)) != 0)
+      span_codes_div<BF16, QT>(raw[u], lut, e);
+    span_store<BF16>(e, (ch0 + u) * kQChunk, codes, absmax, lane, am_lds, blk0);
+  }
+}
+
+// Spans per wave iteration of the plain quantiser.
+constexpr int kQSpans = 2;
+
+template <bool BF16, int QT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void quantize_kernel(const void *__restrict__ W, int64_t n,
                                                             uint8_t *__restrict__ codes,
                                                             float *__restrict__ absmax,
                                                             CodecTables tab) {
-  __shared__ float2 lut[32];
+  __shared__ float2 lut[kBuckets];
   load_lut(lut, tab, QT);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t wave_id = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t full = n / kQChunk;
-  for (int64_t ch = wave_id; ch < full; ch += nwaves) quantize_span<BF16, QT>(W, ch * kQChunk, codes, absmax, lut, lane);
+  const int64_t groups = full / kQSpans;
+  for (int64_t g = wave_id; g < groups; g += nwaves)
+    quantize_spans<BF16, QT, kQSpans>(W, g * kQSpans, codes, absmax, lut, lane, nullptr, 0);
+  // Full spans left over after the groups, one per wave.
+  const int64_t left = full - groups * kQSpans;
+  if (wave_id < left) quantize_spans<BF16, QT, 1>(W, groups * kQSpans + wave_id, codes, absmax, lut, lane, nullptr, 0);
   if (full * kQChunk < n && wave_id == nwaves - 1)
     quantize_tail<BF16, QT>(W, n, full * kQChunk, codes, absmax, lut, lane);
 }
@@ -235,64 +348,74 @@ __device__ __forceinline__ uint32_t dq_code(float a, float step) {
   return (uint32_t)fminf(fmaxf(kf, 0.0f), 255.0f);
 }
 
+// Maximum over the wave, in every lane, without LDS traffic: DPP within each
+// row of 16 lanes (quad swaps, half-row and row mirrors), then the four rows'
+// maxima read out with readlane.
 __device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  return m;
+  m = fmaxf(m, dpp_f32<0xB1>(m));    // quad: lanes i ^ 1
+  m = fmaxf(m, dpp_f32<0x4E>(m));    // quad: lanes i ^ 2
+  m = fmaxf(m, dpp_f32<0x141>(m));   // half-row mirror: the two quads of 8
+  m = fmaxf(m, dpp_f32<0x140>(m));   // row mirror: the two halves of 16
+  const auto rd = [](float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  };
+  return fmaxf(fmaxf(rd(m, 0), rd(m, 16)), fmaxf(rd(m, 32), rd(m, 48)));
 }
 
-// Quantise and double-quantise in one pass: a workgroup owns whole groups of
-// 16384 weights (256 blocks); each wave quantises four 1024-element spans of
-// the group, the block absmaxes also go to LDS, and after one barrier each
-// thread double-quantises one block of the group.
+// Quantise and double-quantise in one pass: a workgroup of 8 waves owns whole
+// groups of 16384 weights (256 blocks); each wave quantises two 1024-element
+// spans of the group, the block absmaxes also go to LDS, and after one barrier
+// each of the first 256 threads double-quantises one block of the group.
+constexpr int kDqThreads = 512;
+constexpr int kDqSpans = kQGroupElems / kQChunk / (kDqThreads / 64);   // spans per wave: 2
+
 template <bool BF16, int QT>
-__global__ __launch_bounds__(kThreads) void quantize_dq_kernel(const void *__restrict__ W, int64_t n,
-                                                               uint8_t *__restrict__ codes,
-                                                               float *__restrict__ absmax,
-                                                               uint8_t *__restrict__ absmax_q,
-                                                               float *__restrict__ scale2, CodecTables tab) {
-  static_assert(kThreads == QN_GROUP, "one thread per block of the group");
-  __shared__ float2 lut[32];
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(BF16 ? 8 : 4, 8))) void quantize_dq_kernel(const void *__restrict__ W, int64_t n,
+                                                                 uint8_t *__restrict__ codes,
+                                                                 float *__restrict__ absmax,
+                                                                 uint8_t *__restrict__ absmax_q,
+                                                                 float *__restrict__ scale2, CodecTables tab) {
+  static_assert(kDqThreads >= QN_GROUP && kDqSpans * (kDqThreads / 64) * kQChunk == kQGroupElems, "group split");
+  __shared__ float2 lut[kBuckets];
   __shared__ float am_s[QN_GROUP];
-  __shared__ float wmax[kThreads / 64];
+  __shared__ float wmax[QN_GROUP / 64];
   load_lut(lut, tab, QT);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nb = (n + QN_BLOCK - 1) / QN_BLOCK;
   const int64_t ngroups = (nb + QN_GROUP - 1) / QN_GROUP;
   const int64_t full = n / kQChunk;
   for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
-    am_s[tid] = 0.0f;
+    if (tid < QN_GROUP) am_s[tid] = 0.0f;
     __syncthreads();   // lut ready, am_s cleared (and the previous group's reads done)
     const int64_t blk0 = g * QN_GROUP;
-    const int64_t ch0 = g * (kQGroupElems / kQChunk) + 4 * wave;   // the wave's four spans
-    if (ch0 + 4 <= full) {
-      // All four spans' loads in flight before the first is encoded.
-      SpanRaw<BF16> raw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) span_load<BF16>(W, (ch0 + i) * kQChunk, lane, raw[i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) span_encode<BF16, QT>(raw[i], (ch0 + i) * kQChunk, codes, absmax, lut, lane, am_s, blk0);
+    const int64_t ch0 = g * (kQGroupElems / kQChunk) + kDqSpans * wave;   // the wave's spans
+    if (ch0 + kDqSpans <= full) {
+      // Both spans' loads in flight before the first is encoded.
+      quantize_spans<BF16, QT, kDqSpans>(W, ch0, codes, absmax, lut, lane, am_s, blk0);
     } else {
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kDqSpans; ++i) {
         const int64_t ch = ch0 + i;
         if (ch < full) {
-          SpanRaw<BF16> raw;
-          span_load<BF16>(W, ch * kQChunk, lane, raw);
-          span_encode<BF16, QT>(raw, ch * kQChunk, codes, absmax, lut, lane, am_s, blk0);
+          quantize_spans<BF16, QT, 1>(W, ch, codes, absmax, lut, lane, am_s, blk0);
         } else if (ch == full && full * kQChunk < n) {
           quantize_tail<BF16, QT>(W, n, full * kQChunk, codes, absmax, lut, lane, am_s, blk0);
         }
       }
     }
     __syncthreads();
-    const float a = am_s[tid];
-    const float m = wave_max(a);
-    if (lane == 0) wmax[wave] = m;
+    float a = 0.0f;
+    if (tid < QN_GROUP) {
+      a = am_s[tid];
+      const float m = wave_max(a);
+      if (lane == 0) wmax[wave] = m;
+    }
     __syncthreads();
-    const float c = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const float step = c / 255.0f;
-    if (tid == 0) scale2[g] = step;
-    if (blk0 + tid < nb) absmax_q[blk0 + tid] = (uint8_t)dq_code(a, step);
+    if (tid < QN_GROUP) {
+      const float c = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+      const float step = c / 255.0f;
+      if (tid == 0) scale2[g] = step;
+      if (blk0 + tid < nb) absmax_q[blk0 + tid] = (uint8_t)dq_code(a, step);
+    }
   }
 }
 
@@ -410,6 +533,20 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
   }
 }
 
+// Workgroups of kernel `fn` (`threads` threads) that fit on one CU at once
+// (occupancy query, cached per kernel).
+int resident_per_cu(const void *fn, int threads = kThreads) {
+  static std::mutex mu;
+  static std::map<const void *, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(fn);
+  if (it != cache.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, 0) != hipSuccess || nb < 1) nb = 1;
+  cache[fn] = nb;
+  return nb;
+}
+
 int grid_for(int64_t work_items, int per_cu_waves = 8) {
   // At most a few workgroups per CU for a grid-stride loop; at least one item each.
   int64_t wgs = (work_items + kThreads - 1) / kThreads;
@@ -428,16 +565,24 @@ void launch_quantize_t(const void *W, int w_is_bf16, int64_t n, uint8_t *codes, 
   if (absmax_q) {
     // One workgroup per group of 16384 weights, a few resident per CU.
     const int64_t groups = (n + kQGroupElems - 1) / kQGroupElems;
-    const int grid = (int)std::min<int64_t>(groups, (int64_t)device_cus() * 8);
+    const void *fn = w_is_bf16 ? reinterpret_cast<const void *>(&quantize_dq_kernel<true, QT>)
+                               : reinterpret_cast<const void *>(&quantize_dq_kernel<false, QT>);
+    const int grid = (int)std::min<int64_t>(groups, (int64_t)device_cus() * resident_per_cu(fn, kDqThreads));
     if (w_is_bf16)
-      hipLaunchKernelGGL((quantize_dq_kernel<true, QT>), dim3(grid), dim3(kThreads), 0, s, W, n, codes, absmax,
+      hipLaunchKernelGGL((quantize_dq_kernel<true, QT>), dim3(grid), dim3(kDqThreads), 0, s, W, n, codes, absmax,
                          absmax_q, scale2, tab);
     else
-      hipLaunchKernelGGL((quantize_dq_kernel<false, QT>), dim3(grid), dim3(kThreads), 0, s, W, n, codes, absmax,
+      hipLaunchKernelGGL((quantize_dq_kernel<false, QT>), dim3(grid), dim3(kDqThreads), 0, s, W, n, codes, absmax,
                          absmax_q, scale2, tab);
     return;
   }
-  const int grid = grid_for((n + kQChunk - 1) / kQChunk * 64);
+  // One wave per kQSpans spans, as many workgroups as are resident at once.
+  const void *fn = w_is_bf16 ? reinterpret_cast<const void *>(&quantize_kernel<true, QT>)
+                             : reinterpret_cast<const void *>(&quantize_kernel<false, QT>);
+  const int64_t wave_iters = std::max<int64_t>(1, (n + kQSpans * kQChunk - 1) / (kQSpans * kQChunk));
+  const int grid = (int)std::max<int64_t>(
+      1, std::min<int64_t>((wave_iters + kThreads / 64 - 1) / (kThreads / 64),
+                           (int64_t)device_cus() * resident_per_cu(fn)));
   if (w_is_bf16)
     hipLaunchKernelGGL((quantize_kernel<true, QT>), dim3(grid), dim3(kThreads), 0, s, W, n, codes, absmax, tab);
   else

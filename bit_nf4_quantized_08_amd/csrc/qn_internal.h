@@ -12,16 +12,18 @@ namespace qn {
 // segment; kernels copy what they index dynamically into LDS), one per 4-bit
 // type (QN_NF4, QN_FP4).
 //   code[16]      the table's values by code (fp32).
-//   thr[32], base[32], lohi[32]  bucket table for the nearest-value search: a
-//   normalised value n in [-1, 1] falls into bucket b = clamp(int(16 n + 16),
-//   0, 31); its level is base[b] + (n >= thr[b]) among the distinct values in
-//   ascending order, and its code is byte (n >= thr[b]) of lohi[b].  For NF4
-//   the code of a level is the level itself.
+//   thr[33], base[33], lohi[33]  bucket table for the nearest-value search: a
+//   normalised value n in [-1, 1 + 2^-23] falls into bucket b = floor(16 n +
+//   16) (0 .. 32; bucket 32 holds n >= 1); its level is base[b] + (n >=
+//   thr[b]) among the distinct values in ascending order, and its code is
+//   byte (n >= thr[b]) of lohi[b].  For NF4 the code of a level is the level
+//   itself.
+constexpr int kBuckets = 33;
 struct CodecTables {
   float code[16];
-  float thr[32];
-  uint32_t base[32];
-  uint32_t lohi[32];
+  float thr[kBuckets];
+  uint32_t base[kBuckets];
+  uint32_t lohi[kBuckets];
 };
 
 // Host: the tables of a 4-bit type (codebook.cpp).  Idempotent, thread-safe.
