@@ -327,6 +327,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="headline step only (for profiling runs)")
+    ap.add_argument("--bulk-only", action="store_true",
+                    help="only the bulk round trip over 4096x4096 bf16 tiles, printed as one JSON line "
+                         "(for profiling the codec kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the run, copy 256 MiB three times (reference for HBM counters)")
     args = ap.parse_args()
@@ -343,6 +346,9 @@ def main():
     lib.load()
     cap = torch.cuda.Stream()
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    if args.bulk_only:
+        print(json.dumps({"bulk_round_trip_bf16_tiles": bulk_stage(torch, lib, dev, cap, log)}), flush=True)
+        return
 
     # ---------------- headline: the 70B-shaped layer
     log("70B layer: quantising 7 weights")
@@ -790,6 +796,39 @@ def other_stages(torch, lib, dev, cap, log):
     torch.cuda.empty_cache()
 
     # ---- bulk sweep: 7.62e9 weights as 4096 x 4096 bf16 tiles, round trip
+    st["bulk_round_trip_bf16_tiles"] = bulk_stage(torch, lib, dev, cap, log)
+
+    # ---- the tiny configuration (launch-bound)
+    from bit_nf4_quantized_08_amd import synth
+    t = synth.tiny_inputs()
+    Wt = torch.from_numpy(t["W"]).to(dev)
+    wt = lib.quantize_weight(Wt)
+    X, A, B, dY = (t[k].to(dev) for k in ("X", "A", "B", "dY"))
+    Yt, Ht = lib.qlora_linear_fwd(X, wt, A, B, t["alpha"], want_H=True)
+    M, r = X.shape[0], A.shape[0]
+    gt = (torch.empty_like(X), torch.empty_like(A), torch.empty_like(B))
+    wsf = lib.workspace(lib.QN_OP_FWD, M, wt.N, wt.K, r, dev)
+    wsb = lib.workspace(lib.QN_OP_BWD, M, wt.N, wt.K, r, dev)
+
+    def qdq():
+        lib.nf4_quantize(Wt, codes=wt.codes, absmax=wt.absmax)
+        lib.nf4_double_quant(wt.absmax, absmax_q=wt.absmax_q, scale2=wt.scale2)
+
+    st["tiny"] = {
+        "quantize_dq_us": round(graph_time_us(torch, cap, qdq, replays=50), 2),
+        "fwd_us": round(graph_time_us(torch, cap, lambda: lib.qlora_linear_fwd(X, wt, A, B, t["alpha"], Y=Yt, H=Ht,
+                                                                               ws=wsf), replays=50), 2),
+        "bwd_us": round(graph_time_us(torch, cap, lambda: lib.qlora_linear_bwd(dY, X, wt, A, B, t["alpha"], H=Ht,
+                                                                               out=gt, ws=wsb), replays=50), 2),
+        "note": "launch-bound: a few microseconds of fixed cost per kernel",
+    }
+    return st
+
+
+def bulk_stage(torch, lib, dev, cap, log):
+    """The bulk quantise / double-quant / dequant round trip over 4096 x 4096
+    bf16 tiles (graph-replayed): per-stage times, GB/s, round-trip error and
+    stored bits per weight."""
     log("bulk round trip")
     SWEEP_WEIGHTS, TILE = 7.62e9, 4096 * 4096
     g_sw = torch.Generator(device=dev)
@@ -839,7 +878,7 @@ def other_stages(torch, lib, dev, cap, log):
     qdq_bytes = q_bytes + nb_t + 4 * (nb_t // 256)          # quantise writes the 8-bit scales and steps too
     deq_bytes = TILE // 2 + nb_t + 4 * (nb_t // 256) + 2 * TILE
     tile_bytes = qdq_bytes + deq_bytes
-    st["bulk_round_trip_bf16_tiles"] = {
+    out = {
         "tile_round_trip_us": round(tile_us, 2),
         "round_trip_GBps": round(tile_bytes / tile_us / 1e3, 1),
         "tile_round_trip_3_launches_us": round(tile3_us, 2),
@@ -860,32 +899,7 @@ def other_stages(torch, lib, dev, cap, log):
     }
     del tiles, sw, sw_out
     torch.cuda.empty_cache()
-
-    # ---- the tiny configuration (launch-bound)
-    from bit_nf4_quantized_08_amd import synth
-    t = synth.tiny_inputs()
-    Wt = torch.from_numpy(t["W"]).to(dev)
-    wt = lib.quantize_weight(Wt)
-    X, A, B, dY = (t[k].to(dev) for k in ("X", "A", "B", "dY"))
-    Yt, Ht = lib.qlora_linear_fwd(X, wt, A, B, t["alpha"], want_H=True)
-    M, r = X.shape[0], A.shape[0]
-    gt = (torch.empty_like(X), torch.empty_like(A), torch.empty_like(B))
-    wsf = lib.workspace(lib.QN_OP_FWD, M, wt.N, wt.K, r, dev)
-    wsb = lib.workspace(lib.QN_OP_BWD, M, wt.N, wt.K, r, dev)
-
-    def qdq():
-        lib.nf4_quantize(Wt, codes=wt.codes, absmax=wt.absmax)
-        lib.nf4_double_quant(wt.absmax, absmax_q=wt.absmax_q, scale2=wt.scale2)
-
-    st["tiny"] = {
-        "quantize_dq_us": round(graph_time_us(torch, cap, qdq, replays=50), 2),
-        "fwd_us": round(graph_time_us(torch, cap, lambda: lib.qlora_linear_fwd(X, wt, A, B, t["alpha"], Y=Yt, H=Ht,
-                                                                               ws=wsf), replays=50), 2),
-        "bwd_us": round(graph_time_us(torch, cap, lambda: lib.qlora_linear_bwd(dY, X, wt, A, B, t["alpha"], H=Ht,
-                                                                               out=gt, ws=wsb), replays=50), 2),
-        "note": "launch-bound: a few microseconds of fixed cost per kernel",
-    }
-    return st
+    return out
 
 
 if __name__ == "__main__":
