@@ -147,3 +147,62 @@ def test_fp4_merge_bit_exact():
     ref = oracle.merge(p, N, K, oracle.dq_absmax(*oracle.double_quant(a)), synth.bf16_values(A),
                        synth.bf16_values(B), 32.0, out="f32", quant_type="fp4")
     np.testing.assert_array_equal(host(got).view(np.uint32), ref.view(np.uint32))
+
+
+def _edge_blocks(qt):
+    """64-element blocks that take the quantiser's rare paths: zero, every
+    element a tie at a representable midpoint, negative zeros, a block whose
+    absmax is so small that 1/a overflows fp32 (the oracle then divides each
+    weight by a), a small normal absmax, huge magnitudes, a tiny value next to
+    O(1) ones."""
+    table = oracle.nf4_codebook() if qt == "nf4" else oracle.fp4_table()
+    lev = np.unique(table)
+    mids = ((lev[:-1].astype(np.float64) + lev[1:]) / 2).astype(np.float32)
+    rng = np.random.default_rng(17)
+    out = [np.zeros(64, np.float32)]
+    b = np.zeros(64, np.float32); b[0] = 1.0
+    for j, m in enumerate(mids[:15]):
+        b[1 + 2 * j] = m
+        b[2 + 2 * j] = np.nextafter(m, np.float32(np.inf))
+    out.append(b)
+    b = np.full(64, -0.0, np.float32); b[5] = -3.25
+    out.append(b)
+    out.append((rng.standard_normal(64) * 5e-40).astype(np.float32))
+    out.append((rng.standard_normal(64) * 3e-38).astype(np.float32))
+    out.append((rng.standard_normal(64) * 2e37).astype(np.float32))
+    b = rng.standard_normal(64).astype(np.float32); b[10] = 1e-30
+    out.append(b)
+    return out
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_edge_blocks_inside_full_spans(qt, bf16):
+    """The edge blocks placed among ordinary Gaussian blocks inside full
+    1024-element spans and full and partial groups of 16384 (the kernels'
+    straight-line span path, not only the tail path), plain and with the fused
+    double quantisation; bit-exact against the oracle."""
+    say(f"edge blocks in full spans {qt} bf16={bf16}")
+    N, K = 3, 8192                      # 24 full spans; groups: one full, one partial
+    W = synth.gaussian((N, K), 0.02, synth.SEED_W + 901).reshape(-1)
+    blocks = _edge_blocks(qt)
+    # (block, kind): different lanes and load instructions of a span, both
+    # halves of the first group, and the partial second group; the block
+    # with an overflowing reciprocal (kind 3) in two spans of its own
+    at = [(3, 0), (8, 1), (17, 2), (40, 3), (129, 4), (250, 5), (300, 6), (301, 0), (383, 1), (333, 3)]
+    for blk, kind in at:
+        W[64 * blk:64 * blk + 64] = blocks[kind]
+    W = W.reshape(N, K)
+    Wo = synth.bf16_values(synth.to_bf16(W)) if bf16 else W
+    p, a, _ = oracle.quantize(Wo, quant_type=qt)
+    k, step = oracle.double_quant(a)
+    # the blocks of kind 3 really take the division path
+    with np.errstate(over="ignore", divide="ignore"):
+        assert np.isinf(np.float32(1.0) / a[[40, 333]]).all(), "no block with an overflowing reciprocal"
+    for dq in (False, True):
+        w = _run(W, qt, bf16, dq)
+        np.testing.assert_array_equal(host(w.codes), p)
+        np.testing.assert_array_equal(host(w.absmax).view(np.uint32), a.view(np.uint32))
+        if dq:
+            np.testing.assert_array_equal(host(w.absmax_q), k)
+            np.testing.assert_array_equal(host(w.scale2).view(np.uint32), step.view(np.uint32))
