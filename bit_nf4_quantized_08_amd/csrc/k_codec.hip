@@ -47,15 +47,16 @@ __device__ __forceinline__ void load_lut(float2 *lut, const CodecTables &tab, in
 }
 
 // ---------------------------------------------------------------- quantise
-// A wave takes 1024 consecutive elements (16 blocks) per iteration.  Its load
-// instructions are fully coalesced (lane l reads the l-th 16 bytes of a 1 KB
-// span), so a block is spread over consecutive lanes: 16 lanes for fp32 input
-// (4 elements each), 8 lanes for bf16 input (8 elements each).  The block
+// A wave takes spans of 1024 consecutive elements (16 blocks), two per
+// iteration of the plain quantiser, with every load of both issued first.  Its
+// load instructions are fully coalesced (lane l reads the l-th 16 bytes of a 1
+// KB span), so a block is spread over consecutive lanes: 16 lanes for fp32
+// input (4 elements each), 8 lanes for bf16 input (8 elements each).  The block
 // absmax is reduced across those lanes with DPP (quad permutes, then a row
 // rotation or half-row mirror); one correctly rounded reciprocal per block;
 // codes are stored from registers as 2 or 4 bytes per lane.  The last partial
-// wave span (fewer than 1024 elements) is done by one wave, 16 elements per
-// lane, with bounds checks.
+// span (fewer than 1024 elements) is done by one wave, 16 elements per lane,
+// with bounds checks.
 constexpr int kQChunk = 1024;
 constexpr int kQGroupElems = QN_GROUP * QN_BLOCK;   // 16384 weights: one double-quant group
 
