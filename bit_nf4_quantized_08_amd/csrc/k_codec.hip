@@ -138,8 +138,8 @@ __device__ void quantize_tail(const void *__restrict__ W, int64_t n, int64_t sta
 // block absmaxes and encodes every element with the block's reciprocal,
 // span_store writes codes and absmaxes (and, when am_lds is given, the
 // absmaxes to am_lds[block - blk0]).  A block whose reciprocal overflows is
-// re-encoded by span_codes_div, behind one wave-uniform test per group of
-// spans, so the common path has no branch and its table lookups can overlap.
+// re-encoded by span_codes_div, behind one wave-uniform test per span, so
+// the common path has no branch and its table lookups can overlap.
 template <bool BF16>
 struct SpanRaw {
   u32x4 v[BF16 ? 2 : 4];
@@ -564,7 +564,7 @@ void launch_quantize_t(const void *W, int w_is_bf16, int64_t n, uint8_t *codes, 
                        float *scale2, hipStream_t s) {
   const CodecTables &tab = codec_tables(QT);
   if (absmax_q) {
-    // One workgroup per group of 16384 weights, a few resident per CU.
+    // One 8-wave workgroup per group of 16384 weights, as many as are resident.
     const int64_t groups = (n + kQGroupElems - 1) / kQGroupElems;
     const void *fn = w_is_bf16 ? reinterpret_cast<const void *>(&quantize_dq_kernel<true, QT>)
                                : reinterpret_cast<const void *>(&quantize_dq_kernel<false, QT>);
